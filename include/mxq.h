@@ -1,0 +1,135 @@
+/*
+ * mxq.h -- C ABI of the MI355X (gfx950) library for the online half of
+ * block-aligned outlier rotation + MXFP4 quantization of LLM activations.
+ *
+ * Operation (DuQuant++ page, "DuQuant++: block-aligned rotation quantization
+ * for MXFP4 activation outliers"):
+ *   sec. 3.1   smoothing: X' = X * Lambda^-1, Lambda a per-channel factor
+ *   sec. 3.2-3.3  rotation: X^ = X' * R, R = BlockDiag(R_b, ..., R_b) with one
+ *              shared 32x32 orthogonal block R_b, so every 32-channel group g
+ *              of a token row is rotated on its own: y_g = x'_g * R_b
+ *   sec. 2.1   MXFP4: each 32-element group gets one shared scale from its
+ *              largest magnitude and every element is rounded to the nearest
+ *              4-bit float
+ *   sec. 5.2 item 1  smoothing and rotation fused into one kernel in front of
+ *              the MXFP4 linear layer (here quantization is fused in as well)
+ *
+ * MXFP4 convention (OCP Microscaling Formats v1.0, FP32-to-MX conversion):
+ *   amax = max_n |y_n| over the 32 rotated values of the group
+ *   e    = floor(log2 amax) - 2  (2 = largest exponent of E2M1), clamped to
+ *          [-127, 127]; amax = 0 gives e = -127
+ *   scale byte S = e + 127 (E8M0, bias 127).  0xFF (NaN) is never produced.
+ *   element code = E2M1 value nearest to y_n / 2^e among
+ *          {0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6}; a value exactly halfway
+ *          goes to the even code (ties-to-even); |y_n / 2^e| > 6 saturates to
+ *          +-6; zero results are always code 0x0 (never 0x8).
+ *   Since amax / 2^e is in [4, 8), the largest element always encodes to 4 or
+ *   6, and at most the top quarter of the range (6, 8) is clipped.
+ *   code nibble: bit 3 sign, bits 2..0 magnitude code (values above by code
+ *   0..7).  Packing: byte j of a group holds element 2j in its low nibble and
+ *   element 2j+1 in its high nibble.
+ *
+ * Layouts (all row-major, dense unless a stride is given):
+ *   x       [tokens][x_row_stride] elements, the first `channels` of a row used
+ *   lambda  [channels] fp32
+ *   r_hat   [32][32] bf16 bit patterns, y_n = sum_k x'_k * r_hat[k][n]
+ *   codes   [tokens][channels / 2] bytes
+ *   scales  [tokens][channels / 32] bytes
+ *
+ * Common rules for every call:
+ *   - Every buffer is DEVICE memory owned by the caller; the library never
+ *     allocates, frees or synchronizes.  `stream` is a hipStream_t passed as
+ *     void* (NULL = the null stream).  Calls are asynchronous: results are
+ *     valid once the caller has synchronized that stream.
+ *   - Arguments are validated on the host before any HIP call; on error
+ *     nothing is launched and nothing is written.  A launch failure returns
+ *     MXQ_ERR_HIP.  Faults during execution surface at the caller's next sync.
+ *   - tokens == 0 or channels == 0 is a valid empty call (returns MXQ_OK,
+ *     launches nothing, pointers may be NULL).
+ *   - Pointers x, codes, y_rot, y and lambda must be 16-byte aligned, and
+ *     x_row_stride * sizeof(element) must be a multiple of 16 (MXQ_ERR_ALIGN).
+ *     scales and r_hat need only their natural alignment.
+ *   - Limits: channels % 32 == 0, tokens and channels below 2^31, and
+ *     tokens * ceil(channels / 1024) below 2^31 (MXQ_ERR_SHAPE).
+ *   - NaN or infinite inputs are outside the contract (no error is raised,
+ *     the output for such a group is unspecified).
+ *   - The library holds no per-call state; calls are thread-safe.  Calls that
+ *     write the same output buffers concurrently race, as with any kernel.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MXQ_OK = 0,
+    MXQ_ERR_NULL = 1,   /* a required pointer is NULL                        */
+    MXQ_ERR_SHAPE = 2,  /* negative size, channels % 32 != 0, or too large   */
+    MXQ_ERR_DTYPE = 3,  /* dtype not supported by this entry point           */
+    MXQ_ERR_ALIGN = 4,  /* pointer or row pitch not aligned as required      */
+    MXQ_ERR_STRIDE = 5, /* x_row_stride < channels                           */
+    MXQ_ERR_HIP = 6     /* the HIP runtime reported an error at launch       */
+} mxq_status;
+
+typedef enum { MXQ_BF16 = 0, MXQ_FP16 = 1, MXQ_FP32 = 2 } mxq_dtype;
+
+/* Smooth + rotate + MXFP4-quantize in one pass over x.
+ * DuQuant++ page sec. 3.3 (online transform X * Lambda^-1 * R) and sec. 2.1
+ * (MXFP4 encoding); the smoothing factor is that of sec. 3.1.
+ *   x        BF16 or FP16 activations (MXQ_ERR_DTYPE otherwise)
+ *   lambda   per-channel divisor, or NULL for no smoothing (same as all ones)
+ *   r_hat    the shared 32x32 block in bf16
+ *   codes, scales  outputs, fully overwritten
+ * The rotation runs on the matrix cores with bf16 operands and fp32
+ * accumulation.  The activations are split into bf16 terms whose sum is
+ * exactly the fp32 value of x' (bf16 x: 1 term; fp16 x: 2 terms; with lambda:
+ * 3 terms of x * (1/lambda) rounded to fp32), so products are exact and only
+ * the fp32 accumulation rounds. */
+mxq_status mxq_rotate_quant(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
+                            int64_t x_row_stride, const float *lambda, const uint16_t *r_hat,
+                            uint8_t *codes, uint8_t *scales, void *stream);
+
+/* Same kernel as mxq_rotate_quant; additionally stores the fp32 rotated
+ * values y [tokens][channels] (dense) when y_rot is not NULL.  Codes and
+ * scales are bit-identical to those of mxq_rotate_quant.  Meant for tests and
+ * error studies: the extra store costs 4 bytes per element. */
+mxq_status mxq_rotate_quant_ex(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
+                               int64_t x_row_stride, const float *lambda, const uint16_t *r_hat,
+                               uint8_t *codes, uint8_t *scales, float *y_rot, void *stream);
+
+/* Plain MXFP4 quantization of x (no smoothing, no rotation); DuQuant++ page
+ * sec. 2.1.  x may be BF16, FP16 or FP32.  Bit-identical to mxq_rotate_quant
+ * with lambda = NULL and r_hat = identity for BF16/FP16 input. */
+mxq_status mxq_quant(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
+                     int64_t x_row_stride, uint8_t *codes, uint8_t *scales, void *stream);
+
+/* Decode MXFP4 back to BF16 or FP32 y [tokens][channels] (dense):
+ * y = (-1)^s * {0, .5, 1, 1.5, 2, 3, 4, 6}[m] * 2^(S - 127) (OCP MX v1.0
+ * E2M1 and E8M0 tables).  All 16 codes are accepted (0x8 gives -0.0);
+ * S = 0xFF gives NaN; values beyond the output type's range give +-inf.
+ * Every finite result is exact in both output types.  The decoded tensor is
+ * the rotated X^ of sec. 3.3, not the original activations. */
+mxq_status mxq_dequant(const uint8_t *codes, const uint8_t *scales, int64_t tokens,
+                       int64_t channels, void *y, int32_t y_dtype, void *stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *mxq_status_str(int32_t status);
+
+/* Launch plan of the quantize kernels, a pure host function that touches no
+ * device: for `tokens` x `channels` on a GPU with `cu_count` compute units it
+ * writes {blocks, waves, tile_columns, row_step, waves_per_block} into
+ * out[0..4].  Returns MXQ_ERR_SHAPE for shapes the entry points reject. */
+mxq_status mxq_plan(int64_t tokens, int64_t channels, int32_t cu_count, int32_t *out);
+
+/* Library ABI version: 1. */
+int32_t mxq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

@@ -1,0 +1,169 @@
+"""MI355X (gfx950) online smoothing + block rotation + MXFP4 quantization.
+
+Thin ctypes binding over ``libmxq.so`` (C ABI in ``include/mxq.h``).  Every
+step of the path runs in the library's HIP kernels; PyTorch only provides
+device memory and the current stream.  There is no CPU fallback: importing
+works without the library, but every call raises if it is not built.
+
+Functions follow the online transform of the DuQuant++ page
+(sec. 3.3: X * Lambda^-1 * R, R block diagonal with one shared 32x32 block)
+and its MXFP4 encoding (sec. 2.1).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libmxq.so")
+
+MXQ_BF16, MXQ_FP16, MXQ_FP32 = 0, 1, 2
+STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_NULL", 2: "MXQ_ERR_SHAPE", 3: "MXQ_ERR_DTYPE",
+          4: "MXQ_ERR_ALIGN", 5: "MXQ_ERR_STRIDE", 6: "MXQ_ERR_HIP"}
+EXPORTS = ("mxq_rotate_quant", "mxq_rotate_quant_ex", "mxq_quant", "mxq_dequant",
+           "mxq_status_str", "mxq_plan", "mxq_version")
+
+_lib = None
+
+
+class MXQError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = int(status)
+        super().__init__(f"{fn}: {STATUS.get(self.status, self.status)}")
+
+
+def library_path() -> str:
+    return LIBRARY
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libmxq.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIBRARY
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with __graft_entry__.build() "
+                           "or python -m mxfp4_activation_rotation_amd._build")
+    lib = ctypes.CDLL(p)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.mxq_rotate_quant.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
+    lib.mxq_rotate_quant_ex.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+    lib.mxq_quant.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp]
+    lib.mxq_dequant.argtypes = [vp, vp, i64, i64, vp, i32, vp]
+    lib.mxq_status_str.argtypes = [i32]
+    lib.mxq_status_str.restype = ctypes.c_char_p
+    lib.mxq_plan.argtypes = [i64, i64, i32, ctypes.POINTER(ctypes.c_int32)]
+    for f in ("mxq_rotate_quant", "mxq_rotate_quant_ex", "mxq_quant", "mxq_dequant", "mxq_plan",
+              "mxq_version"):
+        getattr(lib, f).restype = ctypes.c_int32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+_DT = {torch.bfloat16: MXQ_BF16, torch.float16: MXQ_FP16, torch.float32: MXQ_FP32}
+
+
+def _stream(t: torch.Tensor, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _check_x(x: torch.Tensor, allowed):
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise ValueError("x must be a device tensor")
+    if x.dim() != 2 or (x.shape[0] > 0 and x.shape[1] > 0 and x.stride(1) != 1):
+        raise ValueError("x must be 2-D [tokens, channels] with unit column stride")
+    if x.dtype not in allowed:
+        raise ValueError(f"unsupported x dtype {x.dtype}")
+    return x.shape[0], x.shape[1], (x.stride(0) if x.shape[0] > 1 else x.shape[1])
+
+
+def _outputs(x, T, C, codes, scales):
+    if codes is None:
+        codes = torch.empty((T, C // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((T, C // 32), dtype=torch.uint8, device=x.device)
+    for name, t, shape in (("codes", codes, (T, C // 2)), ("scales", scales, (T, C // 32))):
+        if t.dtype != torch.uint8 or tuple(t.shape) != shape or not t.is_contiguous() or t.device != x.device:
+            raise ValueError(f"{name} must be a contiguous uint8 tensor of shape {shape} on {x.device}")
+    return codes, scales
+
+
+def rotate_quant(x: torch.Tensor, r_hat: torch.Tensor, lam: torch.Tensor | None = None, *,
+                 codes=None, scales=None, y_rot=None, stream=None):
+    """codes, scales = MXFP4(x / lam @ BlockDiag(r_hat)) (and y_rot if given).
+
+    x: bf16/fp16 [tokens, channels] on the GPU; r_hat: bf16 [32, 32] with
+    y_n = sum_k x_k r_hat[k, n]; lam: fp32 [channels] or None.  y_rot, if
+    given, is a contiguous fp32 [tokens, channels] tensor that receives the
+    rotated values (test and error-study use).
+    """
+    lib = load()
+    T, C, stride = _check_x(x, (torch.bfloat16, torch.float16))
+    if r_hat.dtype != torch.bfloat16 or tuple(r_hat.shape) != (32, 32) or not r_hat.is_contiguous() \
+            or r_hat.device != x.device:
+        raise ValueError("r_hat must be a contiguous bf16 [32, 32] tensor on x's device")
+    if lam is not None and (lam.dtype != torch.float32 or tuple(lam.shape) != (C,) or not lam.is_contiguous()
+                            or lam.device != x.device):
+        raise ValueError("lam must be a contiguous fp32 [channels] tensor on x's device")
+    codes, scales = _outputs(x, T, C, codes, scales)
+    if y_rot is not None:
+        if y_rot.dtype != torch.float32 or tuple(y_rot.shape) != (T, C) or not y_rot.is_contiguous():
+            raise ValueError("y_rot must be a contiguous fp32 [tokens, channels] tensor")
+        st = lib.mxq_rotate_quant_ex(_ptr(x), _DT[x.dtype], T, C, stride, _ptr(lam), _ptr(r_hat),
+                                     _ptr(codes), _ptr(scales), _ptr(y_rot), _stream(x, stream))
+        fn = "mxq_rotate_quant_ex"
+    else:
+        st = lib.mxq_rotate_quant(_ptr(x), _DT[x.dtype], T, C, stride, _ptr(lam), _ptr(r_hat),
+                                  _ptr(codes), _ptr(scales), _stream(x, stream))
+        fn = "mxq_rotate_quant"
+    if st != 0:
+        raise MXQError(fn, st)
+    return codes, scales
+
+
+def quant(x: torch.Tensor, *, codes=None, scales=None, stream=None):
+    """Plain MXFP4 quantization of bf16/fp16/fp32 x [tokens, channels]."""
+    lib = load()
+    T, C, stride = _check_x(x, (torch.bfloat16, torch.float16, torch.float32))
+    codes, scales = _outputs(x, T, C, codes, scales)
+    st = lib.mxq_quant(_ptr(x), _DT[x.dtype], T, C, stride, _ptr(codes), _ptr(scales), _stream(x, stream))
+    if st != 0:
+        raise MXQError("mxq_quant", st)
+    return codes, scales
+
+
+def dequant(codes: torch.Tensor, scales: torch.Tensor, out_dtype=torch.float32, *, out=None, stream=None):
+    """Decode MXFP4 codes/scales [tokens, channels/2], [tokens, channels/32] to bf16 or fp32."""
+    lib = load()
+    if codes.dtype != torch.uint8 or scales.dtype != torch.uint8 or codes.dim() != 2:
+        raise ValueError("codes and scales must be uint8 2-D tensors")
+    T, C = codes.shape[0], codes.shape[1] * 2
+    if tuple(scales.shape) != (T, C // 32) or not codes.is_contiguous() or not scales.is_contiguous():
+        raise ValueError("scales must be contiguous [tokens, channels/32]; codes contiguous")
+    if out is None:
+        out = torch.empty((T, C), dtype=out_dtype, device=codes.device)
+    if out.dtype not in (torch.bfloat16, torch.float32) or tuple(out.shape) != (T, C) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16/fp32 [tokens, channels] tensor")
+    st = lib.mxq_dequant(_ptr(codes), _ptr(scales), T, C, _ptr(out), _DT[out.dtype], _stream(codes, stream))
+    if st != 0:
+        raise MXQError("mxq_dequant", st)
+    return out
+
+
+def plan(tokens: int, channels: int, cu_count: int = 256):
+    """Launch plan {blocks, waves, tile_columns, row_step, waves_per_block} (host only)."""
+    lib = load()
+    out = (ctypes.c_int32 * 5)()
+    st = lib.mxq_plan(tokens, channels, cu_count, out)
+    if st != 0:
+        raise MXQError("mxq_plan", st)
+    return dict(zip(("blocks", "waves", "tile_columns", "row_step", "waves_per_block"), list(out)))

@@ -1,0 +1,106 @@
+// Device-side building blocks for gfx950 (CDNA4): MXFP4 group encoding and
+// the bf16 term split feeding the matrix cores.
+//
+// Encoding follows the OCP Microscaling Formats v1.0 FP32-to-MX conversion:
+// shared exponent e = floor(log2 amax) - 2 clamped to [-127, 127] (E8M0 byte
+// e + 127), elements rounded to the nearest E2M1 value of y / 2^e with
+// ties-to-even and saturation.  The DuQuant++ page (sec. 2.1) describes the
+// same two steps: group amax -> shared scale, then round each normalized
+// element to the nearest 4-bit float.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+__device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// Largest |v| over the 32 values of a group whose two halves (16 values each)
+// sit in lanes l and l ^ 32 of the wave; every lane gets the group maximum.
+__device__ __forceinline__ float group_amax(const float* v) {
+    float m0 = fabsf(v[0]);
+    float m1 = fabsf(v[1]);
+#pragma unroll
+    for (int i = 2; i < 16; i += 2) {
+        m0 = fmaxf(m0, fabsf(v[i]));
+        m1 = fmaxf(m1, fabsf(v[i + 1]));
+    }
+    const uint32_t m = as_u32(fmaxf(m0, m1));
+    // v_permlane32_swap with both operands = m: lane l ends up holding
+    // m[l] and m[l ^ 32] in the two results.
+    const auto sw = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+    return fmaxf(as_f32(sw[0]), as_f32(sw[1]));
+}
+
+// E8M0 scale byte for a group maximum m (finite, m >= 0):
+// S = clamp(floor(log2 m) - 2, -127, 127) + 127.  For a normal fp32 m,
+// floor(log2 m) is its biased exponent field minus 127, so S = field - 2.
+// Subnormal or zero m has field 0, and fields 1 and 2 also clamp, giving
+// S = 0 (e = -127).  A finite fp32 never gives S above 252.
+__device__ __forceinline__ uint32_t e8m0_of_amax(float m) {
+    const int field = static_cast<int>(as_u32(m) >> 23);
+    return static_cast<uint32_t>(field > 2 ? field - 2 : 0);
+}
+
+// A code nibble whose magnitude bits are 0 is made +0 (0x0): the gfx950
+// converter keeps the sign of a negative value that rounds to zero (0x8).
+// Per nibble, (mag + 7) has bit 3 set exactly when mag != 0, and the sum
+// never carries into the next nibble.
+__device__ __forceinline__ uint32_t drop_negative_zero(uint32_t d) {
+    const uint32_t mag = d & 0x77777777u;
+    const uint32_t nonzero = (mag + 0x77777777u) & 0x88888888u;
+    return mag | (d & nonzero);
+}
+
+// Eight fp32 values -> one dword of E2M1 codes, element i in nibble i.
+// v_cvt_scalef32_pk_fp4_f32 divides by 2^(field - 127) of `scale`'s biased
+// exponent field (field 0 meaning 2^-127), rounds to nearest even, saturates
+// at +-6, and writes its first operand to the low nibble of the selected byte.
+__device__ __forceinline__ uint32_t encode8(const float* v, float scale) {
+    uint32_t d = 0;
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[0], v[1], scale, 0);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[2], v[3], scale, 1);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[4], v[5], scale, 2);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[6], v[7], scale, 3);
+    return drop_negative_zero(d);
+}
+
+// Upper 16 bits of a and b as one bf16 pair {a_hi in the low half, b_hi in
+// the high half}: the bf16 truncation of two fp32 values in one v_perm_b32.
+__device__ __forceinline__ uint32_t bf16_pair_hi(float a, float b) {
+    return __builtin_amdgcn_perm(as_u32(b), as_u32(a), 0x07060302u);
+}
+
+// fp32 value minus its bf16 truncation (exact in fp32).
+__device__ __forceinline__ float bf16_residual(float a) {
+    return a - as_f32(as_u32(a) & 0xffff0000u);
+}
+
+// Widen 8 packed 16-bit elements (one 16-byte load) to fp32, element order kept.
+template <bool IS_FP16>
+__device__ __forceinline__ void widen8(u32x4_t q, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (IS_FP16) {
+            f[2 * i] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(q[i] & 0xffffu)));
+            f[2 * i + 1] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(q[i] >> 16)));
+        } else {
+            f[2 * i] = as_f32(q[i] << 16);
+            f[2 * i + 1] = as_f32(q[i] & 0xffff0000u);
+        }
+    }
+}
+
+__device__ __forceinline__ void widen4_f32(u32x4_t q, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = as_f32(q[i]);
+}
+
+}  // namespace mxq

@@ -1,0 +1,119 @@
+"""C ABI checks that need no GPU: exports, argument validation, launch plan.
+
+Every call below fails validation on the host, which by contract happens
+before any HIP call, so nothing touches a device.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mxfp4_activation_rotation_amd as mxq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, STRIDE = 0, 1, 2, 3, 4, 5
+P = ctypes.c_void_p(0x10000)       # never dereferenced: validation rejects first
+P_ODD = ctypes.c_void_p(0x10008)   # 8-byte but not 16-byte aligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mxq.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(mxq_[a-z_]+)\s*\(", text)))
+
+
+def test_header_is_plain_c():
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER], check=True)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(mxq.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", mxq.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, re.M), f"{n} not exported as text symbol"
+
+
+def test_library_carries_gfx950_code():
+    data = open(mxq.library_path(), "rb").read()
+    assert b"gfx950" in data
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.mxq_status_str(s).decode().startswith("MXQ_")
+    assert lib.mxq_version() == 1
+
+
+def rq(lib, x=P, dt=0, T=8, C=64, stride=64, lam=None, r=P, codes=P, scales=P):
+    return lib.mxq_rotate_quant(x, dt, T, C, stride, lam, r, codes, scales, None)
+
+
+def test_rotate_quant_validation(lib):
+    assert rq(lib, dt=2) == DTYPE          # fp32 x is not a fused input
+    assert rq(lib, dt=7) == DTYPE
+    assert rq(lib, C=48, stride=48) == SHAPE
+    assert rq(lib, T=-1) == SHAPE
+    assert rq(lib, C=-32) == SHAPE
+    assert rq(lib, T=0, x=None, r=None, codes=None, scales=None) == OK   # empty: no launch
+    assert rq(lib, C=0, stride=0, x=None) == OK
+    assert rq(lib, x=None) == NULL
+    assert rq(lib, r=None) == NULL
+    assert rq(lib, codes=None) == NULL
+    assert rq(lib, scales=None) == NULL
+    assert rq(lib, stride=32) == STRIDE
+    assert rq(lib, x=P_ODD) == ALIGN
+    assert rq(lib, codes=P_ODD) == ALIGN
+    assert rq(lib, lam=P_ODD) == ALIGN
+    assert rq(lib, stride=68) == ALIGN     # 136-byte rows are not 16-byte multiples
+    assert rq(lib, T=1 << 31) == SHAPE
+    assert lib.mxq_rotate_quant_ex(P, 0, 8, 64, 64, None, P, P, P, P_ODD, None) == ALIGN
+
+
+def test_quant_and_dequant_validation(lib):
+    q = lib.mxq_quant
+    assert q(P, 3, 8, 64, 64, P, P, None) == DTYPE
+    assert q(P, 2, 8, 64, 66, P, P, None) == ALIGN   # fp32 rows of 264 bytes
+    assert q(P, 2, 8, 64, 60, P, P, None) == STRIDE
+    assert q(None, 0, 8, 64, 64, P, P, None) == NULL
+    assert q(P, 1, 8, 40, 40, P, P, None) == SHAPE
+    assert q(None, 0, 0, 64, 64, None, None, None) == OK
+    d = lib.mxq_dequant
+    assert d(P, P, 8, 64, P, 1, None) == DTYPE       # fp16 output not offered
+    assert d(P, P, 8, 40, P, 0, None) == SHAPE
+    assert d(None, P, 8, 64, P, 0, None) == NULL
+    assert d(P, P, 8, 64, P_ODD, 2, None) == ALIGN
+    assert d(None, None, 0, 64, None, 2, None) == OK
+
+
+@pytest.mark.parametrize("T,C,cu", [(8192, 14336, 256), (16, 8192, 256), (64, 256, 256), (37, 1440, 256),
+                                    (1, 32, 256), (32768, 8192, 256), (3, 1 << 20, 4), (100000, 96, 80)])
+def test_plan_covers_every_tile_once(T, C, cu):
+    pl = mxq.plan(T, C, cu)
+    tcols, rs, waves = pl["tile_columns"], pl["row_step"], pl["waves"]
+    assert tcols == -(-(C // 32) // 32)
+    assert waves == tcols * rs and 1 <= rs <= T
+    assert pl["blocks"] * pl["waves_per_block"] >= waves > (pl["blocks"] - 1) * pl["waves_per_block"]
+    seen = {}
+    for w in range(waves):
+        tc, r0 = w % tcols, w // tcols
+        n_rows = len(range(r0, T, rs))
+        seen[tc] = seen.get(tc, 0) + n_rows
+    assert seen == {tc: T for tc in range(tcols)}
+
+
+def test_plan_rejects_bad_shapes():
+    for T, C in ((0, 64), (8, 0), (8, 33), (-1, 64)):
+        with pytest.raises(mxq.MXQError):
+            mxq.plan(T, C)
