@@ -1,0 +1,213 @@
+"""Throughput of the fused smooth + rotate + MXFP4 quantization on one MI355X.
+
+A step is one mxq_rotate_quant call over one batch of synthetic activations
+(default workload: down_proj-input shape, bf16 8192 x 14336 with massive
+outliers on 1% of tokens, outlier-aware Householder block, no smoothing).
+Inputs sit in HBM before the timed region starts.  Consecutive steps use
+different buffer sets (together > 3x the 256 MB last-level cache), so every
+step reads its activations from HBM rather than from cache.
+
+Prints one JSON line.  Besides the headline throughput it carries:
+  roofline      the quantize kernel's algorithmic HBM bytes per launch
+                (2 B read + 0.5 B codes + 1/32 B scale per element) over its
+                mean launch time (HIP events around the timed region on the
+                launch stream, divided by the step count), against the 8 TB/s
+                HBM peak; traffic = bytes the kernel really moved,
+                from committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters when
+                they were taken on the current kernel source, else null;
+  cpu_baseline  the fp64 CPU oracle on the host cores, same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "rotate+MXFP4-quant throughput: Gelem/s, HBM GB/s, % of MI355X HBM peak"
+HBM_PEAK_GBPS = 8000.0
+BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0  # bf16/fp16 in, FP4 codes + E8M0 scales out
+KERNEL_SOURCES = ("mxfp4_activation_rotation_amd/csrc/mxq.hip",
+                  "mxfp4_activation_rotation_amd/csrc/mxq_device.h",
+                  "mxfp4_activation_rotation_amd/_build.py")
+COUNTERS = {3: "profiles/rotate_quant_bf16_8192x14336_hbm_counters.txt"}
+WORKLOAD_NAMES = {
+    2: "QKV-input shape: bf16 2048x4096, 0.5% outlier channels x20, lognormal lambda, seeded orthogonal R",
+    3: "down_proj-input shape: bf16 8192x14336, Student-t(3) background, +-U(500,2000) on 1% of tokens "
+       "at channels 17/4099/9001/14000, outlier-aware Householder R (k from a 256-token slice), no lambda",
+    4: "decode-shaped calls: bf16 16x8192 per call, 2 outlier channels x30, lognormal lambda, orthogonal R",
+    5: "large prefill: fp16 32768x8192, 0.1% entries +-U(100,1000), 8 channels x25, "
+       "lambda = amax^0.5 (512-token slice), outlier-aware Householder R",
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_counters(cfg: int):
+    """Per-launch HBM bytes from the committed counter summary, or None when
+    it is absent or was taken on a different kernel source."""
+    rel = COUNTERS.get(cfg)
+    if not rel or not os.path.exists(os.path.join(ROOT, rel)):
+        return None
+    kv = {}
+    for line in open(os.path.join(ROOT, rel)):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, min_seconds: float):
+    import oracle
+    orc = oracle.default()
+    elems = wl.tokens * wl.channels
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        orc.rotate_quant(wl.x, wl.lam, wl.r_hat)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= min_seconds and len(times) >= 3:
+            break
+    med = statistics.median(times)
+    return {"value": round(elems / med / 1e9, 4), "unit": "Gelem/s", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": f"the full {wl.tokens}x{wl.channels} batch, {len(times)} repetitions "
+                      f"({sum(times):.1f} s of CPU wall time), median {med * 1e3:.0f} ms each"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4, 5],
+                    help="workload id (3 = the headline down_proj-input batch)")
+    ap.add_argument("--buffers", type=int, default=0, help="buffer sets to rotate (0 = enough for > 768 MB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this path needs no cross-GPU exchange (each GPU quantizes its own "
+              f"token shard), and runs on more than one GPU are not part of this build "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mxfp4_activation_rotation_amd as mxq
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mxq.load()
+    dev = torch.device("cuda:0")
+    wl = workloads.make_config(args.workload)
+    call_tokens = workloads.SHAPES[4][0] if args.workload == 4 else wl.tokens
+    C = wl.channels
+    elems = call_tokens * C
+    step_bytes = elems * BYTES_PER_ELEM
+
+    n_buf = args.buffers or max(2, int(np.ceil(768e6 / step_bytes)) + 1)
+    if args.workload == 4:
+        n_buf = wl.tokens // call_tokens  # the 256 distinct decode inputs
+    x_all = wl.x.to(dev)
+    xs = [x_all[i * call_tokens:(i + 1) * call_tokens] for i in range(n_buf)] if args.workload == 4 \
+        else [x_all] + [x_all.clone() for _ in range(n_buf - 1)]
+    lam = torch.from_numpy(wl.lam).to(dev) if wl.lam is not None else None
+    r = wl.r_hat.to(dev)
+    outs = [(torch.empty((call_tokens, C // 2), dtype=torch.uint8, device=dev),
+             torch.empty((call_tokens, C // 32), dtype=torch.uint8, device=dev)) for _ in range(n_buf)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        c, s = outs[i % n_buf]
+        mxq.rotate_quant(xs[i % n_buf], r, lam, codes=c, scales=s)
+
+    for i in range(args.warmup):
+        step(i)
+    # One event pair brackets the timed region on the launch stream (the
+    # binding launches on torch's current stream); events between launches
+    # would add several microseconds of queue work to every step.
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
+
+    achieved = step_bytes / mean_launch_s / 1e9
+    value = elems * args.steps / wall / 1e9
+    hbm = read_counters(args.workload)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.x.dtype == torch.bfloat16 else "fp16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "tokens": call_tokens, "channels": C,
+                   "x_dtype": str(wl.x.dtype).replace("torch.", ""), "lambda": wl.lam is not None,
+                   "r_hat": "bf16 32x32", "buffer_sets": n_buf, "parallelism": "single GPU"},
+        "hbm_gbps": round(value * BYTES_PER_ELEM, 1),
+        "pct_hbm_peak": round(100 * value * BYTES_PER_ELEM / HBM_PEAK_GBPS, 2),
+        "launch_us_mean": round(mean_launch_s * 1e6, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None if hbm is None else round(hbm)},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if args.workload == 4:
+        # decode-shaped calls: per-call latency, each call bracketed by its own
+        # event pair (outside the timed region above)
+        lat = []
+        for i in range(n_buf):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step(i)
+            e1.record()
+            e1.synchronize()
+            lat.append(e0.elapsed_time(e1) * 1e3)
+        result["call_latency_us"] = {"p50": round(float(np.percentile(lat, 50)), 2),
+                                     "p99": round(float(np.percentile(lat, 99)), 2), "calls": len(lat)}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -50,7 +50,7 @@
  *     x_row_stride * sizeof(element) must be a multiple of 16 (MXQ_ERR_ALIGN).
  *     scales and r_hat need only their natural alignment.
  *   - Limits: channels % 32 == 0, tokens and channels below 2^31, and
- *     tokens * ceil(channels / 1024) below 2^31 (MXQ_ERR_SHAPE).
+ *     tokens * ceil(channels / 2048) below 2^31 (MXQ_ERR_SHAPE).
  *   - NaN or infinite inputs are outside the contract (no error is raised,
  *     the output for such a group is unspecified).
  *   - The library holds no per-call state; calls are thread-safe.  Calls that

@@ -7,29 +7,33 @@
 // operator of sec. 5.2 item 1 and sec. 5.4 item 3, extended with the
 // quantization).
 //
-// Work decomposition.  A tile is 32 consecutive groups (1024 channels) of one
-// token row; one wave64 owns a tile at a time.  Lane l handles group j = l % 32
-// of the tile and half h = l / 32 of it.  The grid is persistent: each wave
-// keeps one tile column (so its lambda values stay in registers) and walks
-// down the rows with a fixed row step, prefetching the next batch of rows
-// while it computes the current one.
+// Work decomposition.  A wave owns a super-tile: 64 consecutive groups (2048
+// channels) of one token row, processed as four sub-tiles of 16 groups.  In a
+// sub-tile, lane l handles quarter q = l / 16 (channels 8q..8q+7) of group
+// j = l % 16, so each of the wave's four 16-byte loads per lane covers 1 KB
+// contiguously.  The grid is persistent: each wave keeps one super-tile
+// column (its lambda values stay in registers) and walks down the rows with a
+// fixed row step, keeping the next batch of rows in flight (non-temporal
+// loads: the activations are read exactly once).
 //
 // Rotation on the matrix cores (sec. 3.3 asks for the small dense product to
 // run on matrix hardware, and the pitfalls list, item 4, for a batched GEMM
 // over the [..., groups, 32] view rather than one big sparse product).  Per
-// tile we form Y^T = R^T X^T with v_mfma_f32_32x32x16_bf16, twice (k = 0..15,
-// 16..31):
-//   A operand = R^T with its rows permuted, register-resident for the kernel;
-//   B operand = the tile's activations, lane l supplying group l % 32 and
-//               channels 16 s + 8 h + (0..7) in step s -- exactly the two
-//               16-byte loads the lane makes;
-//   D         = lane (j, h), register r holds y[group j][16 h + r], because
-//               row i of A carries output channel pi(i), where the MFMA result
-//               layout puts row 8 (r / 4) + 4 h + (r % 4) in lane half h,
-//               register r.
-// So each lane ends with 16 contiguous rotated values of one group: the group
-// maximum is an in-lane max plus one v_permlane32_swap, and the lane packs 8
-// contiguous code bytes for a single 8-byte store.
+// sub-tile and bf16 term we form Y^T = R^T X^T with two
+// v_mfma_f32_16x16x32_bf16 (output channels split in two halves h = 0, 1):
+//   B operand = the sub-tile's activations: lane l supplies column (group)
+//               l % 16 and k-slots 8 (l / 16) + t -- the 8 channels it loaded;
+//   A operand = R^T with permuted rows, register-resident for the kernel:
+//               row i of MFMA h carries output channel 8 (i / 4) + 4 h + i % 4;
+//   D         = lane l, register r holds row 4 (l / 16) + r of column l % 16,
+//               i.e. output channel 8 q + 4 h + r of group j.
+// So each lane ends with the 8 contiguous rotated values y[8q .. 8q+7] of its
+// group: the group maximum is an in-lane max plus two cross-lane swaps
+// (lanes l ^ 32, l ^ 16), and the lane packs them into one 4-byte code word.
+// After the four sub-tiles, a 4x4 transpose of the code words across lanes
+// j, j+16, j+32, j+48 (two v_permlane32_swap, two v_permlane16_swap) leaves
+// lane l with all 16 code bytes of group l of the super-tile: the wave writes
+// 1 KB of codes and 64 scale bytes, both contiguous and in lane order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,15 +43,23 @@
 #include "mxq_device.h"
 
 #ifndef MXQ_WAVES_PER_CU
-#define MXQ_WAVES_PER_CU 16
+#define MXQ_WAVES_PER_CU 8
 #endif
 #ifndef MXQ_BATCH
 #define MXQ_BATCH 2
+#endif
+#ifndef MXQ_NT_LOAD
+#define MXQ_NT_LOAD 1
+#endif
+#ifndef MXQ_NT_STORE
+#define MXQ_NT_STORE 1
 #endif
 
 namespace mxq {
 
 constexpr int kGroup = 32;
+constexpr int kSub = 4;          // sub-tiles of 16 groups per super-tile
+constexpr int kTileGroups = 64;  // groups per wave super-tile
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = kWave * kWavesPerBlock;
@@ -66,34 +78,53 @@ struct Args {
     float* y;
     int32_t tokens;
     int32_t gpr;      // groups per row = channels / 32
-    int32_t tcols;    // tile columns = ceil(gpr / 32)
-    int32_t row_step; // waves per tile column
+    int32_t tcols;    // super-tile columns = ceil(gpr / 64)
+    int32_t row_step; // waves per super-tile column
     int32_t waves;    // tcols * row_step
 };
 
-// Output channel carried by row i of the A operand (see file comment).
-__device__ __forceinline__ int a_row_channel(int i) {
-    return ((i >> 2) & 1) * 16 + (i >> 3) * 4 + (i & 3);
+__device__ __forceinline__ u32x4_t load16(const void* p) {
+#if MXQ_NT_LOAD
+    return __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+#else
+    return *static_cast<const u32x4_t*>(p);
+#endif
 }
 
-template <int XT, int MODE>
-struct Loads {
-    // 16-byte loads per lane per tile and their element offsets in the row.
-    static constexpr int kN = (XT == kFP32) ? 4 : 2;
-    __device__ static int64_t base(int p, int h) {
-        return static_cast<int64_t>(p) * kGroup + (MODE == kRotate ? 8 * h : 16 * h);
+__device__ __forceinline__ void store_codes16(uint8_t* p, u32x4_t w) {
+#if MXQ_NT_STORE
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+#else
+    *reinterpret_cast<u32x4_t*>(p) = w;
+#endif
+}
+
+// 4x4 transpose of one register per sub-tile across the lanes j, j+16, j+32,
+// j+48: the word in lane 16 k + j, register s moves to lane 16 s + j,
+// register k.  Stage one exchanges lane bit 5 with register bit 1
+// (v_permlane32_swap swaps the upper 32 lanes of its first operand with the
+// lower 32 lanes of its second); stage two exchanges lane bit 4 with register
+// bit 0 (v_permlane16_swap swaps the odd 16-lane rows of its first operand
+// with the even rows of its second).
+__device__ __forceinline__ void transpose_words(uint32_t (&w)[4]) {
+#pragma unroll
+    for (int s0 = 0; s0 < 2; ++s0) {
+        const auto r = __builtin_amdgcn_permlane32_swap(w[s0], w[2 + s0], false, false);
+        w[s0] = r[0];
+        w[2 + s0] = r[1];
     }
-    __device__ static int step(int s) {
-        if constexpr (MODE == kRotate) return 16 * s;
-        else if constexpr (XT == kFP32) return 4 * s;
-        else return 8 * s;
+#pragma unroll
+    for (int s1 = 0; s1 < 2; ++s1) {
+        const auto r = __builtin_amdgcn_permlane16_swap(w[2 * s1], w[2 * s1 + 1], false, false);
+        w[2 * s1] = r[0];
+        w[2 * s1 + 1] = r[1];
     }
-};
+}
 
 template <int XT, int MODE, bool LAM, bool YOUT>
 __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
-    using L = Loads<XT, MODE>;
-    constexpr int kN = L::kN;
+    constexpr int kN = (XT == kFP32) ? 2 : 1;  // 16-byte loads per lane per sub-tile
+    constexpr int esz = (XT == kFP32) ? 4 : 2;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int w = static_cast<int>(blockIdx.x) * kWavesPerBlock + wave;
@@ -101,59 +132,71 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
     const int tc = w % a.tcols;
     const int64_t r0 = w / a.tcols;
     const int64_t rs = a.row_step;
-    const int j = lane & 31;
-    const int h = lane >> 5;
-    const int p = tc * kGroup + j;  // group index within the row
-    const bool valid = p < a.gpr;
+    const int j = lane & 15;
+    const int q = lane >> 4;
+    const int p0 = tc * kTileGroups;  // first group of the super-tile
+    // group handled in sub-tile s, and whether it exists
+    int ps[kSub];
+    bool vs[kSub];
+#pragma unroll
+    for (int s = 0; s < kSub; ++s) {
+        ps[s] = p0 + 16 * s + j;
+        vs[s] = ps[s] < a.gpr;
+    }
+    const int p_out = p0 + lane;  // group whose 16 code bytes this lane stores
+    const bool v_out = p_out < a.gpr;
 
-    // Rotation block as the MFMA A operand (two k-halves), bf16 bits.
+    // Rotation block as the A operands of the two output halves, bf16 bits:
+    // A_h[t] = R[8q + t][8 (j / 4) + 4 h + j % 4].
     bf16x8_t A0, A1;
     if constexpr (MODE == kRotate) {
-        const int n = a_row_channel(j);
+        const int n0 = 8 * (j >> 2) + (j & 3);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            A0[t] = __builtin_bit_cast(__bf16, a.r_hat[(8 * h + t) * kGroup + n]);
-            A1[t] = __builtin_bit_cast(__bf16, a.r_hat[(16 + 8 * h + t) * kGroup + n]);
+            A0[t] = __builtin_bit_cast(__bf16, a.r_hat[(8 * q + t) * kGroup + n0]);
+            A1[t] = __builtin_bit_cast(__bf16, a.r_hat[(8 * q + t) * kGroup + n0 + 4]);
         }
     }
-    // 1 / lambda for the 16 channels this lane feeds (fixed tile column).
-    float il[16];
+    // 1 / lambda for the 8 channels this lane feeds in each sub-tile.
+    float il[kSub][8];
     if constexpr (LAM) {
-        const int64_t c0 = L::base(p, h);
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < kSub; ++s)
 #pragma unroll
             for (int t = 0; t < 8; ++t)
-                il[8 * s + t] = valid ? 1.0f / a.lambda[c0 + 16 * s + t] : 0.0f;
+                il[s][t] = vs[s] ? 1.0f / a.lambda[static_cast<int64_t>(ps[s]) * kGroup + 8 * q + t] : 0.0f;
     }
 
     const char* xb = static_cast<const char*>(a.x);
-    constexpr int esz = (XT == kFP32) ? 4 : 2;
-    const int64_t lane_off = L::base(p, h);
-
-    auto load_rows = [&](u32x4_t (&buf)[kBatch][kN], int64_t r) {
+    auto load_rows = [&](u32x4_t (&buf)[kBatch][kSub][kN], int64_t r) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int64_t rr = r + u * rs;
+            const bool row_ok = rr < a.tokens;
+            const char* row = xb + rr * a.stride * esz;
 #pragma unroll
-            for (int s = 0; s < kN; ++s) buf[u][s] = u32x4_t{0u, 0u, 0u, 0u};
-            if (rr < a.tokens && valid) {
-                const char* row = xb + (rr * a.stride + lane_off) * esz;
+            for (int s = 0; s < kSub; ++s) {
 #pragma unroll
-                for (int s = 0; s < kN; ++s)
-                    buf[u][s] = *reinterpret_cast<const u32x4_t*>(row + static_cast<int64_t>(L::step(s)) * esz);
+                for (int k = 0; k < kN; ++k) buf[u][s][k] = u32x4_t{0u, 0u, 0u, 0u};
+                if (row_ok && vs[s]) {
+                    const char* src = row + (static_cast<int64_t>(ps[s]) * kGroup + 8 * q) * esz;
+#pragma unroll
+                    for (int k = 0; k < kN; ++k) buf[u][s][k] = load16(src + 16 * k);
+                }
             }
         }
     };
 
-    u32x4_t buf[kBatch][kN];
+    u32x4_t buf[kBatch][kSub][kN];
     load_rows(buf, r0);
     for (int64_t r = r0; r < a.tokens; r += kBatch * rs) {
-        u32x4_t cur[kBatch][kN];
+        u32x4_t cur[kBatch][kSub][kN];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
 #pragma unroll
-            for (int s = 0; s < kN; ++s) cur[u][s] = buf[u][s];
+            for (int s = 0; s < kSub; ++s)
+#pragma unroll
+                for (int k = 0; k < kN; ++k) cur[u][s][k] = buf[u][s][k];
         const int64_t rn = r + kBatch * rs;
         if (rn < a.tokens) load_rows(buf, rn);
 
@@ -161,66 +204,72 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
         for (int u = 0; u < kBatch; ++u) {
             const int64_t rr = r + u * rs;
             if (rr >= a.tokens) break;
-            float v[16];
-            if constexpr (MODE == kRotate) {
-                f32x16_t acc = {};
-                if constexpr (XT == kBF16 && !LAM) {
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, __builtin_bit_cast(bf16x8_t, cur[u][0]), acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, __builtin_bit_cast(bf16x8_t, cur[u][1]), acc, 0, 0, 0);
-                } else {
-                    // x' in fp32, then exact bf16 terms: 2 for fp16 x (11-bit
-                    // significand), 3 for x * (1/lambda) (24-bit significand).
-                    float f[16];
-                    widen8<XT == kFP16>(cur[u][0], f);
-                    widen8<XT == kFP16>(cur[u][1], f + 8);
-                    if constexpr (LAM) {
+            uint32_t word[kSub];
+            uint32_t sc[kSub];
 #pragma unroll
-                        for (int t = 0; t < 16; ++t) f[t] *= il[t];
+            for (int s = 0; s < kSub; ++s) {
+                float v[8];
+                if constexpr (MODE == kRotate) {
+                    f32x4_t d0 = {}, d1 = {};
+                    if constexpr (XT == kBF16 && !LAM) {
+                        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, cur[u][s][0]);
+                        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, b, d0, 0, 0, 0);
+                        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b, d1, 0, 0, 0);
+                    } else {
+                        // x' in fp32, then exact bf16 terms: 2 for fp16 x
+                        // (11-bit significand), 3 for x * (1/lambda) (24 bits).
+                        float f[8];
+                        widen8<XT == kFP16>(cur[u][s][0], f);
+                        if constexpr (LAM) {
+#pragma unroll
+                            for (int t = 0; t < 8; ++t) f[t] *= il[s][t];
+                        }
+                        constexpr int kTerms = LAM ? 3 : 2;
+#pragma unroll
+                        for (int term = 0; term < kTerms; ++term) {
+                            u32x4_t bt;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) bt[i] = bf16_pair_hi(f[2 * i], f[2 * i + 1]);
+                            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bt);
+                            d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, b, d0, 0, 0, 0);
+                            d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b, d1, 0, 0, 0);
+                            if (term + 1 < kTerms) {
+#pragma unroll
+                                for (int t = 0; t < 8; ++t) f[t] = bf16_residual(f[t]);
+                            }
+                        }
                     }
-                    constexpr int kTerms = LAM ? 3 : 2;
 #pragma unroll
-                    for (int term = 0; term < kTerms; ++term) {
-                        u32x4_t b0, b1;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            b0[i] = bf16_pair_hi(f[2 * i], f[2 * i + 1]);
-                            b1[i] = bf16_pair_hi(f[8 + 2 * i], f[8 + 2 * i + 1]);
-                        }
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A0, __builtin_bit_cast(bf16x8_t, b0), acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, __builtin_bit_cast(bf16x8_t, b1), acc, 0, 0, 0);
-                        if (term + 1 < kTerms) {
-#pragma unroll
-                            for (int t = 0; t < 16; ++t) f[t] = bf16_residual(f[t]);
-                        }
+                    for (int t = 0; t < 4; ++t) {
+                        v[t] = d0[t];
+                        v[4 + t] = d1[t];
+                    }
+                } else {
+                    if constexpr (XT == kFP32) {
+                        widen4_f32(cur[u][s][0], v);
+                        widen4_f32(cur[u][s][1], v + 4);
+                    } else {
+                        widen8<XT == kFP16>(cur[u][s][0], v);
                     }
                 }
-#pragma unroll
-                for (int t = 0; t < 16; ++t) v[t] = acc[t];
-            } else {
-                if constexpr (XT == kFP32) {
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) widen4_f32(cur[u][s], v + 4 * s);
-                } else {
-                    widen8<XT == kFP16>(cur[u][0], v);
-                    widen8<XT == kFP16>(cur[u][1], v + 8);
+                const float m = group_amax8(v);
+                sc[s] = e8m0_of_amax(m);
+                word[s] = encode8(v, as_f32(sc[s] << 23));
+                if constexpr (YOUT) {
+                    if (vs[s]) {
+                        float* yp = a.y + (rr * a.gpr + ps[s]) * kGroup + 8 * q;
+                        *reinterpret_cast<float4*>(yp) = float4{v[0], v[1], v[2], v[3]};
+                        *reinterpret_cast<float4*>(yp + 4) = float4{v[4], v[5], v[6], v[7]};
+                    }
                 }
             }
-
-            const float m = group_amax(v);
-            const uint32_t S = e8m0_of_amax(m);
-            const float scale = as_f32(S << 23);
-            const uint32_t lo = encode8(v, scale);
-            const uint32_t hi = encode8(v + 8, scale);
-            if (valid) {
-                const int64_t g = rr * a.gpr + p;
-                *reinterpret_cast<u32x2_t*>(a.codes + g * 16 + 8 * h) = u32x2_t{lo, hi};
-                if (h == 0) a.scales[g] = static_cast<uint8_t>(S);
-                if constexpr (YOUT) {
-                    float* yp = a.y + g * kGroup + 16 * h;
-#pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        *reinterpret_cast<float4*>(yp + 4 * s) = float4{v[4 * s], v[4 * s + 1], v[4 * s + 2], v[4 * s + 3]};
-                }
+            transpose_words(word);
+            // the scale of group 16 q + j is the one computed in sub-tile q
+            const uint32_t S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
+            if (v_out) {
+                const int64_t g = rr * a.gpr + p_out;
+                store_codes16(a.codes + g * 16, u32x4_t{word[0], word[1], word[2], word[3]});
+                a.scales[g] = static_cast<uint8_t>(S);
             }
         }
     }
@@ -275,17 +324,18 @@ struct Plan {
 
 constexpr int64_t kMaxI32 = 2147483647;
 
-// Grid for tokens x channels on cu_count CUs.  Target: MXQ_WAVES_PER_CU
-// resident waves per CU.  Waves share a tile column in groups of row_step;
-// among row steps between half and all of the target, pick the one whose
-// last round of rows leaves the fewest waves idle.
-static bool make_plan(int64_t tokens, int64_t channels, int cu_count, Plan* out) {
+// Grid for tokens x channels on cu_count CUs with at most waves_per_cu
+// resident waves per CU (the kernel's occupancy bound, so the persistent grid
+// runs in a single round).  Waves share a super-tile column in groups of
+// row_step; among row steps between half and all of the target, pick the one
+// whose last round of rows leaves the fewest waves idle.
+static bool make_plan(int64_t tokens, int64_t channels, int cu_count, int waves_per_cu, Plan* out) {
     if (tokens <= 0 || channels <= 0 || channels % kGroup) return false;
     if (tokens > kMaxI32 || channels > kMaxI32 - kGroup) return false;
     const int64_t gpr = channels / kGroup;
-    const int64_t tcols = (gpr + kGroup - 1) / kGroup;
+    const int64_t tcols = (gpr + kTileGroups - 1) / kTileGroups;
     if (tokens * tcols > kMaxI32) return false;
-    const int64_t target = static_cast<int64_t>(cu_count > 0 ? cu_count : 1) * MXQ_WAVES_PER_CU;
+    const int64_t target = static_cast<int64_t>(cu_count > 0 ? cu_count : 1) * (waves_per_cu > 0 ? waves_per_cu : 1);
     int64_t rs_max = target / tcols;
     if (rs_max < 1) rs_max = 1;
     if (rs_max > tokens) rs_max = tokens;
@@ -310,6 +360,12 @@ static bool make_plan(int64_t tokens, int64_t channels, int cu_count, Plan* out)
     return true;
 }
 
+// Shapes the launch plan accepts (no device query).
+static bool shape_ok(int64_t tokens, int64_t channels) {
+    Plan pl;
+    return make_plan(tokens, channels, 1, 1, &pl);
+}
+
 // Compute-unit count of the current device, queried once per device.
 static int device_cu_count() {
     static std::atomic<int> cache[64];
@@ -328,18 +384,43 @@ static bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintp
 
 static size_t dtype_size(int32_t dt) { return dt == MXQ_FP32 ? 4 : 2; }
 
+// Resident waves per CU the kernel instance allows (registers), queried once.
 template <int XT, int MODE, bool LAM, bool YOUT>
-static mxq_status launch(const Plan& pl, const Args& a, hipStream_t st) {
+static int occupancy_waves_per_cu() {
+    static std::atomic<int> cached{0};
+    int v = cached.load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, quant_kernel<XT, MODE, LAM, YOUT>, kBlockThreads, 0) !=
+            hipSuccess ||
+        blocks <= 0)
+        blocks = 1;
+    v = blocks * kWavesPerBlock;
+    cached.store(v, std::memory_order_relaxed);
+    return v;
+}
+
+template <int XT, int MODE, bool LAM, bool YOUT>
+static mxq_status launch(Args a, int64_t tokens, int64_t channels, hipStream_t st) {
+    const int occ = occupancy_waves_per_cu<XT, MODE, LAM, YOUT>();
+    Plan pl;
+    if (!make_plan(tokens, channels, device_cu_count(), occ < MXQ_WAVES_PER_CU ? occ : MXQ_WAVES_PER_CU, &pl))
+        return MXQ_ERR_SHAPE;
+    a.tcols = pl.tcols;
+    a.row_step = pl.row_step;
+    a.waves = pl.waves;
     hipLaunchKernelGGL((quant_kernel<XT, MODE, LAM, YOUT>), dim3(pl.blocks), dim3(kBlockThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 
 template <int XT>
-static mxq_status dispatch_rotate(const Plan& pl, const Args& a, hipStream_t st) {
+static mxq_status dispatch_rotate(const Args& a, int64_t tokens, int64_t channels, hipStream_t st) {
     if (a.lambda) {
-        return a.y ? launch<XT, kRotate, true, true>(pl, a, st) : launch<XT, kRotate, true, false>(pl, a, st);
+        return a.y ? launch<XT, kRotate, true, true>(a, tokens, channels, st)
+                   : launch<XT, kRotate, true, false>(a, tokens, channels, st);
     }
-    return a.y ? launch<XT, kRotate, false, true>(pl, a, st) : launch<XT, kRotate, false, false>(pl, a, st);
+    return a.y ? launch<XT, kRotate, false, true>(a, tokens, channels, st)
+               : launch<XT, kRotate, false, false>(a, tokens, channels, st);
 }
 
 static mxq_status check_common(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels,
@@ -362,12 +443,12 @@ static mxq_status rotate_impl(const void* x, int32_t x_dtype, int64_t tokens, in
     if (!aligned(x, 16) || (stride * 2) % 16 || !aligned(codes, 16) || !aligned(r_hat, 2) ||
         (lambda && !aligned(lambda, 16)) || (y && !aligned(y, 16)))
         return MXQ_ERR_ALIGN;
-    Plan pl;
-    if (!make_plan(tokens, channels, device_cu_count(), &pl)) return MXQ_ERR_SHAPE;
+    if (!shape_ok(tokens, channels)) return MXQ_ERR_SHAPE;
     Args a{x, stride, lambda, r_hat, codes, scales, y, static_cast<int32_t>(tokens),
-           static_cast<int32_t>(channels / kGroup), pl.tcols, pl.row_step, pl.waves};
+           static_cast<int32_t>(channels / kGroup), 0, 0, 0};
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return x_dtype == MXQ_BF16 ? dispatch_rotate<kBF16>(pl, a, st) : dispatch_rotate<kFP16>(pl, a, st);
+    return x_dtype == MXQ_BF16 ? dispatch_rotate<kBF16>(a, tokens, channels, st)
+                               : dispatch_rotate<kFP16>(a, tokens, channels, st);
 }
 
 }  // namespace mxq
@@ -399,15 +480,14 @@ mxq_status mxq_quant(const void* x, int32_t x_dtype, int64_t tokens, int64_t cha
     if (x_row_stride < channels) return MXQ_ERR_STRIDE;
     if (!aligned(x, 16) || (x_row_stride * static_cast<int64_t>(dtype_size(x_dtype))) % 16 || !aligned(codes, 16))
         return MXQ_ERR_ALIGN;
-    Plan pl;
-    if (!make_plan(tokens, channels, device_cu_count(), &pl)) return MXQ_ERR_SHAPE;
+    if (!shape_ok(tokens, channels)) return MXQ_ERR_SHAPE;
     Args a{x, x_row_stride, nullptr, nullptr, codes, scales, nullptr, static_cast<int32_t>(tokens),
-           static_cast<int32_t>(channels / kGroup), pl.tcols, pl.row_step, pl.waves};
+           static_cast<int32_t>(channels / kGroup), 0, 0, 0};
     hipStream_t st = static_cast<hipStream_t>(stream);
     switch (x_dtype) {
-        case MXQ_BF16: return launch<kBF16, kQuant, false, false>(pl, a, st);
-        case MXQ_FP16: return launch<kFP16, kQuant, false, false>(pl, a, st);
-        default: return launch<kFP32, kQuant, false, false>(pl, a, st);
+        case MXQ_BF16: return launch<kBF16, kQuant, false, false>(a, tokens, channels, st);
+        case MXQ_FP16: return launch<kFP16, kQuant, false, false>(a, tokens, channels, st);
+        default: return launch<kFP32, kQuant, false, false>(a, tokens, channels, st);
     }
 }
 
@@ -449,7 +529,7 @@ const char* mxq_status_str(int32_t status) {
 mxq_status mxq_plan(int64_t tokens, int64_t channels, int32_t cu_count, int32_t* out) {
     if (!out) return MXQ_ERR_NULL;
     Plan pl;
-    if (!make_plan(tokens, channels, cu_count, &pl)) return MXQ_ERR_SHAPE;
+    if (!make_plan(tokens, channels, cu_count, MXQ_WAVES_PER_CU, &pl)) return MXQ_ERR_SHAPE;
     out[0] = pl.blocks;
     out[1] = pl.waves;
     out[2] = pl.tcols;

@@ -15,28 +15,27 @@
 namespace mxq {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
 __device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
 
-// Largest |v| over the 32 values of a group whose two halves (16 values each)
-// sit in lanes l and l ^ 32 of the wave; every lane gets the group maximum.
-__device__ __forceinline__ float group_amax(const float* v) {
-    float m0 = fabsf(v[0]);
-    float m1 = fabsf(v[1]);
-#pragma unroll
-    for (int i = 2; i < 16; i += 2) {
-        m0 = fmaxf(m0, fabsf(v[i]));
-        m1 = fmaxf(m1, fabsf(v[i + 1]));
-    }
-    const uint32_t m = as_u32(fmaxf(m0, m1));
-    // v_permlane32_swap with both operands = m: lane l ends up holding
-    // m[l] and m[l ^ 32] in the two results.
-    const auto sw = __builtin_amdgcn_permlane32_swap(m, m, false, false);
-    return fmaxf(as_f32(sw[0]), as_f32(sw[1]));
+// Largest |v| of a group whose 32 values sit 8 per lane in lanes j, j+16,
+// j+32, j+48: in-lane max, then v_permlane32_swap and v_permlane16_swap with
+// both operands equal, each leaving x[l] and x[l ^ 32] (resp. l ^ 16) in the
+// two results.
+__device__ __forceinline__ float group_amax8(const float* v) {
+    float m0 = fmaxf(fabsf(v[0]), fabsf(v[1]));
+    float m1 = fmaxf(fabsf(v[2]), fabsf(v[3]));
+    m0 = fmaxf(m0, fmaxf(fabsf(v[4]), fabsf(v[5])));
+    m1 = fmaxf(m1, fmaxf(fabsf(v[6]), fabsf(v[7])));
+    uint32_t m = as_u32(fmaxf(m0, m1));
+    const auto s32 = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+    m = as_u32(fmaxf(as_f32(s32[0]), as_f32(s32[1])));
+    const auto s16 = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+    return fmaxf(as_f32(s16[0]), as_f32(s16[1]));
 }
 
 // E8M0 scale byte for a group maximum m (finite, m >= 0):

@@ -102,7 +102,7 @@ def test_quant_and_dequant_validation(lib):
 def test_plan_covers_every_tile_once(T, C, cu):
     pl = mxq.plan(T, C, cu)
     tcols, rs, waves = pl["tile_columns"], pl["row_step"], pl["waves"]
-    assert tcols == -(-(C // 32) // 32)
+    assert tcols == -(-(C // 32) // 64)
     assert waves == tcols * rs and 1 <= rs <= T
     assert pl["blocks"] * pl["waves_per_block"] >= waves > (pl["blocks"] - 1) * pl["waves_per_block"]
     seen = {}

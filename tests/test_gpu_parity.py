@@ -292,3 +292,43 @@ def test_dequant_round_trip(dev, orc):
     # re-quantizing the decoded tensor returns the same codes and scales
     c2, s2 = mxq.quant(dq)
     assert torch.equal(c2, codes) and torch.equal(s2, scales)
+
+
+# ---- error study (reported, not asserted) --------------------------------------
+
+def test_error_study_config5(dev, orc):
+    """Per-group normalized MXFP4 error ||dq_g - y_g|| / ||y_g|| (the quantity
+    of the DuQuant++ page's Figure 1) on the large-prefill workload for the
+    identity block, a seeded random Hadamard block and the outlier-aware
+    block, all with the same smoothing.  The page prints no values, so the
+    numbers are only reported; the GPU figures are cross-checked against the
+    fp64 oracle on a row sample."""
+    wl = W.make_config(5)
+    xd, lam_d, _ = _to_dev(wl.x, wl.lam, wl.r_hat, dev)
+    blocks = {"identity": W.identity_r(),
+              "random_hadamard": W.bf16_matrix(W.random_hadamard(np.random.default_rng(2005))),
+              "outlier_householder": wl.r_hat}
+    rows = np.sort(np.random.default_rng(2006).choice(wl.tokens, 256, replace=False))
+    report = {}
+    for name, r in blocks.items():
+        y = torch.empty(wl.x.shape, dtype=torch.float32, device=dev)
+        codes, scales = mxq.rotate_quant(xd, r.to(dev), lam_d, y_rot=y)
+        dq = mxq.dequant(codes, scales, torch.float32)
+        yg = y.view(-1, GROUP).double()
+        ny = yg.norm(dim=1)
+        keep = ny > 0
+        eps = ((dq.view(-1, GROUP).double() - yg).norm(dim=1)[keep] / ny[keep])
+        mean, p99 = float(eps.mean()), float(torch.quantile(eps[::16].float(), 0.99))
+        # oracle cross-check on a row sample
+        xs = wl.x[torch.from_numpy(rows)].contiguous()
+        c_ref, s_ref, y_ref = orc.rotate_quant(xs, wl.lam, r, want_y=True)
+        e_ref = O.group_error(y_ref, orc.dequant(c_ref, s_ref))
+        sel = torch.from_numpy(rows).to(dev)
+        e_gpu = eps.view(wl.tokens, -1)[sel].cpu().numpy().reshape(-1) if bool(keep.all()) else None
+        if e_gpu is not None:
+            assert abs(e_gpu.mean() - e_ref.mean()) <= 1e-3 * e_ref.mean() + 1e-6
+        report[name] = {"mean": round(mean, 5), "p99": round(p99, 5), "oracle_sample_mean": round(float(e_ref.mean()), 5)}
+        assert np.isfinite(mean) and 0 < mean < 1
+        del y, dq, codes, scales
+        torch.cuda.empty_cache()
+    print(f"  error study, config 5 (k={wl.meta['k']}): {report}", flush=True)
