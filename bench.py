@@ -102,6 +102,9 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4, 5],
                     help="workload id (3 = the headline down_proj-input batch)")
     ap.add_argument("--buffers", type=int, default=0, help="buffer sets to rotate (0 = enough for > 768 MB)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the K timed launches once as a HIP graph and time one replay "
+                         "(how decode-shaped loops are driven; removes per-call host overhead)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -148,6 +151,20 @@ def main():
 
     for i in range(args.warmup):
         step(i)
+    graph = None
+    if args.graph:
+        # Capture exactly the K timed launches (same buffers, same order).
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        capture_stream = torch.cuda.Stream()
+        capture_stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(capture_stream):
+            graph.capture_begin()
+            for i in range(args.steps):
+                step(args.warmup + i)
+            graph.capture_end()
+        torch.cuda.current_stream().wait_stream(capture_stream)
+        graph.replay()  # one untimed replay after capture
     # One event pair brackets the timed region on the launch stream (the
     # binding launches on torch's current stream); events between launches
     # would add several microseconds of queue work to every step.
@@ -156,8 +173,11 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(args.warmup + i)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -181,7 +201,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[args.workload], "tokens": call_tokens, "channels": C,
                    "x_dtype": str(wl.x.dtype).replace("torch.", ""), "lambda": wl.lam is not None,
-                   "r_hat": "bf16 32x32", "buffer_sets": n_buf, "parallelism": "single GPU"},
+                   "r_hat": "bf16 32x32", "buffer_sets": n_buf, "parallelism": "single GPU",
+                   "launch": "hip graph of the K launches" if args.graph else "eager launches"},
         "hbm_gbps": round(value * BYTES_PER_ELEM, 1),
         "pct_hbm_peak": round(100 * value * BYTES_PER_ELEM / HBM_PEAK_GBPS, 2),
         "launch_us_mean": round(mean_launch_s * 1e6, 3),

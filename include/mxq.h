@@ -49,8 +49,8 @@
  *   - Pointers x, codes, y_rot, y and lambda must be 16-byte aligned, and
  *     x_row_stride * sizeof(element) must be a multiple of 16 (MXQ_ERR_ALIGN).
  *     scales and r_hat need only their natural alignment.
- *   - Limits: channels % 32 == 0, tokens and channels below 2^31, and
- *     tokens * ceil(channels / 2048) below 2^31 (MXQ_ERR_SHAPE).
+ *   - Limits: channels % 32 == 0, tokens below 2^31, channels at most 2^28,
+ *     and tokens * ceil(channels / 2048) below 2^31 (MXQ_ERR_SHAPE).
  *   - NaN or infinite inputs are outside the contract (no error is raised,
  *     the output for such a group is unspecified).
  *   - The library holds no per-call state; calls are thread-safe.  Calls that
@@ -87,8 +87,10 @@ typedef enum { MXQ_BF16 = 0, MXQ_FP16 = 1, MXQ_FP32 = 2 } mxq_dtype;
  * The rotation runs on the matrix cores with bf16 operands and fp32
  * accumulation.  The activations are split into bf16 terms whose sum is
  * exactly the fp32 value of x' (bf16 x: 1 term; fp16 x: 2 terms; with lambda:
- * 3 terms of x * (1/lambda) rounded to fp32), so products are exact and only
- * the fp32 accumulation rounds. */
+ * 3 terms of x' = x * rcp(lambda), rcp the hardware reciprocal, within 1 ulp),
+ * so the products are exact and only the fp32 accumulation rounds.
+ * lambda entries must be finite normal fp32 values with |lambda| in
+ * [2^-126, 2^126]; others give unspecified codes for their groups. */
 mxq_status mxq_rotate_quant(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
                             int64_t x_row_stride, const float *lambda, const uint16_t *r_hat,
                             uint8_t *codes, uint8_t *scales, void *stream);

@@ -67,23 +67,35 @@ def load(path: str | None = None) -> ctypes.CDLL:
 _DT = {torch.bfloat16: MXQ_BF16, torch.float16: MXQ_FP16, torch.float32: MXQ_FP32}
 
 
+try:  # raw current-stream handle without building a Stream object
+    _raw_stream = torch._C._cuda_getCurrentRawStream
+except AttributeError:  # pragma: no cover
+    _raw_stream = None
+
+
 def _stream(t: torch.Tensor, stream):
-    s = stream if stream is not None else torch.cuda.current_stream(t.device)
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(t.device.index)
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    return t.data_ptr() if t is not None else None
 
 
 def _check_x(x: torch.Tensor, allowed):
-    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
         raise ValueError("x must be a device tensor")
-    if x.dim() != 2 or (x.shape[0] > 0 and x.shape[1] > 0 and x.stride(1) != 1):
-        raise ValueError("x must be 2-D [tokens, channels] with unit column stride")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [tokens, channels]")
+    T, C = x.shape
+    if T > 0 and C > 0 and x.stride(1) != 1:
+        raise ValueError("x must have unit column stride")
     if x.dtype not in allowed:
         raise ValueError(f"unsupported x dtype {x.dtype}")
-    return x.shape[0], x.shape[1], (x.stride(0) if x.shape[0] > 1 else x.shape[1])
+    return T, C, (x.stride(0) if T > 1 else C)
 
 
 def _outputs(x, T, C, codes, scales):
@@ -92,7 +104,7 @@ def _outputs(x, T, C, codes, scales):
     if scales is None:
         scales = torch.empty((T, C // 32), dtype=torch.uint8, device=x.device)
     for name, t, shape in (("codes", codes, (T, C // 2)), ("scales", scales, (T, C // 32))):
-        if t.dtype != torch.uint8 or tuple(t.shape) != shape or not t.is_contiguous() or t.device != x.device:
+        if t.dtype != torch.uint8 or t.shape != shape or not t.is_contiguous() or t.device != x.device:
             raise ValueError(f"{name} must be a contiguous uint8 tensor of shape {shape} on {x.device}")
     return codes, scales
 
@@ -108,15 +120,15 @@ def rotate_quant(x: torch.Tensor, r_hat: torch.Tensor, lam: torch.Tensor | None 
     """
     lib = load()
     T, C, stride = _check_x(x, (torch.bfloat16, torch.float16))
-    if r_hat.dtype != torch.bfloat16 or tuple(r_hat.shape) != (32, 32) or not r_hat.is_contiguous() \
+    if r_hat.dtype != torch.bfloat16 or r_hat.shape != (32, 32) or not r_hat.is_contiguous() \
             or r_hat.device != x.device:
         raise ValueError("r_hat must be a contiguous bf16 [32, 32] tensor on x's device")
-    if lam is not None and (lam.dtype != torch.float32 or tuple(lam.shape) != (C,) or not lam.is_contiguous()
+    if lam is not None and (lam.dtype != torch.float32 or lam.shape != (C,) or not lam.is_contiguous()
                             or lam.device != x.device):
         raise ValueError("lam must be a contiguous fp32 [channels] tensor on x's device")
     codes, scales = _outputs(x, T, C, codes, scales)
     if y_rot is not None:
-        if y_rot.dtype != torch.float32 or tuple(y_rot.shape) != (T, C) or not y_rot.is_contiguous():
+        if y_rot.dtype != torch.float32 or y_rot.shape != (T, C) or not y_rot.is_contiguous():
             raise ValueError("y_rot must be a contiguous fp32 [tokens, channels] tensor")
         st = lib.mxq_rotate_quant_ex(_ptr(x), _DT[x.dtype], T, C, stride, _ptr(lam), _ptr(r_hat),
                                      _ptr(codes), _ptr(scales), _ptr(y_rot), _stream(x, stream))

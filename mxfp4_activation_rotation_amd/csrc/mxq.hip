@@ -42,11 +42,20 @@
 #include "../../include/mxq.h"
 #include "mxq_device.h"
 
+// Resident waves per CU and rows in flight per wave: one setting for the
+// single-term kernels (bf16 rotate, plain quantization), one for the kernels
+// that split activations into several bf16 terms (fp16 and/or lambda).
 #ifndef MXQ_WAVES_PER_CU
 #define MXQ_WAVES_PER_CU 8
 #endif
 #ifndef MXQ_BATCH
-#define MXQ_BATCH 2
+#define MXQ_BATCH 1
+#endif
+#ifndef MXQ_WAVES_PER_CU_SPLIT
+#define MXQ_WAVES_PER_CU_SPLIT 16
+#endif
+#ifndef MXQ_BATCH_SPLIT
+#define MXQ_BATCH_SPLIT 1
 #endif
 #ifndef MXQ_NT_LOAD
 #define MXQ_NT_LOAD 1
@@ -63,7 +72,14 @@ constexpr int kTileGroups = 64;  // groups per wave super-tile
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = kWave * kWavesPerBlock;
-constexpr int kBatch = MXQ_BATCH;  // rows in flight per wave
+
+// Does this kernel instance split the activations into several bf16 terms?
+template <int XT, int MODE, bool LAM>
+constexpr bool kSplit = MODE == 1 && (XT != MXQ_BF16 || LAM);
+template <int XT, int MODE, bool LAM>
+constexpr int kBatchOf = kSplit<XT, MODE, LAM> ? MXQ_BATCH_SPLIT : MXQ_BATCH;  // rows in flight per wave
+template <int XT, int MODE, bool LAM>
+constexpr int kWavesPerCuOf = kSplit<XT, MODE, LAM> ? MXQ_WAVES_PER_CU_SPLIT : MXQ_WAVES_PER_CU;
 
 enum : int { kBF16 = MXQ_BF16, kFP16 = MXQ_FP16, kFP32 = MXQ_FP32 };
 enum : int { kQuant = 0, kRotate = 1 };
@@ -83,21 +99,14 @@ struct Args {
     int32_t waves;    // tcols * row_step
 };
 
-__device__ __forceinline__ u32x4_t load16(const void* p) {
-#if MXQ_NT_LOAD
-    return __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
-#else
-    return *static_cast<const u32x4_t*>(p);
-#endif
+// Buffer resource for `bytes` bytes at `base` (raw buffer, stride 0): loads
+// beyond `bytes` return zero and stores beyond it are dropped, which is how
+// lanes of groups past the end of a row are handled without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
 }
 
-__device__ __forceinline__ void store_codes16(uint8_t* p, u32x4_t w) {
-#if MXQ_NT_STORE
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
-#else
-    *reinterpret_cast<u32x4_t*>(p) = w;
-#endif
-}
+constexpr int kAuxNT = 2;  // cache policy bits of buffer ops: non-temporal
 
 // 4x4 transpose of one register per sub-tile across the lanes j, j+16, j+32,
 // j+48: the word in lane 16 k + j, register s moves to lane 16 s + j,
@@ -124,7 +133,8 @@ __device__ __forceinline__ void transpose_words(uint32_t (&w)[4]) {
 template <int XT, int MODE, bool LAM, bool YOUT>
 __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
     constexpr int kN = (XT == kFP32) ? 2 : 1;  // 16-byte loads per lane per sub-tile
-    constexpr int esz = (XT == kFP32) ? 4 : 2;
+    constexpr uint32_t esz = (XT == kFP32) ? 4 : 2;
+    constexpr int kBatch = kBatchOf<XT, MODE, LAM>;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int w = static_cast<int>(blockIdx.x) * kWavesPerBlock + wave;
@@ -132,20 +142,45 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
     const int tc = w % a.tcols;
     const int64_t r0 = w / a.tcols;
     const int64_t rs = a.row_step;
+    const int64_t T = a.tokens;
     const int j = lane & 15;
     const int q = lane >> 4;
     const int p0 = tc * kTileGroups;  // first group of the super-tile
-    // group handled in sub-tile s, and whether it exists
-    int ps[kSub];
-    bool vs[kSub];
-#pragma unroll
-    for (int s = 0; s < kSub; ++s) {
-        ps[s] = p0 + 16 * s + j;
-        vs[s] = ps[s] < a.gpr;
-    }
-    const int p_out = p0 + lane;  // group whose 16 code bytes this lane stores
-    const bool v_out = p_out < a.gpr;
+    const uint32_t gpr = static_cast<uint32_t>(a.gpr);
 
+    // Byte offsets inside a row: the 8 channels (8q..8q+7) of group p0+16s+j
+    // that this lane loads in sub-tile s, and the group p0+lane whose codes
+    // and scale it stores.  Groups past the row end fall outside the row's
+    // buffer range: their loads read zero and their stores are dropped.
+    uint32_t xoff[kSub];
+#pragma unroll
+    for (int s = 0; s < kSub; ++s) xoff[s] = (static_cast<uint32_t>(p0 + 16 * s + j) * kGroup + 8 * q) * esz;
+    const uint32_t row_bytes = gpr * kGroup * esz;
+    const uint32_t code_off = static_cast<uint32_t>(p0 + lane) * 16;
+    const uint32_t scale_off = static_cast<uint32_t>(p0 + lane);
+    const char* xb = static_cast<const char*>(a.x);
+
+    typedef u32x4_t Rows[kBatch][kSub][kN];
+    auto load_rows = [&](Rows& buf, int64_t r) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t rr = r + u * rs;
+            if (rr < T) {
+                const auto rsrc = row_rsrc(xb + rr * a.stride * esz, row_bytes);
+#pragma unroll
+                for (int s = 0; s < kSub; ++s)
+#pragma unroll
+                    for (int k = 0; k < kN; ++k)
+                        buf[u][s][k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, xoff[s] + 16 * k, 0,
+                                                                             MXQ_NT_LOAD ? kAuxNT : 0);
+            }
+        }
+    };
+
+    Rows bufA, bufB;
+    load_rows(bufA, r0);
+
+    // Block and smoothing factors are set up while the first rows load.
     // Rotation block as the A operands of the two output halves, bf16 bits:
     // A_h[t] = R[8q + t][8 (j / 4) + 4 h + j % 4].
     bf16x8_t A0, A1;
@@ -157,53 +192,30 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
             A1[t] = __builtin_bit_cast(__bf16, a.r_hat[(8 * q + t) * kGroup + n0 + 4]);
         }
     }
-    // 1 / lambda for the 8 channels this lane feeds in each sub-tile.
+    // 1 / lambda for the 8 channels this lane feeds in each sub-tile
+    // (v_rcp_f32, within 1 ulp).  Lanes of groups past the row end get 0.
     float il[kSub][8];
     if constexpr (LAM) {
+        const auto lrsrc = row_rsrc(a.lambda, gpr * kGroup * 4);
 #pragma unroll
-        for (int s = 0; s < kSub; ++s)
+        for (int s = 0; s < kSub; ++s) {
+            const uint32_t off = (static_cast<uint32_t>(p0 + 16 * s + j) * kGroup + 8 * q) * 4;
+            const u32x4_t l0 = __builtin_amdgcn_raw_buffer_load_b128(lrsrc, off, 0, 0);
+            const u32x4_t l1 = __builtin_amdgcn_raw_buffer_load_b128(lrsrc, off + 16, 0, 0);
+            const bool valid = p0 + 16 * s + j < a.gpr;
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
-                il[s][t] = vs[s] ? 1.0f / a.lambda[static_cast<int64_t>(ps[s]) * kGroup + 8 * q + t] : 0.0f;
-    }
-
-    const char* xb = static_cast<const char*>(a.x);
-    auto load_rows = [&](u32x4_t (&buf)[kBatch][kSub][kN], int64_t r) {
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int64_t rr = r + u * rs;
-            const bool row_ok = rr < a.tokens;
-            const char* row = xb + rr * a.stride * esz;
-#pragma unroll
-            for (int s = 0; s < kSub; ++s) {
-#pragma unroll
-                for (int k = 0; k < kN; ++k) buf[u][s][k] = u32x4_t{0u, 0u, 0u, 0u};
-                if (row_ok && vs[s]) {
-                    const char* src = row + (static_cast<int64_t>(ps[s]) * kGroup + 8 * q) * esz;
-#pragma unroll
-                    for (int k = 0; k < kN; ++k) buf[u][s][k] = load16(src + 16 * k);
-                }
+            for (int t = 0; t < 4; ++t) {
+                il[s][t] = valid ? __builtin_amdgcn_rcpf(as_f32(l0[t])) : 0.0f;
+                il[s][4 + t] = valid ? __builtin_amdgcn_rcpf(as_f32(l1[t])) : 0.0f;
             }
         }
-    };
+    }
 
-    u32x4_t buf[kBatch][kSub][kN];
-    load_rows(buf, r0);
-    for (int64_t r = r0; r < a.tokens; r += kBatch * rs) {
-        u32x4_t cur[kBatch][kSub][kN];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u)
-#pragma unroll
-            for (int s = 0; s < kSub; ++s)
-#pragma unroll
-                for (int k = 0; k < kN; ++k) cur[u][s][k] = buf[u][s][k];
-        const int64_t rn = r + kBatch * rs;
-        if (rn < a.tokens) load_rows(buf, rn);
-
+    auto process_rows = [&](const Rows& buf, int64_t r) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int64_t rr = r + u * rs;
-            if (rr >= a.tokens) break;
+            if (rr >= T) break;
             uint32_t word[kSub];
             uint32_t sc[kSub];
 #pragma unroll
@@ -212,14 +224,14 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
                 if constexpr (MODE == kRotate) {
                     f32x4_t d0 = {}, d1 = {};
                     if constexpr (XT == kBF16 && !LAM) {
-                        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, cur[u][s][0]);
+                        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, buf[u][s][0]);
                         d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, b, d0, 0, 0, 0);
                         d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b, d1, 0, 0, 0);
                     } else {
                         // x' in fp32, then exact bf16 terms: 2 for fp16 x
                         // (11-bit significand), 3 for x * (1/lambda) (24 bits).
                         float f[8];
-                        widen8<XT == kFP16>(cur[u][s][0], f);
+                        widen8<XT == kFP16>(buf[u][s][0], f);
                         if constexpr (LAM) {
 #pragma unroll
                             for (int t = 0; t < 8; ++t) f[t] *= il[s][t];
@@ -246,32 +258,44 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
                     }
                 } else {
                     if constexpr (XT == kFP32) {
-                        widen4_f32(cur[u][s][0], v);
-                        widen4_f32(cur[u][s][1], v + 4);
+                        widen4_f32(buf[u][s][0], v);
+                        widen4_f32(buf[u][s][1], v + 4);
                     } else {
-                        widen8<XT == kFP16>(cur[u][s][0], v);
+                        widen8<XT == kFP16>(buf[u][s][0], v);
                     }
                 }
-                const float m = group_amax8(v);
-                sc[s] = e8m0_of_amax(m);
-                word[s] = encode8(v, as_f32(sc[s] << 23));
+                const uint32_t scale_bits = e8m0_scale_bits(group_amax8(v));
+                sc[s] = scale_bits >> 23;
+                word[s] = encode8(v, as_f32(scale_bits));
                 if constexpr (YOUT) {
-                    if (vs[s]) {
-                        float* yp = a.y + (rr * a.gpr + ps[s]) * kGroup + 8 * q;
-                        *reinterpret_cast<float4*>(yp) = float4{v[0], v[1], v[2], v[3]};
-                        *reinterpret_cast<float4*>(yp + 4) = float4{v[4], v[5], v[6], v[7]};
-                    }
+                    const auto yrsrc = row_rsrc(a.y + rr * a.gpr * kGroup, gpr * kGroup * 4);
+                    const uint32_t off = (static_cast<uint32_t>(p0 + 16 * s + j) * kGroup + 8 * q) * 4;
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        u32x4_t{as_u32(v[0]), as_u32(v[1]), as_u32(v[2]), as_u32(v[3])}, yrsrc, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        u32x4_t{as_u32(v[4]), as_u32(v[5]), as_u32(v[6]), as_u32(v[7])}, yrsrc, off + 16, 0, 0);
                 }
             }
             transpose_words(word);
             // the scale of group 16 q + j is the one computed in sub-tile q
             const uint32_t S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
-            if (v_out) {
-                const int64_t g = rr * a.gpr + p_out;
-                store_codes16(a.codes + g * 16, u32x4_t{word[0], word[1], word[2], word[3]});
-                a.scales[g] = static_cast<uint8_t>(S);
-            }
+            const auto crsrc = row_rsrc(a.codes + rr * a.gpr * 16, gpr * 16);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{word[0], word[1], word[2], word[3]}, crsrc, code_off, 0,
+                                                   MXQ_NT_STORE ? kAuxNT : 0);
+            const auto srsrc = row_rsrc(a.scales + rr * a.gpr, gpr);
+            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, scale_off, 0, 0);
         }
+    };
+
+    // Two row buffers alternate: the next batch is in flight while the
+    // current one is computed.
+    const int64_t step = kBatch * rs;
+    for (int64_t r = r0; r < T; r += 2 * step) {
+        if (r + step < T) load_rows(bufB, r + step);
+        process_rows(bufA, r);
+        if (r + step >= T) break;
+        if (r + 2 * step < T) load_rows(bufA, r + 2 * step);
+        process_rows(bufB, r + step);
     }
 }
 
@@ -323,6 +347,9 @@ struct Plan {
 };
 
 constexpr int64_t kMaxI32 = 2147483647;
+// Row byte counts (up to 4 bytes per channel) must fit a buffer resource's
+// 32-bit record count.
+constexpr int64_t kMaxChannels = int64_t(1) << 28;
 
 // Grid for tokens x channels on cu_count CUs with at most waves_per_cu
 // resident waves per CU (the kernel's occupancy bound, so the persistent grid
@@ -331,7 +358,7 @@ constexpr int64_t kMaxI32 = 2147483647;
 // whose last round of rows leaves the fewest waves idle.
 static bool make_plan(int64_t tokens, int64_t channels, int cu_count, int waves_per_cu, Plan* out) {
     if (tokens <= 0 || channels <= 0 || channels % kGroup) return false;
-    if (tokens > kMaxI32 || channels > kMaxI32 - kGroup) return false;
+    if (tokens > kMaxI32 || channels > kMaxChannels) return false;
     const int64_t gpr = channels / kGroup;
     const int64_t tcols = (gpr + kTileGroups - 1) / kTileGroups;
     if (tokens * tcols > kMaxI32) return false;
@@ -404,8 +431,8 @@ template <int XT, int MODE, bool LAM, bool YOUT>
 static mxq_status launch(Args a, int64_t tokens, int64_t channels, hipStream_t st) {
     const int occ = occupancy_waves_per_cu<XT, MODE, LAM, YOUT>();
     Plan pl;
-    if (!make_plan(tokens, channels, device_cu_count(), occ < MXQ_WAVES_PER_CU ? occ : MXQ_WAVES_PER_CU, &pl))
-        return MXQ_ERR_SHAPE;
+    constexpr int want = kWavesPerCuOf<XT, MODE, LAM>;
+    if (!make_plan(tokens, channels, device_cu_count(), occ < want ? occ : want, &pl)) return MXQ_ERR_SHAPE;
     a.tcols = pl.tcols;
     a.row_step = pl.row_step;
     a.waves = pl.waves;
@@ -496,7 +523,7 @@ mxq_status mxq_dequant(const uint8_t* codes, const uint8_t* scales, int64_t toke
     if (y_dtype != MXQ_BF16 && y_dtype != MXQ_FP32) return MXQ_ERR_DTYPE;
     if (tokens < 0 || channels < 0 || channels % kGroup) return MXQ_ERR_SHAPE;
     if (tokens == 0 || channels == 0) return MXQ_OK;
-    if (tokens > kMaxI32 || channels > kMaxI32 - kGroup) return MXQ_ERR_SHAPE;
+    if (tokens > kMaxI32 || channels > kMaxChannels) return MXQ_ERR_SHAPE;
     if (!codes || !scales || !y) return MXQ_ERR_NULL;
     if (!aligned(codes, 16) || !aligned(y, 16)) return MXQ_ERR_ALIGN;
     const int64_t halves = tokens * (channels / kGroup) * 2;

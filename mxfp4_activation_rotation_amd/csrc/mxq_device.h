@@ -38,14 +38,16 @@ __device__ __forceinline__ float group_amax8(const float* v) {
     return fmaxf(as_f32(s16[0]), as_f32(s16[1]));
 }
 
-// E8M0 scale byte for a group maximum m (finite, m >= 0):
-// S = clamp(floor(log2 m) - 2, -127, 127) + 127.  For a normal fp32 m,
-// floor(log2 m) is its biased exponent field minus 127, so S = field - 2.
-// Subnormal or zero m has field 0, and fields 1 and 2 also clamp, giving
-// S = 0 (e = -127).  A finite fp32 never gives S above 252.
-__device__ __forceinline__ uint32_t e8m0_of_amax(float m) {
-    const int field = static_cast<int>(as_u32(m) >> 23);
-    return static_cast<uint32_t>(field > 2 ? field - 2 : 0);
+// E8M0 scale of a group maximum m (finite, m >= 0), returned as S << 23, with
+// S = clamp(floor(log2 m) - 2, -127, 127) + 127.  As an fp32 pattern that is
+// 2^(S-127) for S >= 1 and +0.0 for S = 0; the FP4 converter reads only the
+// exponent field, so both mean 2^(S-127) to it.  For a normal fp32 m,
+// floor(log2 m) is its biased exponent field minus 127, so S = field - 2;
+// subnormal or zero m (field 0) and fields 1 and 2 clamp to S = 0.  One
+// saturating subtract on the exponent bits does both.  A finite fp32 never
+// gives S above 252.
+__device__ __forceinline__ uint32_t e8m0_scale_bits(float m) {
+    return __builtin_elementwise_sub_sat(as_u32(m) & 0x7f800000u, 2u << 23);
 }
 
 // A code nibble whose magnitude bits are 0 is made +0 (0x0): the gfx950

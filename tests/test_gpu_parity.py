@@ -332,3 +332,50 @@ def test_error_study_config5(dev, orc):
         del y, dq, codes, scales
         torch.cuda.empty_cache()
     print(f"  error study, config 5 (k={wl.meta['k']}): {report}", flush=True)
+
+
+def test_graph_capture_replays(dev):
+    """The entry points launch no allocation, memset or synchronization, so a
+    HIP graph of several calls replays correctly: every replay (with eager
+    work and synchronizations between replays) matches the eager results."""
+    wl = W.make_config(2)
+    xd, lam_d, rd = _to_dev(wl.x, wl.lam, wl.r_hat, dev)
+    halves = [xd[:1024], xd[1024:]]
+    outs = [(torch.empty((1024, wl.channels // 2), dtype=torch.uint8, device=dev),
+             torch.empty((1024, wl.channels // GROUP), dtype=torch.uint8, device=dev)) for _ in halves]
+    eager = [mxq.rotate_quant(h, rd, lam_d) for h in halves]
+    eager_q = mxq.quant(xd)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    qc = torch.empty_like(eager_q[0])
+    qs = torch.empty_like(eager_q[1])
+    with torch.cuda.stream(s):
+        g.capture_begin()
+        for h, (c, sc) in zip(halves, outs):
+            mxq.rotate_quant(h, rd, lam_d, codes=c, scales=sc)
+        mxq.quant(xd, codes=qc, scales=qs)
+        g.capture_end()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        for c, sc in outs:  # eager work between replays
+            c.zero_()
+            sc.zero_()
+        qc.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for (c, sc), (ce, se) in zip(outs, eager):
+            assert torch.equal(c, ce) and torch.equal(sc, se), f"replay {rep} differs"
+        assert torch.equal(qc, eager_q[0]) and torch.equal(qs, eager_q[1])
+
+
+def test_fp16_without_lambda_two_terms(dev, orc):
+    """fp16 activations without smoothing (two exact bf16 terms) through a
+    real block, on a row sample of the large-prefill workload."""
+    wl = W.make_config(5)
+    rows = np.sort(np.random.default_rng(107).choice(wl.tokens, 1024, replace=False))
+    xs = wl.x[torch.from_numpy(rows)].contiguous()
+    full_fused_check(xs, None, wl.r_hat, dev, orc)
+    full_fused_check(xs, None, W.make_config(2).r_hat, dev, orc)
