@@ -63,6 +63,23 @@
 #ifndef MXQ_NT_STORE
 #define MXQ_NT_STORE 1
 #endif
+#ifndef MXQ_NT_SCALE
+#define MXQ_NT_SCALE 0
+#endif
+#ifndef MXQ_WAVES_PER_BLOCK
+#define MXQ_WAVES_PER_BLOCK 4
+#endif
+#ifndef MXQ_DEQUANT_WAVES_PER_CU
+#define MXQ_DEQUANT_WAVES_PER_CU 16
+#endif
+#ifndef MXQ_DEQUANT_UNROLL
+#define MXQ_DEQUANT_UNROLL 16
+#endif
+// Smallest acceptable fraction of busy wave-rows in the last round; among
+// row steps meeting it, the plan takes the one with the most waves.
+#ifndef MXQ_PLAN_MIN_EFF
+#define MXQ_PLAN_MIN_EFF 1.0
+#endif
 
 namespace mxq {
 
@@ -70,7 +87,7 @@ constexpr int kGroup = 32;
 constexpr int kSub = 4;          // sub-tiles of 16 groups per super-tile
 constexpr int kTileGroups = 64;  // groups per wave super-tile
 constexpr int kWave = 64;
-constexpr int kWavesPerBlock = 4;
+constexpr int kWavesPerBlock = MXQ_WAVES_PER_BLOCK;
 constexpr int kBlockThreads = kWave * kWavesPerBlock;
 
 // Does this kernel instance split the activations into several bf16 terms?
@@ -283,7 +300,8 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
             __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{word[0], word[1], word[2], word[3]}, crsrc, code_off, 0,
                                                    MXQ_NT_STORE ? kAuxNT : 0);
             const auto srsrc = row_rsrc(a.scales + rr * a.gpr, gpr);
-            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, scale_off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, scale_off, 0,
+                                                 MXQ_NT_SCALE ? kAuxNT : 0);
         }
     };
 
@@ -299,42 +317,63 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
     }
 }
 
-// Decode: one lane per half group (16 codes, one 8-byte load).
+// Decode.  A lane turns 8 (bf16 output) or 4 (fp32 output) consecutive codes
+// into one 16-byte store, so each wave store instruction writes 1 KB
+// contiguously.  v_cvt_scalef32_pk_bf16_fp4 decodes the two codes of one
+// byte and multiplies by 2^(S-127) taken from the exponent field of its scale
+// operand; on every code byte and every scale byte it gives exactly the
+// E2M1 value times 2^(S-127) (subnormal results kept, +-inf beyond the
+// range, NaN for S = 0xFF, -0 for code 0x8).  Every finite result is exact
+// in bf16, so fp32 output is the bf16 result widened.  (The fp32-output form
+// of the converter is not used: this compiler folds its second result into
+// the first.)
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kBlockThreads) void dequant_kernel(const uint8_t* codes, const uint8_t* scales,
-                                                               void* y, int64_t halves) {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t q = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; q < halves; q += stride) {
-        const int64_t g = q >> 1;
-        const u32x2_t c = *reinterpret_cast<const u32x2_t*>(codes + q * 8);
-        const int S = scales[g];
-        uint32_t out[16];
+                                                               void* y, int64_t elems) {
+    constexpr int kPerLane = OUT_BF16 ? 8 : 4;
+    constexpr int64_t kChunk = kWave * kPerLane;              // elements per wave store
+    constexpr int kUnroll = MXQ_DEQUANT_UNROLL;               // chunks per wave iteration
+    constexpr uint32_t osz = OUT_BF16 ? 2 : 4;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock +
+                         __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+    const uint32_t first = static_cast<uint32_t>(lane * kPerLane);  // lane's first element in a chunk
+    for (int64_t base = wave * kUnroll * kChunk; base < elems; base += waves * kUnroll * kChunk) {
+        const int64_t rem = elems - base;
+        // n elements (a multiple of 32) from here on belong to this iteration
+        const uint32_t n = static_cast<uint32_t>(rem < kUnroll * kChunk ? rem : kUnroll * kChunk);
+        const auto crsrc = row_rsrc(codes + base / 2, n / 2);
+        const auto srsrc = row_rsrc(scales + base / kGroup, n / kGroup);
+        const auto yrsrc = row_rsrc(static_cast<char*>(y) + base * osz, n * osz);
+        uint32_t c[kUnroll], S[kUnroll];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t code = (c[i >> 3] >> (4 * (i & 7))) & 0xfu;
-            const uint32_t mag = code & 7u;
-            // E2M1 magnitude as fp32: codes 2..7 are 2^(mag/2 - 1) * (1 + (mag & 1) / 2),
-            // whose fp32 pattern is (mag + 252) << 22; code 1 is 0.5, code 0 is 0.
-            const uint32_t bits = mag >= 2u ? (mag + 252u) << 22 : (mag == 1u ? 0x3f000000u : 0u);
-            float v = __builtin_amdgcn_ldexpf(as_f32(bits), S - 127);
-            uint32_t u = as_u32(v) | ((code & 8u) << 28);
-            if (S == 255) u = 0x7fc00000u;
-            out[i] = u;
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t e = static_cast<uint32_t>(u * kChunk) + first;
+            S[u] = __builtin_amdgcn_raw_buffer_load_b8(srsrc, e / kGroup, 0, 0);
+            if constexpr (OUT_BF16)
+                c[u] = __builtin_amdgcn_raw_buffer_load_b32(crsrc, e / 2, 0, kAuxNT);
+            else
+                c[u] = __builtin_amdgcn_raw_buffer_load_b16(crsrc, e / 2, 0, kAuxNT);
         }
-        if constexpr (OUT_BF16) {
-            u32x4_t o0, o1;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                o0[i] = (out[2 * i] >> 16) | (out[2 * i + 1] & 0xffff0000u);
-                o1[i] = (out[8 + 2 * i] >> 16) | (out[8 + 2 * i + 1] & 0xffff0000u);
+        for (int u = 0; u < kUnroll; ++u) {
+            const float scale = as_f32(S[u] << 23);
+            u32x4_t out;
+            if constexpr (OUT_BF16) {
+                out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[u], scale, 0));
+                out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[u], scale, 1));
+                out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[u], scale, 2));
+                out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[u], scale, 3));
+            } else {
+                const uint32_t p0 =
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[u], scale, 0));
+                const uint32_t p1 =
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[u], scale, 1));
+                out = u32x4_t{p0 << 16, p0 & 0xffff0000u, p1 << 16, p1 & 0xffff0000u};
             }
-            u32x4_t* yp = reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(y) + q * 16);
-            yp[0] = o0;
-            yp[1] = o1;
-        } else {
-            u32x4_t* yp = reinterpret_cast<u32x4_t*>(static_cast<float*>(y) + q * 16);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) yp[s] = u32x4_t{out[4 * s], out[4 * s + 1], out[4 * s + 2], out[4 * s + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(out, yrsrc, (static_cast<uint32_t>(u * kChunk) + first) * osz, 0,
+                                                   kAuxNT);
         }
     }
 }
@@ -373,6 +412,10 @@ static bool make_plan(int64_t tokens, int64_t channels, int cu_count, int waves_
         const int64_t rs = (tokens + q - 1) / q;
         if (rs < 1) break;
         const double eff = static_cast<double>(tokens) / static_cast<double>(q * rs);
+        if (eff >= MXQ_PLAN_MIN_EFF - 1e-12) {  // first hit has the most waves
+            best_rs = rs;
+            break;
+        }
         if (eff > best_eff + 1e-12) {
             best_eff = eff;
             best_rs = rs;
@@ -526,17 +569,19 @@ mxq_status mxq_dequant(const uint8_t* codes, const uint8_t* scales, int64_t toke
     if (tokens > kMaxI32 || channels > kMaxChannels) return MXQ_ERR_SHAPE;
     if (!codes || !scales || !y) return MXQ_ERR_NULL;
     if (!aligned(codes, 16) || !aligned(y, 16)) return MXQ_ERR_ALIGN;
-    const int64_t halves = tokens * (channels / kGroup) * 2;
-    int64_t blocks = (halves + kBlockThreads - 1) / kBlockThreads;
-    const int64_t cap = static_cast<int64_t>(device_cu_count()) * 32;
+    const int64_t elems = tokens * channels;
+    const int64_t per_wave = (y_dtype == MXQ_BF16 ? 8 : 4) * kWave * MXQ_DEQUANT_UNROLL;
+    const int64_t chunks = (elems + per_wave - 1) / per_wave;
+    int64_t blocks = (chunks + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t cap = static_cast<int64_t>(device_cu_count()) * (MXQ_DEQUANT_WAVES_PER_CU / kWavesPerBlock);
     if (blocks > cap) blocks = cap;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (y_dtype == MXQ_BF16)
         hipLaunchKernelGGL((dequant_kernel<true>), dim3(static_cast<unsigned>(blocks)), dim3(kBlockThreads), 0, st,
-                           codes, scales, y, halves);
+                           codes, scales, y, elems);
     else
         hipLaunchKernelGGL((dequant_kernel<false>), dim3(static_cast<unsigned>(blocks)), dim3(kBlockThreads), 0, st,
-                           codes, scales, y, halves);
+                           codes, scales, y, elems);
     return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 
