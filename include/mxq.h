@@ -59,6 +59,7 @@
 #ifndef MXQ_H
 #define MXQ_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -117,6 +118,53 @@ mxq_status mxq_quant(const void *x, int32_t x_dtype, int64_t tokens, int64_t cha
  * the rotated X^ of sec. 3.3, not the original activations. */
 mxq_status mxq_dequant(const uint8_t *codes, const uint8_t *scales, int64_t tokens,
                        int64_t channels, void *y, int32_t y_dtype, void *stream);
+
+/* ---- offline calibration of the shared block (DuQuant++ page sec. 3.2) ----
+ * Greedy outlier-aware construction of the 32x32 block R_b, in fp64 as the
+ * page advises (sec. 3 pitfalls, item 3), on the GPU.  Two calls:
+ *
+ * mxq_calib_worst_group: over the calibration activations x [tokens][stride]
+ *   (BF16, FP16 or FP32; the first `channels` of each row), divided by lambda
+ *   when lambda is not NULL (the search runs on X / Lambda, sec. 5.1 item 3),
+ *   find the 32-channel group with the largest |value| (ties: lowest group)
+ *   and copy that group's slice X_worst to x_worst [tokens][32] fp64.
+ *   group (one int64) and linf (one double) receive the group index and its
+ *   largest |value|.  All pointers are device memory.
+ *
+ * mxq_calib_givens: starting from R = I, repeat at most max_steps times (the
+ *   page uses 128): d = the column of x_worst holding the largest |value|
+ *   (ties: lowest column); for every other column j the Givens rotation
+ *   G(d, j) with angle pi/4, which maps (x_d, x_j) to
+ *   (c x_d - s x_j, s x_d + c x_j), c = s = sqrt(1/2); keep the j whose
+ *   rotated tensor has the smallest largest |value| (ties: lowest j); if
+ *   that value is not larger than the current one, R <- R G and
+ *   x_worst <- x_worst G, else stop.  Outputs (device memory):
+ *     x_worst      overwritten with x_worst * R
+ *     r_block      [32][32] fp64, row-major, y = x * r_block
+ *     linf_history [max_steps + 1] fp64: entry 0 the initial largest |value|,
+ *                  entry i the value after step i (i <= *steps_done; the
+ *                  sequence never increases); later entries untouched
+ *     steps_done   one int32: number of rotations taken
+ *     pairs        [max_steps][2] int32 (d, j) of each step taken, or NULL
+ *   Every product and sum is a separately rounded fp64 operation in a fixed
+ *   order: results are bit-reproducible.  Each step is two kernel launches.
+ *
+ * Both take a device workspace of at least mxq_calib_workspace_bytes(channels)
+ * bytes (channels = 0 is enough for mxq_calib_givens), 256-byte aligned and
+ * owned by the caller; calls sharing a workspace must not overlap.  Errors:
+ * MXQ_ERR_DTYPE, MXQ_ERR_SHAPE (tokens <= 0, channels not a positive
+ * multiple of 32, max_steps < 0), MXQ_ERR_NULL, MXQ_ERR_STRIDE, MXQ_ERR_ALIGN
+ * (workspace too small or misaligned, fp64 outputs not 8-byte aligned), all
+ * before any launch; MXQ_ERR_HIP on a launch failure. */
+size_t mxq_calib_workspace_bytes(int64_t channels);
+
+mxq_status mxq_calib_worst_group(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
+                                 int64_t x_row_stride, const float *lambda, double *x_worst, int64_t *group,
+                                 double *linf, void *workspace, size_t workspace_bytes, void *stream);
+
+mxq_status mxq_calib_givens(double *x_worst, int64_t tokens, int32_t max_steps, double *r_block,
+                            double *linf_history, int32_t *steps_done, int32_t *pairs, void *workspace,
+                            size_t workspace_bytes, void *stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *mxq_status_str(int32_t status);

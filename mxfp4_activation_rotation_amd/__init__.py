@@ -23,7 +23,8 @@ MXQ_BF16, MXQ_FP16, MXQ_FP32 = 0, 1, 2
 STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_NULL", 2: "MXQ_ERR_SHAPE", 3: "MXQ_ERR_DTYPE",
           4: "MXQ_ERR_ALIGN", 5: "MXQ_ERR_STRIDE", 6: "MXQ_ERR_HIP"}
 EXPORTS = ("mxq_rotate_quant", "mxq_rotate_quant_ex", "mxq_quant", "mxq_dequant",
-           "mxq_status_str", "mxq_plan", "mxq_version")
+           "mxq_status_str", "mxq_plan", "mxq_version", "mxq_calib_workspace_bytes",
+           "mxq_calib_worst_group", "mxq_calib_givens")
 
 _lib = None
 
@@ -56,8 +57,13 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.mxq_status_str.argtypes = [i32]
     lib.mxq_status_str.restype = ctypes.c_char_p
     lib.mxq_plan.argtypes = [i64, i64, i32, ctypes.POINTER(ctypes.c_int32)]
+    sz = ctypes.c_size_t
+    lib.mxq_calib_workspace_bytes.argtypes = [i64]
+    lib.mxq_calib_workspace_bytes.restype = sz
+    lib.mxq_calib_worst_group.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+    lib.mxq_calib_givens.argtypes = [vp, i64, i32, vp, vp, vp, vp, vp, sz, vp]
     for f in ("mxq_rotate_quant", "mxq_rotate_quant_ex", "mxq_quant", "mxq_dequant", "mxq_plan",
-              "mxq_version"):
+              "mxq_version", "mxq_calib_worst_group", "mxq_calib_givens"):
         getattr(lib, f).restype = ctypes.c_int32
     if path is None:
         _lib = lib
@@ -179,3 +185,58 @@ def plan(tokens: int, channels: int, cu_count: int = 256):
     if st != 0:
         raise MXQError("mxq_plan", st)
     return dict(zip(("blocks", "waves", "tile_columns", "row_step", "waves_per_block"), list(out)))
+
+
+# ---- offline calibration of the shared block (DuQuant++ page sec. 3.2) -----
+
+def _workspace(channels: int, device):
+    n = int(load().mxq_calib_workspace_bytes(channels))
+    return torch.empty((n + 256,), dtype=torch.uint8, device=device), n
+
+
+def _aligned256(buf):
+    ptr = buf.data_ptr()
+    return ptr + ((-ptr) % 256)
+
+
+def calib_worst_group(x: torch.Tensor, lam: torch.Tensor | None = None, *, stream=None):
+    """(x_worst [tokens, 32] fp64, group index tensor, its largest |value| tensor).
+
+    x: bf16/fp16/fp32 calibration activations [tokens, channels] on the GPU;
+    lam: fp32 [channels] or None.  The group and value stay on the device
+    (0-d tensors) so the call does not synchronize."""
+    lib = load()
+    T, C, stride = _check_x(x, (torch.bfloat16, torch.float16, torch.float32))
+    if lam is not None and (lam.dtype != torch.float32 or lam.shape != (C,) or not lam.is_contiguous()):
+        raise ValueError("lam must be a contiguous fp32 [channels] tensor")
+    xw = torch.empty((T, 32), dtype=torch.float64, device=x.device)
+    group = torch.empty((), dtype=torch.int64, device=x.device)
+    linf = torch.empty((), dtype=torch.float64, device=x.device)
+    ws, n = _workspace(C, x.device)
+    st = lib.mxq_calib_worst_group(_ptr(x), _DT[x.dtype], T, C, stride, _ptr(lam), _ptr(xw), _ptr(group),
+                                   _ptr(linf), _aligned256(ws), n, _stream(x, stream))
+    if st != 0:
+        raise MXQError("mxq_calib_worst_group", st)
+    return xw, group, linf
+
+
+def calib_givens(x_worst: torch.Tensor, max_steps: int = 128, *, stream=None):
+    """Greedy Givens search on x_worst [tokens, 32] fp64 (overwritten with
+    x_worst @ R).  Returns (R [32, 32] fp64, history [max_steps + 1] fp64,
+    steps_done 0-d int32, pairs [max_steps, 2] int32), all on the device;
+    entries of history and pairs past steps_done are unspecified."""
+    lib = load()
+    if x_worst.dtype != torch.float64 or x_worst.dim() != 2 or x_worst.shape[1] != 32 \
+            or not x_worst.is_contiguous() or not x_worst.is_cuda:
+        raise ValueError("x_worst must be a contiguous fp64 [tokens, 32] device tensor")
+    dev = x_worst.device
+    r = torch.empty((32, 32), dtype=torch.float64, device=dev)
+    hist = torch.empty((max_steps + 1,), dtype=torch.float64, device=dev)
+    done = torch.empty((), dtype=torch.int32, device=dev)
+    pairs = torch.empty((max(max_steps, 1), 2), dtype=torch.int32, device=dev)
+    ws, n = _workspace(0, dev)
+    st = lib.mxq_calib_givens(_ptr(x_worst), x_worst.shape[0], max_steps, _ptr(r), _ptr(hist), _ptr(done),
+                              _ptr(pairs), _aligned256(ws), n, _stream(x_worst, stream))
+    if st != 0:
+        raise MXQError("mxq_calib_givens", st)
+    return r, hist, done, pairs

@@ -7,7 +7,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "mxq.hip")]
+SOURCES = [os.path.join(PKG, "csrc", "mxq.hip"), os.path.join(PKG, "csrc", "mxq_calib.hip")]
 LIBRARY = os.path.join(PKG, "libmxq.so")
 ARCH = "gfx950"
 

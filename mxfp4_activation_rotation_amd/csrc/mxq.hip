@@ -41,6 +41,7 @@
 
 #include "../../include/mxq.h"
 #include "mxq_device.h"
+#include "mxq_internal.h"
 
 // Resident waves per CU and rows in flight per wave: one setting for the
 // single-term kernels (bf16 rotate, plain quantization), one for the kernels
@@ -436,8 +437,7 @@ static bool shape_ok(int64_t tokens, int64_t channels) {
     return make_plan(tokens, channels, 1, 1, &pl);
 }
 
-// Compute-unit count of the current device, queried once per device.
-static int device_cu_count() {
+int device_cu_count() {
     static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 256;

@@ -1,0 +1,456 @@
+// Offline calibration of the shared 32x32 rotation block on gfx950, in fp64.
+//
+// DuQuant++ page ("DuQuant++: block-aligned rotation quantization for MXFP4
+// activation outliers"), sec. 3.2: pick the 32-channel group of the (smoothed,
+// sec. 5.1 item 3) calibration activations with the largest L-infinity norm
+// (X_worst, all calibration tokens of that group), then grow a rotation
+// greedily: at each of up to 128 steps take the dimension d holding the
+// largest |value|, try a Givens rotation of d with each of the other 31
+// dimensions, and keep the one that leaves the smallest L-infinity norm.  The
+// page asks for double precision (sec. 3 pitfalls, item 3); every product and
+// sum below is a separately rounded fp64 operation (no contraction), in a
+// fixed order, so the result is reproducible bit for bit.
+//
+// Readings where the page is silent: the rotation angle is pi/4, so a step
+// maps (x_d, x_j) to (c x_d - s x_j, s x_d + c x_j) with c = s = sqrt(1/2);
+// ties go to the lowest column / candidate / group index; a step is taken
+// while the best candidate does not raise the norm, and the search stops when
+// every candidate would raise it or X_worst is zero.
+//
+// Work layout.  X_worst is [T][32] fp64 (256 bytes per token).  In the scan
+// kernel lane l of a wave holds column l % 32 of token 2 p + l / 32, so one
+// load instruction reads two whole tokens (512 bytes).  Each step is a scan
+// launch over all tokens (apply the previous step's rotation in place, and
+// for the current d accumulate, per candidate j, the maxima of both rotated
+// columns) followed by a one-block decide launch.  Because the maxima of the
+// two rotated columns are exactly the new column maxima of the chosen
+// candidate, one pass over X_worst per step suffices.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mxq.h"
+#include "mxq_device.h"
+#include "mxq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace mxq {
+namespace calib {
+
+constexpr int kW = 32;               // block width
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kThreads = kWave * kWavesPerBlock;
+constexpr double kC = 0x1.6a09e667f3bcdp-1;  // sqrt(1/2), correctly rounded
+constexpr double kS = 0x1.6a09e667f3bcdp-1;
+
+struct State {
+    int32_t d;           // dimension holding the current maximum
+    int32_t pd, pj;      // rotation accepted but not yet applied to X_worst (-1: none)
+    int32_t steps_done;
+    int32_t stopped;
+    int32_t pad;
+    double linf;
+    double colmax[kW];
+};
+
+__device__ __forceinline__ double shfl_d(double v, int src) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_ds_bpermute(src << 2, static_cast<int>(u & 0xffffffffu));
+    const int hi = __builtin_amdgcn_ds_bpermute(src << 2, static_cast<int>(u >> 32));
+    return __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                          static_cast<uint32_t>(lo));
+}
+
+// ---- worst group ----------------------------------------------------------
+
+__global__ void fill_u64(uint64_t* p, int64_t n, uint64_t v) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// |x / lambda| maxima per group.  Thread layout: one thread per (token, group)
+// pair within a grid-stride loop; each thread reads its group's 32 values of
+// one token (64 or 128 bytes), so a wave covers 64 consecutive groups.
+template <int XT, bool LAM>
+__global__ __launch_bounds__(kThreads) void group_max_kernel(const void* x, int64_t stride, const float* lambda,
+                                                            int64_t tokens, int64_t gpr, uint64_t* gmax) {
+    const int64_t total = tokens * gpr;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += step) {
+        const int64_t t = i / gpr;
+        const int64_t g = i - t * gpr;
+        double m = 0.0;
+        for (int k = 0; k < kW; ++k) {
+            const int64_t c = g * kW + k;
+            double v;
+            if constexpr (XT == MXQ_BF16) {
+                const uint16_t b = static_cast<const uint16_t*>(x)[t * stride + c];
+                v = static_cast<double>(as_f32(static_cast<uint32_t>(b) << 16));
+            } else if constexpr (XT == MXQ_FP16) {
+                const uint16_t b = static_cast<const uint16_t*>(x)[t * stride + c];
+                v = static_cast<double>(static_cast<float>(__builtin_bit_cast(_Float16, b)));
+            } else {
+                v = static_cast<double>(static_cast<const float*>(x)[t * stride + c]);
+            }
+            if constexpr (LAM) v = v / static_cast<double>(lambda[c]);
+            const double a = fabs(v);
+            m = a > m ? a : m;
+        }
+        // non-negative doubles order like their bit patterns
+        atomicMax(reinterpret_cast<unsigned long long*>(gmax + g),
+                  static_cast<unsigned long long>(__builtin_bit_cast(uint64_t, m)));
+    }
+}
+
+// First group with the largest maximum (one block).
+__global__ void pick_group_kernel(const uint64_t* gmax, int64_t gpr, int64_t* group, double* linf) {
+    __shared__ uint64_t best_v[kThreads];
+    __shared__ int64_t best_i[kThreads];
+    uint64_t bv = 0;
+    int64_t bi = 0;
+    bool have = false;
+    for (int64_t g = threadIdx.x; g < gpr; g += blockDim.x) {
+        const uint64_t v = gmax[g];
+        if (!have || v > bv) {
+            bv = v;
+            bi = g;
+            have = true;
+        }
+    }
+    best_v[threadIdx.x] = have ? bv : 0;
+    best_i[threadIdx.x] = have ? bi : INT64_MAX;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t v = 0;
+        int64_t i = INT64_MAX;
+        for (int k = 0; k < static_cast<int>(blockDim.x); ++k) {
+            if (best_i[k] == INT64_MAX) continue;
+            if (i == INT64_MAX || best_v[k] > v || (best_v[k] == v && best_i[k] < i)) {
+                v = best_v[k];
+                i = best_i[k];
+            }
+        }
+        *group = i;
+        *linf = __builtin_bit_cast(double, v);
+    }
+}
+
+template <int XT, bool LAM>
+__global__ __launch_bounds__(kThreads) void extract_kernel(const void* x, int64_t stride, const float* lambda,
+                                                          int64_t tokens, const int64_t* group, double* xw) {
+    const int64_t g = *group;
+    const int64_t total = tokens * kW;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += step) {
+        const int64_t t = i / kW;
+        const int64_t c = g * kW + (i - t * kW);
+        double v;
+        if constexpr (XT == MXQ_BF16) {
+            v = static_cast<double>(as_f32(static_cast<uint32_t>(static_cast<const uint16_t*>(x)[t * stride + c]) << 16));
+        } else if constexpr (XT == MXQ_FP16) {
+            v = static_cast<double>(
+                static_cast<float>(__builtin_bit_cast(_Float16, static_cast<const uint16_t*>(x)[t * stride + c])));
+        } else {
+            v = static_cast<double>(static_cast<const float*>(x)[t * stride + c]);
+        }
+        if constexpr (LAM) v = v / static_cast<double>(lambda[c]);
+        xw[i] = v;
+    }
+}
+
+// ---- greedy Givens search --------------------------------------------------
+
+enum : int { kModeInit = 0, kModeStep = 1, kModeApply = 2 };
+
+// One pass over X_worst.  Apply the pending rotation (pd, pj) in place, then
+// (kModeStep) for the current d accumulate per candidate j the maxima of
+// |c x_d - s x_j| and |s x_d + c x_j|, or (kModeInit) the column maxima.
+// Per-block partial maxima go to partials[block][32][2].
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void scan_kernel(double* xw, int64_t tokens, const State* st,
+                                                       double* partials) {
+    __shared__ double red[kWavesPerBlock][kW][2];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int k = lane & (kW - 1);
+    const int half = lane >> 5;
+    int pd = -1, pj = -1, d = 0;
+    if (MODE != kModeInit) {
+        if (st->stopped && st->pd < 0) return;  // nothing left to do (uniform for the grid)
+        pd = st->pd;
+        pj = st->pj;
+        d = st->d;
+    }
+    const bool eval = MODE == kModeStep && !st->stopped;
+    double m1 = 0.0, m2 = 0.0;
+    const int64_t pairs = (tokens + 1) / 2;
+    const int64_t wstep = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+    for (int64_t p = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave; p < pairs; p += wstep) {
+        const int64_t t = 2 * p + half;
+        const bool row_ok = t < tokens;
+        double v = row_ok ? xw[t * kW + k] : 0.0;
+        if (pd >= 0) {
+            const double xd = shfl_d(v, pd + kW * half);
+            const double xj = shfl_d(v, pj + kW * half);
+            if (k == pd) v = kC * xd - kS * xj;
+            if (k == pj) v = kS * xd + kC * xj;
+            if (row_ok && (k == pd || k == pj)) xw[t * kW + k] = v;
+        }
+        if (MODE == kModeInit) {
+            const double a = fabs(v);
+            m1 = a > m1 ? a : m1;
+        } else if (eval) {
+            const double xd = shfl_d(v, d + kW * half);
+            if (row_ok && k != d) {
+                const double a1 = fabs(kC * xd - kS * v);
+                const double a2 = fabs(kS * xd + kC * v);
+                m1 = a1 > m1 ? a1 : m1;
+                m2 = a2 > m2 ? a2 : m2;
+            }
+        }
+    }
+    if (MODE == kModeApply) return;
+    // combine the two token halves of the wave, then the waves of the block
+    const double o1 = shfl_d(m1, lane ^ 32);
+    const double o2 = shfl_d(m2, lane ^ 32);
+    m1 = o1 > m1 ? o1 : m1;
+    m2 = o2 > m2 ? o2 : m2;
+    if (half == 0) {
+        red[wave][k][0] = m1;
+        red[wave][k][1] = m2;
+    }
+    __syncthreads();
+    if (threadIdx.x < kW) {
+        double a = red[0][threadIdx.x][0], b = red[0][threadIdx.x][1];
+        for (int w = 1; w < kWavesPerBlock; ++w) {
+            a = red[w][threadIdx.x][0] > a ? red[w][threadIdx.x][0] : a;
+            b = red[w][threadIdx.x][1] > b ? red[w][threadIdx.x][1] : b;
+        }
+        partials[(static_cast<int64_t>(blockIdx.x) * kW + threadIdx.x) * 2] = a;
+        partials[(static_cast<int64_t>(blockIdx.x) * kW + threadIdx.x) * 2 + 1] = b;
+    }
+}
+
+// One block of 32 threads: reduce the partials and take (or refuse) a step.
+// Values shared between the threads go through LDS; thread 0 takes the
+// decisions and writes the scalar state.
+template <int MODE>
+__global__ void decide_kernel(State* st, const double* partials, int nblocks, double* r, double* history,
+                              int32_t* pairs_out, int32_t* steps_done) {
+    __shared__ double M1[kW], M2[kW], cm[kW];
+    __shared__ int acc_d, acc_j;  // accepted pair (acc_j < 0: none)
+    const int j = threadIdx.x;
+    if (MODE == kModeStep && st->stopped) return;  // uniform
+    double a = 0.0, b = 0.0;
+    for (int blk = 0; blk < nblocks; ++blk) {
+        const double pa = partials[(static_cast<int64_t>(blk) * kW + j) * 2];
+        const double pb = partials[(static_cast<int64_t>(blk) * kW + j) * 2 + 1];
+        a = pa > a ? pa : a;
+        b = pb > b ? pb : b;
+    }
+    M1[j] = a;
+    M2[j] = b;
+    cm[j] = MODE == kModeInit ? a : st->colmax[j];
+    __syncthreads();
+    if (j == 0) {
+        acc_j = -1;
+        if (MODE == kModeInit) {
+            double m = 0.0;
+            int dd = 0;
+            for (int c = 0; c < kW; ++c)
+                if (cm[c] > m) {
+                    m = cm[c];
+                    dd = c;
+                }
+            st->linf = m;
+            st->d = dd;
+            st->pd = -1;
+            st->pj = -1;
+            st->steps_done = 0;
+            st->stopped = m == 0.0;
+            history[0] = m;
+            *steps_done = 0;
+        } else {
+            const int d = st->d;
+            const double linf = st->linf;
+            double best = 0.0;
+            int bj = -1;
+            if (linf > 0.0) {
+                for (int c = 0; c < kW; ++c) {
+                    if (c == d) continue;
+                    double rest = 0.0;
+                    for (int k2 = 0; k2 < kW; ++k2)
+                        if (k2 != d && k2 != c && cm[k2] > rest) rest = cm[k2];
+                    double norm = M1[c] > M2[c] ? M1[c] : M2[c];
+                    norm = rest > norm ? rest : norm;
+                    if (bj < 0 || norm < best) {
+                        best = norm;
+                        bj = c;
+                    }
+                }
+            }
+            if (bj < 0 || best > linf) {  // zero block, or every candidate raises the norm
+                st->stopped = 1;
+                st->pd = -1;
+                st->pj = -1;
+            } else {
+                cm[d] = M1[bj];
+                cm[bj] = M2[bj];
+                double m = 0.0;
+                int dd = 0;
+                for (int c = 0; c < kW; ++c)
+                    if (cm[c] > m) {
+                        m = cm[c];
+                        dd = c;
+                    }
+                const int s = st->steps_done;
+                history[s + 1] = m;
+                if (pairs_out) {
+                    pairs_out[2 * s] = d;
+                    pairs_out[2 * s + 1] = bj;
+                }
+                st->linf = m;
+                st->pd = d;
+                st->pj = bj;
+                st->d = dd;
+                st->steps_done = s + 1;
+                *steps_done = s + 1;
+                acc_d = d;
+                acc_j = bj;
+            }
+        }
+    }
+    __syncthreads();
+    st->colmax[j] = cm[j];
+    if (MODE == kModeInit) {
+        for (int i = 0; i < kW; ++i) r[i * kW + j] = (i == j) ? 1.0 : 0.0;
+    } else if (acc_j >= 0) {
+        // R <- R G: columns d and j of row `j` (thread j owns row j)
+        const int d = acc_d, c = acc_j;
+        const double rd = r[j * kW + d], rc = r[j * kW + c];
+        r[j * kW + d] = kC * rd - kS * rc;
+        r[j * kW + c] = kS * rd + kC * rc;
+    }
+}
+
+}  // namespace calib
+
+// ---- host entry points ------------------------------------------------------
+
+using calib::State;
+
+static constexpr int64_t kCalibMaxBlocks = 1024;
+
+static int64_t scan_blocks(int64_t tokens) {
+    const int64_t pairs = (tokens + 1) / 2;
+    int64_t b = (pairs + calib::kWavesPerBlock - 1) / calib::kWavesPerBlock;
+    const int64_t cap = static_cast<int64_t>(device_cu_count()) * 2;
+    if (b > cap) b = cap;
+    if (b > kCalibMaxBlocks) b = kCalibMaxBlocks;
+    return b < 1 ? 1 : b;
+}
+
+static size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+static size_t calib_workspace_bytes(int64_t channels) {
+    const int64_t gpr = channels > 0 ? channels / calib::kW : 0;
+    return align256(sizeof(State)) + align256(static_cast<size_t>(kCalibMaxBlocks) * calib::kW * 2 * sizeof(double)) +
+           align256(static_cast<size_t>(gpr) * sizeof(uint64_t));
+}
+
+template <int XT, bool LAM>
+static void launch_worst(const void* x, int64_t stride, const float* lambda, int64_t tokens, int64_t gpr,
+                         uint64_t* gmax, int64_t* group, double* linf, double* xw, hipStream_t st) {
+    const int64_t fill_blocks = (gpr + 255) / 256;
+    hipLaunchKernelGGL(calib::fill_u64, dim3(static_cast<unsigned>(fill_blocks)), dim3(256), 0, st, gmax, gpr,
+                       uint64_t(0));
+    int64_t blocks = (tokens * gpr + calib::kThreads - 1) / calib::kThreads;
+    const int64_t cap = static_cast<int64_t>(device_cu_count()) * 16;
+    if (blocks > cap) blocks = cap;
+    hipLaunchKernelGGL((calib::group_max_kernel<XT, LAM>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(calib::kThreads), 0, st, x, stride, lambda, tokens, gpr, gmax);
+    hipLaunchKernelGGL(calib::pick_group_kernel, dim3(1), dim3(calib::kThreads), 0, st, gmax, gpr, group, linf);
+    int64_t eblocks = (tokens * calib::kW + calib::kThreads - 1) / calib::kThreads;
+    if (eblocks > cap) eblocks = cap;
+    hipLaunchKernelGGL((calib::extract_kernel<XT, LAM>), dim3(static_cast<unsigned>(eblocks)),
+                       dim3(calib::kThreads), 0, st, x, stride, lambda, tokens, group, xw);
+}
+
+static mxq_status calib_worst_group(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels, int64_t stride,
+                             const float* lambda, double* x_worst, int64_t* group, double* linf, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    if (x_dtype != MXQ_BF16 && x_dtype != MXQ_FP16 && x_dtype != MXQ_FP32) return MXQ_ERR_DTYPE;
+    if (tokens <= 0 || channels <= 0 || channels % calib::kW || tokens > (int64_t(1) << 40) / channels)
+        return MXQ_ERR_SHAPE;
+    if (!x || !x_worst || !group || !linf || !workspace) return MXQ_ERR_NULL;
+    if (stride < channels) return MXQ_ERR_STRIDE;
+    if (workspace_bytes < calib_workspace_bytes(channels) || (reinterpret_cast<uintptr_t>(workspace) & 255) ||
+        (reinterpret_cast<uintptr_t>(x_worst) & 7) || (reinterpret_cast<uintptr_t>(group) & 7) ||
+        (reinterpret_cast<uintptr_t>(linf) & 7))
+        return MXQ_ERR_ALIGN;
+    const int64_t gpr = channels / calib::kW;
+    char* ws = static_cast<char*>(workspace);
+    uint64_t* gmax = reinterpret_cast<uint64_t*>(
+        ws + align256(sizeof(State)) + align256(static_cast<size_t>(kCalibMaxBlocks) * calib::kW * 2 * sizeof(double)));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (x_dtype * 2 + (lambda ? 1 : 0)) {
+        case MXQ_BF16 * 2: launch_worst<MXQ_BF16, false>(x, stride, lambda, tokens, gpr, gmax, group, linf, x_worst, st); break;
+        case MXQ_BF16 * 2 + 1: launch_worst<MXQ_BF16, true>(x, stride, lambda, tokens, gpr, gmax, group, linf, x_worst, st); break;
+        case MXQ_FP16 * 2: launch_worst<MXQ_FP16, false>(x, stride, lambda, tokens, gpr, gmax, group, linf, x_worst, st); break;
+        case MXQ_FP16 * 2 + 1: launch_worst<MXQ_FP16, true>(x, stride, lambda, tokens, gpr, gmax, group, linf, x_worst, st); break;
+        case MXQ_FP32 * 2: launch_worst<MXQ_FP32, false>(x, stride, lambda, tokens, gpr, gmax, group, linf, x_worst, st); break;
+        default: launch_worst<MXQ_FP32, true>(x, stride, lambda, tokens, gpr, gmax, group, linf, x_worst, st); break;
+    }
+    return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+}
+
+static mxq_status calib_givens(double* x_worst, int64_t tokens, int32_t max_steps, double* r, double* history,
+                        int32_t* steps_done, int32_t* pairs, void* workspace, size_t workspace_bytes, void* stream) {
+    if (tokens <= 0 || tokens > (int64_t(1) << 40) || max_steps < 0 || max_steps > 1000000) return MXQ_ERR_SHAPE;
+    if (!x_worst || !r || !history || !steps_done || !workspace) return MXQ_ERR_NULL;
+    if (workspace_bytes < calib_workspace_bytes(0) || (reinterpret_cast<uintptr_t>(workspace) & 255) ||
+        (reinterpret_cast<uintptr_t>(x_worst) & 7) || (reinterpret_cast<uintptr_t>(r) & 7) ||
+        (reinterpret_cast<uintptr_t>(history) & 7) || (reinterpret_cast<uintptr_t>(steps_done) & 3) ||
+        (reinterpret_cast<uintptr_t>(pairs) & 3))
+        return MXQ_ERR_ALIGN;
+    char* ws = static_cast<char*>(workspace);
+    State* state = reinterpret_cast<State*>(ws);
+    double* partials = reinterpret_cast<double*>(ws + align256(sizeof(State)));
+    const int64_t nb = scan_blocks(tokens);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 grid(static_cast<unsigned>(nb)), block(calib::kThreads);
+    hipLaunchKernelGGL(calib::scan_kernel<calib::kModeInit>, grid, block, 0, st, x_worst, tokens, state, partials);
+    hipLaunchKernelGGL(calib::decide_kernel<calib::kModeInit>, dim3(1), dim3(calib::kW), 0, st, state, partials,
+                       static_cast<int>(nb), r, history, pairs, steps_done);
+    for (int32_t s = 0; s < max_steps; ++s) {
+        hipLaunchKernelGGL(calib::scan_kernel<calib::kModeStep>, grid, block, 0, st, x_worst, tokens, state,
+                           partials);
+        hipLaunchKernelGGL(calib::decide_kernel<calib::kModeStep>, dim3(1), dim3(calib::kW), 0, st, state,
+                           partials, static_cast<int>(nb), r, history, pairs, steps_done);
+    }
+    hipLaunchKernelGGL(calib::scan_kernel<calib::kModeApply>, grid, block, 0, st, x_worst, tokens, state, partials);
+    return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+}
+
+}  // namespace mxq
+
+extern "C" {
+
+size_t mxq_calib_workspace_bytes(int64_t channels) { return mxq::calib_workspace_bytes(channels); }
+
+mxq_status mxq_calib_worst_group(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels,
+                                 int64_t x_row_stride, const float* lambda, double* x_worst, int64_t* group,
+                                 double* linf, void* workspace, size_t workspace_bytes, void* stream) {
+    return mxq::calib_worst_group(x, x_dtype, tokens, channels, x_row_stride, lambda, x_worst, group, linf,
+                                  workspace, workspace_bytes, stream);
+}
+
+mxq_status mxq_calib_givens(double* x_worst, int64_t tokens, int32_t max_steps, double* r_block,
+                            double* linf_history, int32_t* steps_done, int32_t* pairs, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    return mxq::calib_givens(x_worst, tokens, max_steps, r_block, linf_history, steps_done, pairs, workspace,
+                             workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+"""fp64 reference of the offline calibration of the shared rotation block.
+
+TEST INFRASTRUCTURE ONLY (like the rest of ``oracle/``).  Follows the greedy
+search of the DuQuant++ page, sec. 3.2 ("constructing the outlier-aware
+block-diagonal rotation"), in the page's order, with the page's advice to
+search in double precision (sec. 3 pitfalls, item 3):
+
+1. worst group: over all 32-channel groups of the (smoothed, sec. 5.1 item 3)
+   calibration activations X' = X / Lambda, the group whose tokens x 32 slice
+   has the largest absolute value; that slice is X_worst;
+2. start from the 32x32 identity;
+3. for at most ``steps`` steps (the page uses 128):
+   a. d = the dimension (column of X_worst) holding the largest |value|;
+   b. for every other dimension j, the Givens rotation mixing d and j;
+   c. the L-infinity norm of X_worst times each candidate;
+   d. keep the candidate with the smallest norm;
+   e. R <- R * G;  f. X_worst <- X_worst * G.
+4. R is then shared by every group (BlockDiag(R, ..., R)).
+
+Readings where the page is silent (listed in the design notes too):
+* the rotation angle is pi/4 (equal mixing of the two dimensions), so in the
+  row-vector convention a step maps (x_d, x_j) to
+  (c x_d - s x_j, s x_d + c x_j) with c = s = sqrt(1/2);
+* ties: d is the lowest column holding the maximum, the chosen j the lowest
+  index among equally good candidates, the worst group the lowest index;
+* a step is taken while the best candidate does not raise the norm; the
+  search stops early when every candidate would raise it, or when X_worst is
+  all zero.
+
+Every product, sum and difference is an fp64 operation written out in
+NumPy (no fused multiply-add), in the order stated here.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+GROUP = 32
+C = S = math.sqrt(0.5)
+
+
+def smoothed(x, lam=None) -> np.ndarray:
+    """X' = X / Lambda in fp64 (exact upcast of bf16/fp16/fp32 input)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.to(torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    xs = np.asarray(x, dtype=np.float64)
+    if lam is not None:
+        xs = xs / np.asarray(lam, dtype=np.float64)[None, :]
+    return xs
+
+
+def worst_group(x, lam=None):
+    """(group index, its L-infinity norm, X_worst [T, 32] fp64)."""
+    xs = smoothed(x, lam)
+    T, Cn = xs.shape
+    per_group = np.abs(xs).reshape(T, Cn // GROUP, GROUP).max(axis=(0, 2))
+    g = int(np.argmax(per_group))  # first index among ties
+    return g, float(per_group[g]), np.ascontiguousarray(xs[:, g * GROUP:(g + 1) * GROUP])
+
+
+def greedy_givens(x_worst, steps: int = 128):
+    """Greedy outlier-aware search.  Returns (R [32, 32], X_worst * R,
+    norm history [steps_done + 1], chosen pairs [(d, j)])."""
+    cur = np.array(x_worst, dtype=np.float64, copy=True)
+    R = np.eye(GROUP)
+    colmax = np.abs(cur).max(axis=0) if cur.shape[0] else np.zeros(GROUP)
+    linf = float(colmax.max())
+    history = [linf]
+    pairs = []
+    for _ in range(steps):
+        if linf == 0.0:
+            break
+        d = int(np.argmax(colmax))
+        xd = cur[:, d]
+        best = None
+        for j in range(GROUP):
+            if j == d:
+                continue
+            xj = cur[:, j]
+            new_d = C * xd - S * xj
+            new_j = S * xd + C * xj
+            m_d = float(np.abs(new_d).max())
+            m_j = float(np.abs(new_j).max())
+            rest = max([float(colmax[k]) for k in range(GROUP) if k != d and k != j], default=0.0)
+            norm = max(m_d, m_j, rest)
+            if best is None or norm < best[0]:
+                best = (norm, j, m_d, m_j, new_d, new_j)
+        norm, j, m_d, m_j, new_d, new_j = best
+        if norm > linf:
+            break
+        cur[:, d] = new_d
+        cur[:, j] = new_j
+        r_d = C * R[:, d] - S * R[:, j]
+        r_j = S * R[:, d] + C * R[:, j]
+        R[:, d] = r_d
+        R[:, j] = r_j
+        colmax[d] = m_d
+        colmax[j] = m_j
+        linf = float(colmax.max())
+        history.append(linf)
+        pairs.append((d, j))
+    return R, cur, np.array(history), pairs

@@ -117,3 +117,24 @@ def test_plan_rejects_bad_shapes():
     for T, C in ((0, 64), (8, 0), (8, 33), (-1, 64)):
         with pytest.raises(mxq.MXQError):
             mxq.plan(T, C)
+
+
+def test_calibration_validation(lib):
+    ws = lib.mxq_calib_workspace_bytes(14336)
+    assert ws >= lib.mxq_calib_workspace_bytes(0) > 0
+    W16 = ctypes.c_void_p(0x20000)  # 256-byte aligned stand-in, never dereferenced
+    w = lib.mxq_calib_worst_group
+    assert w(P, 5, 8, 64, 64, None, P, P, P, W16, ws, None) == DTYPE
+    assert w(P, 0, 0, 64, 64, None, P, P, P, W16, ws, None) == SHAPE
+    assert w(P, 0, 8, 48, 48, None, P, P, P, W16, ws, None) == SHAPE
+    assert w(None, 0, 8, 64, 64, None, P, P, P, W16, ws, None) == NULL
+    assert w(P, 0, 8, 64, 32, None, P, P, P, W16, ws, None) == STRIDE
+    assert w(P, 0, 8, 64, 64, None, P, P, P, W16, 16, None) == ALIGN
+    assert w(P, 0, 8, 64, 64, None, P, P, P, ctypes.c_void_p(0x20010), ws, None) == ALIGN
+    g = lib.mxq_calib_givens
+    assert g(P, 0, 128, P, P, P, None, W16, ws, None) == SHAPE
+    assert g(P, 8, -1, P, P, P, None, W16, ws, None) == SHAPE
+    assert g(None, 8, 128, P, P, P, None, W16, ws, None) == NULL
+    assert g(P, 8, 128, P, None, P, None, W16, ws, None) == NULL
+    assert g(P, 8, 128, P, P, P, None, W16, 8, None) == ALIGN
+    assert g(ctypes.c_void_p(0x10004), 8, 128, P, P, P, None, W16, ws, None) == ALIGN
