@@ -35,8 +35,7 @@ METRIC = "rotate+MXFP4-quant throughput: Gelem/s, HBM GB/s, % of MI355X HBM peak
 HBM_PEAK_GBPS = 8000.0
 BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0  # bf16/fp16 in, FP4 codes + E8M0 scales out
 KERNEL_SOURCES = ("mxfp4_activation_rotation_amd/csrc/mxq.hip",
-                  "mxfp4_activation_rotation_amd/csrc/mxq_device.h",
-                  "mxfp4_activation_rotation_amd/_build.py")
+                  "mxfp4_activation_rotation_amd/csrc/mxq_device.h")
 COUNTERS = {3: "profiles/rotate_quant_bf16_8192x14336_hbm_counters.txt"}
 WORKLOAD_NAMES = {
     2: "QKV-input shape: bf16 2048x4096, 0.5% outlier channels x20, lognormal lambda, seeded orthogonal R",
@@ -49,10 +48,13 @@ WORKLOAD_NAMES = {
 
 
 def kernel_source_hash() -> str:
+    """Hash of the quantize kernel's sources and compile flags."""
+    from mxfp4_activation_rotation_amd import _build
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    h.update(" ".join(_build.FLAGS).encode())
     return h.hexdigest()[:16]
 
 
@@ -94,6 +96,60 @@ def cpu_baseline(wl, min_seconds: float):
                       f"({sum(times):.1f} s of CPU wall time), median {med * 1e3:.0f} ms each"}
 
 
+def bench_calibration(args):
+    """Greedy block search (128 steps max) on a 262144 x 32 fp64 block; each
+    timed call starts from a fresh copy of the block (copied outside the
+    events).  The scan kernel reads the block once per step and writes the
+    two rotated columns of the previous step."""
+    import numpy as np
+    import torch
+
+    import mxfp4_activation_rotation_amd as mxq
+    import workloads
+
+    dev = torch.device("cuda:0")
+    xw_host = workloads.calibration_block()
+    pristine = torch.from_numpy(xw_host).to(dev)
+    work = torch.empty_like(pristine)
+    reps = max(1, min(args.steps, 20))
+    times = []
+    for i in range(3 + reps):
+        work.copy_(pristine)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _, hist, done, _ = mxq.calib_givens(work, 128)
+        e1.record()
+        e1.synchronize()
+        if i >= 3:
+            times.append(e0.elapsed_time(e1))
+    steps = int(done)
+    ms = float(np.median(times))
+    T = xw_host.shape[0]
+    scans = steps + 2  # init scan, one per step (the last step's pass finds no better candidate), final apply
+    bytes_per_scan = T * 32 * 8
+    result = {
+        "metric": "greedy block calibration time (DuQuant++ page sec. 3.2), GPU fp64",
+        "value": round(ms, 3), "unit": "ms per search", "higher_is_better": False, "n_gpus": 1,
+        "steps": reps, "data": "synthetic",
+        "config": {"workload": "page-scale X_worst: 128 x 2048 tokens x 32 channels fp64, Student-t(3) "
+                               "background, +-U(200,800) on 2000 tokens of channel 9",
+                   "tokens": T, "max_steps": 128, "steps_taken": steps},
+        "ms_per_step": round(ms / max(steps, 1), 4),
+        "scan_bytes_per_step": bytes_per_scan,
+        "achieved_GBps_all_launches": round(bytes_per_scan * scans / (ms * 1e-3) / 1e9, 1),
+        "linf": [float(hist[0]), float(hist[steps])],
+    }
+    if not args.no_cpu_baseline:
+        from oracle import calibration as CAL
+        t0 = time.perf_counter()
+        CAL.greedy_givens(xw_host, 128)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(dt * 1e3, 1), "unit": "ms per search", "cores": 1,
+                                  "kind": "oracle", "sample": "the same block, one search (NumPy fp64)"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,6 +161,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="capture the K timed launches once as a HIP graph and time one replay "
                          "(how decode-shaped loops are driven; removes per-call host overhead)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="time the greedy block calibration (DuQuant++ page sec. 3.2) on a "
+                         "page-scale block instead of the quantization path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -126,6 +185,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     mxq.load()
+    if args.calibrate:
+        bench_calibration(args)
+        return
     dev = torch.device("cuda:0")
     wl = workloads.make_config(args.workload)
     call_tokens = workloads.SHAPES[4][0] if args.workload == 4 else wl.tokens

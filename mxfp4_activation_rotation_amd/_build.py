@@ -19,16 +19,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmxq.so)")
 
 
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
+    # no packed-fp32 VALU ops (v_pk_*_f32) anywhere in the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernels run with the IEEE mode bit clear: v_max/v_min need no
+    # canonicalizing copies (NaN inputs are outside the contract)
+    "-mno-amdgpu-ieee", "-fno-honor-nans",
+    # matrix-core results straight into VGPRs (no accumulator copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+]
+
+
 def command(out: str = LIBRARY, defines=()) -> list[str]:
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
-            # no packed-fp32 VALU ops (v_pk_*_f32) anywhere in the device code
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            # kernels run with the IEEE mode bit clear: v_max/v_min need no
-            # canonicalizing copies (NaN inputs are outside the contract)
-            "-mno-amdgpu-ieee", "-fno-honor-nans",
-            # matrix-core results straight into VGPRs (no accumulator copies)
-            "-mllvm", "-amdgpu-mfma-vgpr-form",
-            "-I", os.path.join(ROOT, "include"),
+    return [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"),
             *[f"-D{d}" for d in defines], "-o", out, *SOURCES]
 
 

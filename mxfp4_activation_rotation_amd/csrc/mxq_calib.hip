@@ -41,6 +41,8 @@ constexpr int kW = 32;               // block width
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kThreads = kWave * kWavesPerBlock;
+constexpr int kUnroll = 8;           // token pairs per scan iteration
+constexpr int kSlices = 32;          // decide kernel: threads per candidate
 constexpr double kC = 0x1.6a09e667f3bcdp-1;  // sqrt(1/2), correctly rounded
 constexpr double kS = 0x1.6a09e667f3bcdp-1;
 
@@ -186,27 +188,37 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(double* xw, int64_t toke
     double m1 = 0.0, m2 = 0.0;
     const int64_t pairs = (tokens + 1) / 2;
     const int64_t wstep = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
-    for (int64_t p = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave; p < pairs; p += wstep) {
-        const int64_t t = 2 * p + half;
-        const bool row_ok = t < tokens;
-        double v = row_ok ? xw[t * kW + k] : 0.0;
-        if (pd >= 0) {
-            const double xd = shfl_d(v, pd + kW * half);
-            const double xj = shfl_d(v, pj + kW * half);
-            if (k == pd) v = kC * xd - kS * xj;
-            if (k == pj) v = kS * xd + kC * xj;
-            if (row_ok && (k == pd || k == pj)) xw[t * kW + k] = v;
+    // kUnroll token pairs per iteration, all loads issued before any is used
+    for (int64_t p0 = (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave) * kUnroll; p0 < pairs;
+         p0 += wstep * kUnroll) {
+        double v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t t = 2 * (p0 + u) + half;
+            v[u] = t < tokens ? xw[t * kW + k] : 0.0;
         }
-        if (MODE == kModeInit) {
-            const double a = fabs(v);
-            m1 = a > m1 ? a : m1;
-        } else if (eval) {
-            const double xd = shfl_d(v, d + kW * half);
-            if (row_ok && k != d) {
-                const double a1 = fabs(kC * xd - kS * v);
-                const double a2 = fabs(kS * xd + kC * v);
-                m1 = a1 > m1 ? a1 : m1;
-                m2 = a2 > m2 ? a2 : m2;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t t = 2 * (p0 + u) + half;
+            const bool row_ok = t < tokens;
+            if (pd >= 0) {
+                const double xd = shfl_d(v[u], pd + kW * half);
+                const double xj = shfl_d(v[u], pj + kW * half);
+                if (k == pd) v[u] = kC * xd - kS * xj;
+                if (k == pj) v[u] = kS * xd + kC * xj;
+                if (row_ok && (k == pd || k == pj)) xw[t * kW + k] = v[u];
+            }
+            if (MODE == kModeInit) {
+                const double a = fabs(v[u]);
+                m1 = a > m1 ? a : m1;
+            } else if (eval) {
+                const double xd = shfl_d(v[u], d + kW * half);
+                if (row_ok && k != d) {
+                    const double a1 = fabs(kC * xd - kS * v[u]);
+                    const double a2 = fabs(kS * xd + kC * v[u]);
+                    m1 = a1 > m1 ? a1 : m1;
+                    m2 = a2 > m2 ? a2 : m2;
+                }
             }
         }
     }
@@ -232,28 +244,41 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(double* xw, int64_t toke
     }
 }
 
-// One block of 32 threads: reduce the partials and take (or refuse) a step.
-// Values shared between the threads go through LDS; thread 0 takes the
-// decisions and writes the scalar state.
+// One block of 32 x 32 threads: thread (slice, j) reduces every 32nd block's
+// partial maxima of candidate j, slice 0 combines the slices, and thread 0
+// takes (or refuses) the step and writes the scalar state.  Values shared
+// between threads go through LDS.
 template <int MODE>
-__global__ void decide_kernel(State* st, const double* partials, int nblocks, double* r, double* history,
-                              int32_t* pairs_out, int32_t* steps_done) {
+__global__ __launch_bounds__(kW * kSlices) void decide_kernel(State* st, const double* partials, int nblocks,
+                                                             double* r, double* history, int32_t* pairs_out,
+                                                             int32_t* steps_done) {
     __shared__ double M1[kW], M2[kW], cm[kW];
+    __shared__ double part[kSlices][kW][2];
     __shared__ int acc_d, acc_j;  // accepted pair (acc_j < 0: none)
-    const int j = threadIdx.x;
+    const int j = threadIdx.x & (kW - 1);
+    const int slice = threadIdx.x / kW;
     if (MODE == kModeStep && st->stopped) return;  // uniform
     double a = 0.0, b = 0.0;
-    for (int blk = 0; blk < nblocks; ++blk) {
+    for (int blk = slice; blk < nblocks; blk += kSlices) {
         const double pa = partials[(static_cast<int64_t>(blk) * kW + j) * 2];
         const double pb = partials[(static_cast<int64_t>(blk) * kW + j) * 2 + 1];
         a = pa > a ? pa : a;
         b = pb > b ? pb : b;
     }
-    M1[j] = a;
-    M2[j] = b;
-    cm[j] = MODE == kModeInit ? a : st->colmax[j];
+    part[slice][j][0] = a;
+    part[slice][j][1] = b;
     __syncthreads();
-    if (j == 0) {
+    if (slice == 0) {
+        for (int sl = 1; sl < kSlices; ++sl) {
+            a = part[sl][j][0] > a ? part[sl][j][0] : a;
+            b = part[sl][j][1] > b ? part[sl][j][1] : b;
+        }
+        M1[j] = a;
+        M2[j] = b;
+        cm[j] = MODE == kModeInit ? a : st->colmax[j];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
         acc_j = -1;
         if (MODE == kModeInit) {
             double m = 0.0;
@@ -322,6 +347,7 @@ __global__ void decide_kernel(State* st, const double* partials, int nblocks, do
         }
     }
     __syncthreads();
+    if (slice != 0) return;
     st->colmax[j] = cm[j];
     if (MODE == kModeInit) {
         for (int i = 0; i < kW; ++i) r[i * kW + j] = (i == j) ? 1.0 : 0.0;
@@ -344,8 +370,9 @@ static constexpr int64_t kCalibMaxBlocks = 1024;
 
 static int64_t scan_blocks(int64_t tokens) {
     const int64_t pairs = (tokens + 1) / 2;
-    int64_t b = (pairs + calib::kWavesPerBlock - 1) / calib::kWavesPerBlock;
-    const int64_t cap = static_cast<int64_t>(device_cu_count()) * 2;
+    const int64_t per_block = static_cast<int64_t>(calib::kWavesPerBlock) * calib::kUnroll;
+    int64_t b = (pairs + per_block - 1) / per_block;
+    const int64_t cap = static_cast<int64_t>(device_cu_count()) * 4;
     if (b > cap) b = cap;
     if (b > kCalibMaxBlocks) b = kCalibMaxBlocks;
     return b < 1 ? 1 : b;
@@ -421,12 +448,13 @@ static mxq_status calib_givens(double* x_worst, int64_t tokens, int32_t max_step
     hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid(static_cast<unsigned>(nb)), block(calib::kThreads);
     hipLaunchKernelGGL(calib::scan_kernel<calib::kModeInit>, grid, block, 0, st, x_worst, tokens, state, partials);
-    hipLaunchKernelGGL(calib::decide_kernel<calib::kModeInit>, dim3(1), dim3(calib::kW), 0, st, state, partials,
+    const dim3 dblock(calib::kW * calib::kSlices);
+    hipLaunchKernelGGL(calib::decide_kernel<calib::kModeInit>, dim3(1), dblock, 0, st, state, partials,
                        static_cast<int>(nb), r, history, pairs, steps_done);
     for (int32_t s = 0; s < max_steps; ++s) {
         hipLaunchKernelGGL(calib::scan_kernel<calib::kModeStep>, grid, block, 0, st, x_worst, tokens, state,
                            partials);
-        hipLaunchKernelGGL(calib::decide_kernel<calib::kModeStep>, dim3(1), dim3(calib::kW), 0, st, state,
+        hipLaunchKernelGGL(calib::decide_kernel<calib::kModeStep>, dim3(1), dblock, 0, st, state,
                            partials, static_cast<int>(nb), r, history, pairs, steps_done);
     }
     hipLaunchKernelGGL(calib::scan_kernel<calib::kModeApply>, grid, block, 0, st, x_worst, tokens, state, partials);

@@ -64,10 +64,7 @@ def test_large_calibration_set(dev):
 def test_page_scale_block(dev):
     """128 sequences x 2048 tokens of one 32-channel group (the page's
     calibration size, sec. 3 pitfalls item 1), fed to the search directly."""
-    rng = np.random.default_rng(11)
-    xw = rng.standard_t(3, size=(128 * 2048, 32))
-    rows = rng.choice(xw.shape[0], 2000, replace=False)
-    xw[rows, 9] = rng.choice([-1.0, 1.0], 2000) * rng.uniform(200, 800, 2000)
+    xw = W.calibration_block()
     t = torch.from_numpy(xw).to(dev)
     R, hist, done, pairs = mxq.calib_givens(t, 128)
     torch.cuda.synchronize()

@@ -227,3 +227,18 @@ def random_activations(rng: np.random.Generator, tokens: int, channels: int,
                        dtype: torch.dtype = torch.bfloat16, scale: float = 1.0) -> torch.Tensor:
     """Small seeded N(0, scale^2) activation block for unit and parity tests."""
     return to_dtype(scale * rng.standard_normal((tokens, channels)), dtype)
+
+
+CALIB_TOKENS = 128 * 2048  # the page's calibration set size: 128 sequences of 2048 tokens
+
+
+def calibration_block(seed: int = 2011, tokens: int = CALIB_TOKENS) -> np.ndarray:
+    """Seeded stand-in for X_worst at the page's calibration size (sec. 3
+    pitfalls, item 1): Student-t(3) background over 32 channels, with
+    massive +-U(200, 800) values on 2000 seeded tokens of channel 9."""
+    rng = np.random.default_rng(seed)
+    xw = rng.standard_t(3, size=(tokens, GROUP))
+    n = min(2000, tokens)
+    rows = rng.choice(tokens, n, replace=False)
+    xw[rows, 9] = rng.choice(np.array([-1.0, 1.0]), n) * rng.uniform(200.0, 800.0, n)
+    return xw
