@@ -238,3 +238,60 @@ def group_error(y, dq):
     ny = np.linalg.norm(y, axis=1)
     keep = ny > 0
     return np.linalg.norm(dq[keep] - y[keep], axis=1) / ny[keep]
+
+
+# ---- MXFP4 x MXFP4 product (the consumer of the quantized activations) -----
+
+def gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, orc: "Oracle | None" = None):
+    """Y = dq(A) dq(B)^T in fp64, and S = |dq(A)| |dq(B)|^T (the sum of
+    |products| per output, the scale of the fp32 accumulation error).
+
+    A is [M, K] MXFP4 (codes [M, K/2], scales [M, K/32]); B is [N, K] (the
+    weights, quantized along the reduction dimension K).  The DuQuant++ page
+    (sec. 3.3, 5.4 item 3) feeds the rotated, quantized activations to an
+    MXFP4 linear layer with pre-absorbed, pre-quantized weights; this is that
+    product, exactly (dequantization is exact, the matmul is fp64)."""
+    orc = orc or default()
+    a = orc.dequant(a_codes, a_scales)
+    b = orc.dequant(b_codes, b_scales)
+    return a @ b.T, np.abs(a) @ np.abs(b).T
+
+
+def _as_f64(a):
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            return a.detach().cpu().to(torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(a, dtype=np.float64)
+
+
+def absorb_weights(w_lin, lam, r):
+    """Rows of the absorbed weight matrix, in fp64.
+
+    The DuQuant++ page (sec. 3.3, eq. for W-hat) folds the smoothing and the
+    rotation into the weights: with Y = X W, W-hat = R^T Lambda W, so that
+    (X Lambda^-1 R)(R^T Lambda W) = X W for orthogonal R.  ``w_lin`` holds W
+    transposed, one row per output feature ([N, K], the usual linear-layer
+    layout); row n of W-hat^T is (w_n * Lambda) BlockDiag(R, ..., R), i.e.
+    each 32-channel group of w_n * Lambda times the shared 32x32 block.
+    ``lam`` may be None (Lambda = I)."""
+    w = _as_f64(w_lin)
+    if lam is not None:
+        w = w * _as_f64(lam)[None, :]
+    N, K = w.shape
+    if K % GROUP:
+        raise ValueError("K must be a multiple of 32")
+    r = _as_f64(r)
+    return (w.reshape(N, K // GROUP, GROUP) @ r).reshape(N, K)
+
+
+def absorb_quant(w_lin, lam, r, orc: "Oracle | None" = None):
+    """MXFP4 codes [N, K/2] and scales [N, K/32] of the absorbed weights
+    (each row quantized along K, the reduction dimension of the product)."""
+    orc = orc or default()
+    w = absorb_weights(w_lin, lam, r)
+    N, K = w.shape
+    codes, scales = orc.encode_groups(w)
+    return codes.reshape(N, K // 2), scales.reshape(N, K // GROUP)
