@@ -119,6 +119,47 @@ mxq_status mxq_quant(const void *x, int32_t x_dtype, int64_t tokens, int64_t cha
 mxq_status mxq_dequant(const uint8_t *codes, const uint8_t *scales, int64_t tokens,
                        int64_t channels, void *y, int32_t y_dtype, void *stream);
 
+/* ---- the consumer: MXFP4 x MXFP4 linear layer ----------------------------
+ * DuQuant++ page sec. 3.3 (weight absorption, W^ = R^T Lambda W, so that
+ * (X Lambda^-1 R)(R^T Lambda W) = X W) and sec. 5.2 (the rotated MXFP4
+ * activations feed an MXFP4 linear layer).
+ *
+ * mxq_absorb_quant: offline preparation of the weights.  w holds W^T, one
+ *   row of `cols` = K input features per output feature (the usual linear
+ *   layer layout [N][K], BF16 or FP16, row pitch w_row_stride elements).
+ *   Each row is multiplied by lambda (per input feature, fp32; NULL = no
+ *   smoothing), rotated group by group with the shared 32x32 block r_hat
+ *   (same convention as mxq_rotate_quant: y_n = sum_k w'_k r_hat[k][n]) and
+ *   MXFP4-encoded along K: codes [rows][cols/2], scales [rows][cols/32], the
+ *   B operand of mxq_gemm_mxfp4.  The product w * lambda is rounded once to
+ *   fp32 and then split into exact bf16 terms, as in mxq_rotate_quant.  Same
+ *   rules, limits and errors as mxq_rotate_quant.
+ *
+ * mxq_gemm_mxfp4: y[m][n] = sum_k dq(A)[m][k] * dq(B)[n][k], where
+ *   A = (a_codes [M][K/2], a_scales [M][K/32]) are quantized activations as
+ *   written by mxq_rotate_quant (M tokens, K channels) and
+ *   B = (b_codes [N][K/2], b_scales [N][K/32]) the quantized weights as
+ *   written by mxq_absorb_quant.  y is [M][ldy] FP32 (y_dtype MXQ_FP32) or
+ *   BF16 (MXQ_BF16, round-to-nearest-even of the fp32 result); only the first
+ *   N entries of each row are written.  Runs on the scaled matrix cores
+ *   (v_mfma_scale_f32_16x16x128_f8f6f4, E2M1 operands, E8M0 block scales):
+ *   every product is exact and the sum is accumulated in fp32, so each FP32
+ *   output is within 2 K 2^-24 sum_k |dq(A)[m][k] dq(B)[n][k]| of the exact
+ *   value (much closer in practice) as long as products and partial sums stay
+ *   in the fp32 normal range.  Scale bytes 0xFF (NaN) give NaN.
+ *   Requirements: K % 256 == 0 and K <= 2^24, M and N below 2^31
+ *   (MXQ_ERR_SHAPE); a_codes, b_codes 16-byte aligned, a_scales, b_scales
+ *   2-byte aligned, y aligned to its element (MXQ_ERR_ALIGN); ldy >= N
+ *   (MXQ_ERR_STRIDE).  M == 0 or N == 0 is an empty call; K == 0 writes
+ *   zeros (the code and scale pointers may then be NULL). */
+mxq_status mxq_absorb_quant(const void *w, int32_t w_dtype, int64_t rows, int64_t cols,
+                            int64_t w_row_stride, const float *lambda, const uint16_t *r_hat,
+                            uint8_t *codes, uint8_t *scales, void *stream);
+
+mxq_status mxq_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
+                          const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, void *y,
+                          int32_t y_dtype, int64_t ldy, void *stream);
+
 /* ---- offline calibration of the shared block (DuQuant++ page sec. 3.2) ----
  * Greedy outlier-aware construction of the 32x32 block R_b, in fp64 as the
  * page advises (sec. 3 pitfalls, item 3), on the GPU.  Two calls:

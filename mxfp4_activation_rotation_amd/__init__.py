@@ -24,7 +24,7 @@ STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_NULL", 2: "MXQ_ERR_SHAPE", 3: "MXQ_ERR_DTYPE"
           4: "MXQ_ERR_ALIGN", 5: "MXQ_ERR_STRIDE", 6: "MXQ_ERR_HIP"}
 EXPORTS = ("mxq_rotate_quant", "mxq_rotate_quant_ex", "mxq_quant", "mxq_dequant",
            "mxq_status_str", "mxq_plan", "mxq_version", "mxq_calib_workspace_bytes",
-           "mxq_calib_worst_group", "mxq_calib_givens")
+           "mxq_calib_worst_group", "mxq_calib_givens", "mxq_absorb_quant", "mxq_gemm_mxfp4")
 
 _lib = None
 
@@ -62,8 +62,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.mxq_calib_workspace_bytes.restype = sz
     lib.mxq_calib_worst_group.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]
     lib.mxq_calib_givens.argtypes = [vp, i64, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.mxq_absorb_quant.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
+    lib.mxq_gemm_mxfp4.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp]
     for f in ("mxq_rotate_quant", "mxq_rotate_quant_ex", "mxq_quant", "mxq_dequant", "mxq_plan",
-              "mxq_version", "mxq_calib_worst_group", "mxq_calib_givens"):
+              "mxq_version", "mxq_calib_worst_group", "mxq_calib_givens", "mxq_absorb_quant",
+              "mxq_gemm_mxfp4"):
         getattr(lib, f).restype = ctypes.c_int32
     if path is None:
         _lib = lib
@@ -174,6 +177,59 @@ def dequant(codes: torch.Tensor, scales: torch.Tensor, out_dtype=torch.float32, 
     st = lib.mxq_dequant(_ptr(codes), _ptr(scales), T, C, _ptr(out), _DT[out.dtype], _stream(codes, stream))
     if st != 0:
         raise MXQError("mxq_dequant", st)
+    return out
+
+
+def absorb_quant(w: torch.Tensor, r_hat: torch.Tensor, lam: torch.Tensor | None = None, *,
+                 codes=None, scales=None, stream=None):
+    """Quantized absorbed weights: codes, scales = MXFP4((w * lam) @ BlockDiag(r_hat)).
+
+    w: bf16/fp16 [N, K] on the GPU, one row per output feature (W^T of
+    Y = X W); lam: fp32 [K] or None; r_hat as in :func:`rotate_quant`.  The
+    result is the B operand of :func:`gemm_mxfp4`.
+    """
+    lib = load()
+    N, K, stride = _check_x(w, (torch.bfloat16, torch.float16))
+    if r_hat.dtype != torch.bfloat16 or r_hat.shape != (32, 32) or not r_hat.is_contiguous() \
+            or r_hat.device != w.device:
+        raise ValueError("r_hat must be a contiguous bf16 [32, 32] tensor on w's device")
+    if lam is not None and (lam.dtype != torch.float32 or lam.shape != (K,) or not lam.is_contiguous()
+                            or lam.device != w.device):
+        raise ValueError("lam must be a contiguous fp32 [K] tensor on w's device")
+    codes, scales = _outputs(w, N, K, codes, scales)
+    st = lib.mxq_absorb_quant(_ptr(w), _DT[w.dtype], N, K, stride, _ptr(lam), _ptr(r_hat),
+                              _ptr(codes), _ptr(scales), _stream(w, stream))
+    if st != 0:
+        raise MXQError("mxq_absorb_quant", st)
+    return codes, scales
+
+
+def gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Tensor, b_scales: torch.Tensor,
+               out_dtype=torch.float32, *, out=None, stream=None):
+    """y [M, N] = dq(A) @ dq(B)^T on the scaled matrix cores.
+
+    A = (a_codes [M, K/2], a_scales [M, K/32]) from :func:`rotate_quant`,
+    B = (b_codes [N, K/2], b_scales [N, K/32]) from :func:`absorb_quant`.
+    out: optional fp32/bf16 [M, N] tensor with unit column stride.
+    """
+    lib = load()
+    for t in (a_codes, a_scales, b_codes, b_scales):
+        if t.dtype != torch.uint8 or t.dim() != 2 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("codes and scales must be contiguous uint8 2-D device tensors")
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = b_codes.shape[0]
+    if b_codes.shape[1] * 2 != K or tuple(a_scales.shape) != (M, K // 32) or tuple(b_scales.shape) != (N, K // 32):
+        raise ValueError("operand shapes disagree: codes [rows, K/2], scales [rows, K/32]")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    if out.dtype not in (torch.bfloat16, torch.float32) or tuple(out.shape) != (M, N) or \
+            (M > 0 and N > 0 and out.stride(1) != 1):
+        raise ValueError("out must be a bf16/fp32 [M, N] tensor with unit column stride")
+    ldy = out.stride(0) if M > 1 else N
+    st = lib.mxq_gemm_mxfp4(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K,
+                            _ptr(out), _DT[out.dtype], ldy, _stream(a_codes, stream))
+    if st != 0:
+        raise MXQError("mxq_gemm_mxfp4", st)
     return out
 
 

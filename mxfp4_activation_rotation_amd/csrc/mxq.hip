@@ -92,11 +92,16 @@ constexpr int kWavesPerBlock = MXQ_WAVES_PER_BLOCK;
 constexpr int kBlockThreads = kWave * kWavesPerBlock;
 
 // Does this kernel instance split the activations into several bf16 terms?
-template <int XT, int MODE, bool LAM>
-constexpr bool kSplit = MODE == 1 && (XT != MXQ_BF16 || LAM);
-template <int XT, int MODE, bool LAM>
+// Per-channel factor applied before the block product: none, x / lambda
+// (online smoothing of activations) or x * lambda (offline absorption of the
+// smoothing factors into weight rows).
+enum : int { kLamNone = 0, kLamDiv = 1, kLamMul = 2 };
+
+template <int XT, int MODE, int LAM>
+constexpr bool kSplit = MODE == 1 && (XT != MXQ_BF16 || LAM != kLamNone);
+template <int XT, int MODE, int LAM>
 constexpr int kBatchOf = kSplit<XT, MODE, LAM> ? MXQ_BATCH_SPLIT : MXQ_BATCH;  // rows in flight per wave
-template <int XT, int MODE, bool LAM>
+template <int XT, int MODE, int LAM>
 constexpr int kWavesPerCuOf = kSplit<XT, MODE, LAM> ? MXQ_WAVES_PER_CU_SPLIT : MXQ_WAVES_PER_CU;
 
 enum : int { kBF16 = MXQ_BF16, kFP16 = MXQ_FP16, kFP32 = MXQ_FP32 };
@@ -148,7 +153,7 @@ __device__ __forceinline__ void transpose_words(uint32_t (&w)[4]) {
     }
 }
 
-template <int XT, int MODE, bool LAM, bool YOUT>
+template <int XT, int MODE, int LAM, bool YOUT>
 __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
     constexpr int kN = (XT == kFP32) ? 2 : 1;  // 16-byte loads per lane per sub-tile
     constexpr uint32_t esz = (XT == kFP32) ? 4 : 2;
@@ -210,10 +215,11 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
             A1[t] = __builtin_bit_cast(__bf16, a.r_hat[(8 * q + t) * kGroup + n0 + 4]);
         }
     }
-    // 1 / lambda for the 8 channels this lane feeds in each sub-tile
-    // (v_rcp_f32, within 1 ulp).  Lanes of groups past the row end get 0.
+    // 1 / lambda (v_rcp_f32, within 1 ulp), or lambda itself, for the 8
+    // channels this lane feeds in each sub-tile.  Lanes of groups past the
+    // row end get 0.
     float il[kSub][8];
-    if constexpr (LAM) {
+    if constexpr (LAM != kLamNone) {
         const auto lrsrc = row_rsrc(a.lambda, gpr * kGroup * 4);
 #pragma unroll
         for (int s = 0; s < kSub; ++s) {
@@ -223,8 +229,10 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
             const bool valid = p0 + 16 * s + j < a.gpr;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                il[s][t] = valid ? __builtin_amdgcn_rcpf(as_f32(l0[t])) : 0.0f;
-                il[s][4 + t] = valid ? __builtin_amdgcn_rcpf(as_f32(l1[t])) : 0.0f;
+                const float f0 = LAM == kLamMul ? as_f32(l0[t]) : __builtin_amdgcn_rcpf(as_f32(l0[t]));
+                const float f1 = LAM == kLamMul ? as_f32(l1[t]) : __builtin_amdgcn_rcpf(as_f32(l1[t]));
+                il[s][t] = valid ? f0 : 0.0f;
+                il[s][4 + t] = valid ? f1 : 0.0f;
             }
         }
     }
@@ -241,20 +249,21 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
                 float v[8];
                 if constexpr (MODE == kRotate) {
                     f32x4_t d0 = {}, d1 = {};
-                    if constexpr (XT == kBF16 && !LAM) {
+                    if constexpr (XT == kBF16 && LAM == kLamNone) {
                         const bf16x8_t b = __builtin_bit_cast(bf16x8_t, buf[u][s][0]);
                         d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, b, d0, 0, 0, 0);
                         d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b, d1, 0, 0, 0);
                     } else {
                         // x' in fp32, then exact bf16 terms: 2 for fp16 x
-                        // (11-bit significand), 3 for x * (1/lambda) (24 bits).
+                        // (11-bit significand), 3 for x * (1/lambda) or
+                        // x * lambda (24 bits).
                         float f[8];
                         widen8<XT == kFP16>(buf[u][s][0], f);
-                        if constexpr (LAM) {
+                        if constexpr (LAM != kLamNone) {
 #pragma unroll
                             for (int t = 0; t < 8; ++t) f[t] *= il[s][t];
                         }
-                        constexpr int kTerms = LAM ? 3 : 2;
+                        constexpr int kTerms = LAM != kLamNone ? 3 : 2;
 #pragma unroll
                         for (int term = 0; term < kTerms; ++term) {
                             u32x4_t bt;
@@ -455,7 +464,7 @@ static bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintp
 static size_t dtype_size(int32_t dt) { return dt == MXQ_FP32 ? 4 : 2; }
 
 // Resident waves per CU the kernel instance allows (registers), queried once.
-template <int XT, int MODE, bool LAM, bool YOUT>
+template <int XT, int MODE, int LAM, bool YOUT>
 static int occupancy_waves_per_cu() {
     static std::atomic<int> cached{0};
     int v = cached.load(std::memory_order_relaxed);
@@ -470,7 +479,7 @@ static int occupancy_waves_per_cu() {
     return v;
 }
 
-template <int XT, int MODE, bool LAM, bool YOUT>
+template <int XT, int MODE, int LAM, bool YOUT>
 static mxq_status launch(Args a, int64_t tokens, int64_t channels, hipStream_t st) {
     const int occ = occupancy_waves_per_cu<XT, MODE, LAM, YOUT>();
     Plan pl;
@@ -486,11 +495,11 @@ static mxq_status launch(Args a, int64_t tokens, int64_t channels, hipStream_t s
 template <int XT>
 static mxq_status dispatch_rotate(const Args& a, int64_t tokens, int64_t channels, hipStream_t st) {
     if (a.lambda) {
-        return a.y ? launch<XT, kRotate, true, true>(a, tokens, channels, st)
-                   : launch<XT, kRotate, true, false>(a, tokens, channels, st);
+        return a.y ? launch<XT, kRotate, kLamDiv, true>(a, tokens, channels, st)
+                   : launch<XT, kRotate, kLamDiv, false>(a, tokens, channels, st);
     }
-    return a.y ? launch<XT, kRotate, false, true>(a, tokens, channels, st)
-               : launch<XT, kRotate, false, false>(a, tokens, channels, st);
+    return a.y ? launch<XT, kRotate, kLamNone, true>(a, tokens, channels, st)
+               : launch<XT, kRotate, kLamNone, false>(a, tokens, channels, st);
 }
 
 static mxq_status check_common(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels,
@@ -521,6 +530,28 @@ static mxq_status rotate_impl(const void* x, int32_t x_dtype, int64_t tokens, in
                                : dispatch_rotate<kFP16>(a, tokens, channels, st);
 }
 
+static mxq_status absorb_impl(const void* w, int32_t w_dtype, int64_t rows, int64_t cols, int64_t stride,
+                              const float* lambda, const uint16_t* r_hat, uint8_t* codes, uint8_t* scales,
+                              void* stream) {
+    mxq_status s = check_common(w, w_dtype, rows, cols, stride, false);
+    if (s != MXQ_OK) return s;
+    if (rows == 0 || cols == 0) return MXQ_OK;
+    if (!w || !r_hat || !codes || !scales) return MXQ_ERR_NULL;
+    if (stride < cols) return MXQ_ERR_STRIDE;
+    if (!aligned(w, 16) || (stride * 2) % 16 || !aligned(codes, 16) || !aligned(r_hat, 2) ||
+        (lambda && !aligned(lambda, 16)))
+        return MXQ_ERR_ALIGN;
+    if (!shape_ok(rows, cols)) return MXQ_ERR_SHAPE;
+    Args a{w, stride, lambda, r_hat, codes, scales, nullptr, static_cast<int32_t>(rows),
+           static_cast<int32_t>(cols / kGroup), 0, 0, 0};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (w_dtype == MXQ_BF16)
+        return lambda ? launch<kBF16, kRotate, kLamMul, false>(a, rows, cols, st)
+                      : launch<kBF16, kRotate, kLamNone, false>(a, rows, cols, st);
+    return lambda ? launch<kFP16, kRotate, kLamMul, false>(a, rows, cols, st)
+                  : launch<kFP16, kRotate, kLamNone, false>(a, rows, cols, st);
+}
+
 }  // namespace mxq
 
 using namespace mxq;
@@ -541,6 +572,12 @@ mxq_status mxq_rotate_quant_ex(const void* x, int32_t x_dtype, int64_t tokens, i
                        stream);
 }
 
+mxq_status mxq_absorb_quant(const void* w, int32_t w_dtype, int64_t rows, int64_t cols, int64_t w_row_stride,
+                            const float* lambda, const uint16_t* r_hat, uint8_t* codes, uint8_t* scales,
+                            void* stream) {
+    return absorb_impl(w, w_dtype, rows, cols, w_row_stride, lambda, r_hat, codes, scales, stream);
+}
+
 mxq_status mxq_quant(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels, int64_t x_row_stride,
                      uint8_t* codes, uint8_t* scales, void* stream) {
     mxq_status s = check_common(x, x_dtype, tokens, channels, x_row_stride, true);
@@ -555,9 +592,9 @@ mxq_status mxq_quant(const void* x, int32_t x_dtype, int64_t tokens, int64_t cha
            static_cast<int32_t>(channels / kGroup), 0, 0, 0};
     hipStream_t st = static_cast<hipStream_t>(stream);
     switch (x_dtype) {
-        case MXQ_BF16: return launch<kBF16, kQuant, false, false>(a, tokens, channels, st);
-        case MXQ_FP16: return launch<kFP16, kQuant, false, false>(a, tokens, channels, st);
-        default: return launch<kFP32, kQuant, false, false>(a, tokens, channels, st);
+        case MXQ_BF16: return launch<kBF16, kQuant, kLamNone, false>(a, tokens, channels, st);
+        case MXQ_FP16: return launch<kFP16, kQuant, kLamNone, false>(a, tokens, channels, st);
+        default: return launch<kFP32, kQuant, kLamNone, false>(a, tokens, channels, st);
     }
 }
 

@@ -27,7 +27,7 @@ def lib():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(mxq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mxq_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_is_plain_c():
@@ -138,3 +138,44 @@ def test_calibration_validation(lib):
     assert g(P, 8, 128, P, None, P, None, W16, ws, None) == NULL
     assert g(P, 8, 128, P, P, P, None, W16, 8, None) == ALIGN
     assert g(ctypes.c_void_p(0x10004), 8, 128, P, P, P, None, W16, ws, None) == ALIGN
+
+
+def aq(lib, w=P, dt=0, N=8, K=64, stride=64, lam=None, r=P, codes=P, scales=P):
+    return lib.mxq_absorb_quant(w, dt, N, K, stride, lam, r, codes, scales, None)
+
+
+def test_absorb_quant_validation(lib):
+    assert aq(lib, dt=2) == DTYPE
+    assert aq(lib, K=48, stride=48) == SHAPE
+    assert aq(lib, N=-1) == SHAPE
+    assert aq(lib, N=0, w=None, r=None, codes=None, scales=None) == OK
+    assert aq(lib, w=None) == NULL
+    assert aq(lib, r=None) == NULL
+    assert aq(lib, codes=None) == NULL
+    assert aq(lib, stride=32) == STRIDE
+    assert aq(lib, w=P_ODD) == ALIGN
+    assert aq(lib, lam=P_ODD) == ALIGN
+    assert aq(lib, N=1 << 31) == SHAPE
+
+
+def gm(lib, a=P, sa=P, b=P, sb=P, M=8, N=8, K=256, y=P, dt=2, ldy=8):
+    return lib.mxq_gemm_mxfp4(a, sa, b, sb, M, N, K, y, dt, ldy, None)
+
+
+def test_gemm_validation(lib):
+    assert gm(lib, dt=1) == DTYPE          # fp16 output is not offered
+    assert gm(lib, K=128) == SHAPE         # K must be a multiple of 256
+    assert gm(lib, K=-256) == SHAPE
+    assert gm(lib, M=-1) == SHAPE
+    assert gm(lib, K=(1 << 24) + 256) == SHAPE
+    assert gm(lib, M=1 << 31) == SHAPE
+    assert gm(lib, M=0, a=None, sa=None, b=None, sb=None, y=None) == OK
+    assert gm(lib, N=0, y=None) == OK
+    assert gm(lib, y=None) == NULL
+    assert gm(lib, a=None) == NULL
+    assert gm(lib, sb=None) == NULL
+    assert gm(lib, ldy=7) == STRIDE
+    assert gm(lib, a=P_ODD) == ALIGN
+    assert gm(lib, b=P_ODD) == ALIGN
+    assert gm(lib, sa=ctypes.c_void_p(0x10001)) == ALIGN
+    assert gm(lib, y=ctypes.c_void_p(0x10002)) == ALIGN            # fp32 output: 4-byte alignment

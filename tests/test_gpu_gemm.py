@@ -1,0 +1,214 @@
+"""The MXFP4 consumer on an MI355X: absorbed-weight quantization and the
+W4A4 product, through the C ABI, against the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_activation_rotation_amd as mxq
+import oracle as O
+import workloads as W
+from parity import check_against_oracle, check_same_precision
+
+pytestmark = pytest.mark.gpu
+GROUP = 32
+U = 2.0 ** -24
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    mxq.load()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return O.default()
+
+
+def _dev_u8(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def gemm_gpu(ac, asc, bc, bsc, dev, out_dtype=torch.float32, out=None):
+    y = mxq.gemm_mxfp4(_dev_u8(ac, dev), _dev_u8(asc, dev), _dev_u8(bc, dev), _dev_u8(bsc, dev),
+                       out_dtype, out=out)
+    torch.cuda.synchronize()
+    return y
+
+
+def check_product(y, ref, s_abs, K, where=""):
+    """fp32 accumulation bound: |y - exact| <= 2 K 2^-24 sum |products|."""
+    y = np.asarray(y, dtype=np.float64)
+    err = np.abs(y - ref)
+    bound = 2.0 * K * U * s_abs
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, f"{where}: {len(bad)} outputs outside the bound, first {bad[:3].tolist()}"
+    rel = err / np.maximum(s_abs, np.finfo(np.float64).tiny)
+    return float(rel.max())
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 16, 256), (128, 128, 512), (1, 1, 256), (200, 130, 768),
+                                   (300, 257, 1024), (129, 383, 2048), (64, 640, 4096)])
+def test_gemm_random_operands(dev, orc, M, N, K):
+    rng = np.random.default_rng(M * 7919 + N * 31 + K)
+    ac, asc = W.random_mxfp4(rng, M, K)
+    bc, bsc = W.random_mxfp4(rng, N, K)
+    print(f"  gemm M={M} N={N} K={K}", flush=True)
+    ref, s_abs = O.gemm_mxfp4(ac, asc, bc, bsc, orc)
+    y = gemm_gpu(ac, asc, bc, bsc, dev).cpu().numpy()
+    worst = check_product(y, ref, s_abs, K, f"{M}x{N}x{K}")
+    print(f"    worst |err| / sum|products| = {worst:.3g}", flush=True)
+    # bf16 output: the round-to-nearest-even of the same fp32 sums
+    yb = gemm_gpu(ac, asc, bc, bsc, dev, torch.bfloat16).cpu()
+    assert torch.equal(yb.view(torch.int16), torch.from_numpy(y).to(torch.bfloat16).view(torch.int16))
+
+
+def test_gemm_one_hot_products(dev, orc):
+    """Each output picks exactly one product: codes one-hot along K with the
+    extreme magnitudes and a wide spread of scales (exact results)."""
+    M, N, K = 32, 48, 512
+    rng = np.random.default_rng(11)
+    ac = np.zeros((M, K // 2), np.uint8)
+    bc = np.zeros((N, K // 2), np.uint8)
+    ka = rng.integers(0, K, M)
+    for m in range(M):
+        code = int(rng.integers(1, 16)) or 1
+        ac[m, ka[m] // 2] = code << (4 * (ka[m] % 2))
+    for n in range(N):
+        kb = ka[n % M]  # output (n % M, n) has one product, others have none
+        code = int(rng.integers(1, 16)) or 1
+        bc[n, kb // 2] = code << (4 * (kb % 2))
+    asc = rng.integers(60, 190, (M, K // GROUP)).astype(np.uint8)
+    bsc = rng.integers(60, 190, (N, K // GROUP)).astype(np.uint8)
+    ref, _ = O.gemm_mxfp4(ac, asc, bc, bsc, orc)
+    y = gemm_gpu(ac, asc, bc, bsc, dev).cpu().numpy().astype(np.float64)
+    assert np.array_equal(y, ref)
+
+
+def test_gemm_strided_output_and_tails(dev, orc):
+    M, N, K = 70, 90, 256
+    rng = np.random.default_rng(12)
+    ac, asc = W.random_mxfp4(rng, M, K)
+    bc, bsc = W.random_mxfp4(rng, N, K)
+    base = torch.full((M, 100), 7.25, dtype=torch.float32, device=dev)
+    out = base[:, :N]
+    gemm_gpu(ac, asc, bc, bsc, dev, out=out)
+    ref, s_abs = O.gemm_mxfp4(ac, asc, bc, bsc, orc)
+    full = base.cpu().numpy()
+    check_product(full[:, :N], ref, s_abs, K, "strided")
+    assert np.all(full[:, N:] == 7.25)  # columns past N untouched
+
+
+def test_gemm_empty_and_zero_k(dev):
+    z = torch.empty((0, 128), dtype=torch.uint8, device=dev)
+    zs = torch.empty((0, 8), dtype=torch.uint8, device=dev)
+    b = torch.zeros((5, 128), dtype=torch.uint8, device=dev)
+    bs = torch.zeros((5, 8), dtype=torch.uint8, device=dev)
+    assert mxq.gemm_mxfp4(z, zs, b, bs).shape == (0, 5)
+    a0 = torch.empty((3, 0), dtype=torch.uint8, device=dev)
+    b0 = torch.empty((4, 0), dtype=torch.uint8, device=dev)
+    y = torch.full((3, 4), 5.0, device=dev)
+    mxq.gemm_mxfp4(a0, a0, b0, b0, out=y)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y).item() == 0
+
+
+def test_gemm_nan_scale(dev):
+    """E8M0 0xFF is NaN (OCP MX v1.0): a row with a NaN scale gives NaN."""
+    M, N, K = 16, 16, 256
+    rng = np.random.default_rng(13)
+    ac, asc = W.random_mxfp4(rng, M, K)
+    bc, bsc = W.random_mxfp4(rng, N, K)
+    asc[3, 2] = 0xFF
+    y = gemm_gpu(ac, asc, bc, bsc, dev).cpu().numpy()
+    assert np.all(np.isnan(y[3])) and not np.any(np.isnan(np.delete(y, 3, axis=0)))
+
+
+# ---- weight absorption ------------------------------------------------------------
+
+def _absorb_check(w, lam, r, dev, orc):
+    lam_d = None if lam is None else torch.from_numpy(lam).to(dev)
+    codes, scales = mxq.absorb_quant(w.to(dev), r.to(dev), lam_d)
+    torch.cuda.synchronize()
+    codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
+    c_ref, s_ref = O.absorb_quant(w, lam, r, orc)
+    y_ref = O.absorb_weights(w, lam, r)
+    wl = w.to(torch.float64).numpy()
+    if lam is not None:
+        wl = wl * lam.astype(np.float64)[None, :]
+    norms = np.linalg.norm(wl.reshape(wl.shape[0], -1, GROUP), axis=2)
+    return check_against_oracle(codes, scales, c_ref, s_ref, lambda rows: y_ref[rows], norms), codes, scales
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_absorb_quant_against_oracle(dev, orc, dtype):
+    rng = np.random.default_rng(21)
+    N, K = 384, 4096
+    w = W.linear_weights(N, K, seed=22, dtype=dtype)
+    lam = np.exp(0.5 * rng.standard_normal(K)).astype(np.float32)
+    r = W.bf16_matrix(W.qr_orthogonal(rng))
+    for lam_case in (lam, None):
+        stats, _, _ = _absorb_check(w, lam_case, r, dev, orc)
+        print(f"  absorb {dtype} lambda={'yes' if lam_case is not None else 'no'}: {stats}", flush=True)
+
+
+def test_absorb_identity_is_plain_quant(dev):
+    w = W.linear_weights(64, 512, seed=23)
+    c1, s1 = mxq.absorb_quant(w.to(dev), W.identity_r().to(dev))
+    c2, s2 = mxq.quant(w.to(dev))
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2) and torch.equal(s1, s2)
+
+
+# ---- the whole consumer: rotate + quantize X, absorb + quantize W, multiply ---------
+
+def _pipeline(x, lam, r, w, dev):
+    xd = x.to(dev)
+    lam_d = None if lam is None else torch.from_numpy(lam).to(dev)
+    rd = r.to(dev)
+    ac, asc = mxq.rotate_quant(xd, rd, lam_d)
+    bc, bsc = mxq.absorb_quant(w.to(dev), rd, lam_d)
+    y = mxq.gemm_mxfp4(ac, asc, bc, bsc)
+    torch.cuda.synchronize()
+    return ac, asc, bc, bsc, y
+
+
+def test_consumer_pipeline_config2(dev, orc):
+    """Config-2 activations (2048 x 4096, lambda) through a 4096 -> 1024
+    layer: the product stage against the oracle on the GPU's own operands,
+    and the W4A4 result against the exact X W (a quantization-error report)."""
+    wl = W.make_config(2)
+    w = W.linear_weights(1024, wl.channels, seed=24)
+    ac, asc, bc, bsc, y = _pipeline(wl.x, wl.lam, wl.r_hat, w, dev)
+    ac, asc, bc, bsc = (t.cpu().numpy() for t in (ac, asc, bc, bsc))
+    ref, s_abs = O.gemm_mxfp4(ac, asc, bc, bsc, orc)
+    check_product(y.cpu().numpy(), ref, s_abs, wl.channels, "config 2 pipeline")
+    exact = wl.x.to(torch.float64).numpy() @ w.to(torch.float64).numpy().T
+    rel = np.linalg.norm(y.cpu().numpy() - exact) / np.linalg.norm(exact)
+    print(f"  W4A4 relative Frobenius error vs exact X W: {rel:.4f}", flush=True)
+    assert rel < 0.5
+
+
+def test_consumer_full_size_sampled(dev, orc):
+    """The down_proj-shaped product the bench times (8192 x 14336 activations
+    of config 3, 4096 outputs), checked on 512 sampled outputs."""
+    wl = W.make_config(3)
+    w = W.linear_weights(W.DOWN_PROJ_OUT, wl.channels)
+    ac, asc, bc, bsc, y = _pipeline(wl.x, wl.lam, wl.r_hat, w, dev)
+    rng = np.random.default_rng(25)
+    ms = rng.integers(0, wl.tokens, 512)
+    ns = rng.integers(0, W.DOWN_PROJ_OUT, 512)
+    um, un = np.unique(ms), np.unique(ns)
+    da = orc.dequant(ac[torch.from_numpy(um).to(dev)].cpu().numpy(), asc[torch.from_numpy(um).to(dev)].cpu().numpy())
+    db = orc.dequant(bc[torch.from_numpy(un).to(dev)].cpu().numpy(), bsc[torch.from_numpy(un).to(dev)].cpu().numpy())
+    ia = np.searchsorted(um, ms)
+    ib = np.searchsorted(un, ns)
+    ref = np.einsum("ik,ik->i", da[ia], db[ib])
+    s_abs = np.einsum("ik,ik->i", np.abs(da[ia]), np.abs(db[ib]))
+    got = y[torch.from_numpy(ms).to(dev), torch.from_numpy(ns).to(dev)].cpu().numpy()
+    worst = check_product(got, ref, s_abs, wl.channels, "full size")
+    print(f"  full-size sampled worst |err| / sum|products| = {worst:.3g}", flush=True)
+    assert not torch.isnan(y).any().item()

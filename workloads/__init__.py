@@ -242,3 +242,31 @@ def calibration_block(seed: int = 2011, tokens: int = CALIB_TOKENS) -> np.ndarra
     rows = rng.choice(tokens, n, replace=False)
     xw[rows, 9] = rng.choice(np.array([-1.0, 1.0]), n) * rng.uniform(200.0, 800.0, n)
     return xw
+
+
+# ---- the consumer linear layer --------------------------------------------------
+
+# LLaMA-3-8B down_proj: 14336 input features -> 4096 outputs.  Config 3's
+# activations are that layer's input.
+DOWN_PROJ_OUT = 4096
+
+
+def linear_weights(out_features: int, in_features: int, seed: int = 3001,
+                   dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """Seeded stand-in for a trained linear layer's weights, [out, in] (the
+    transpose of W in Y = X W): N(0, 1/in) entries, as at initialisation, so
+    every output has unit-order variance for unit-variance inputs."""
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((out_features, in_features), dtype=np.float32)
+    w *= np.float32(1.0 / math.sqrt(in_features))
+    return torch.from_numpy(w).to(dtype)
+
+
+def random_mxfp4(rng: np.random.Generator, rows: int, k: int, scale_lo: int = 110,
+                 scale_hi: int = 140) -> tuple[np.ndarray, np.ndarray]:
+    """Uniformly random MXFP4 operand: every byte of codes [rows, k/2] drawn
+    from 0..255 (all 16 codes in both nibbles, -0 included), every scale byte
+    from [scale_lo, scale_hi]."""
+    codes = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    scales = rng.integers(scale_lo, scale_hi + 1, size=(rows, k // GROUP), dtype=np.uint8)
+    return codes, scales
