@@ -147,7 +147,7 @@ mxq_status mxq_dequant(const uint8_t *codes, const uint8_t *scales, int64_t toke
  *   output is within 2 K 2^-24 sum_k |dq(A)[m][k] dq(B)[n][k]| of the exact
  *   value (much closer in practice) as long as products and partial sums stay
  *   in the fp32 normal range.  Scale bytes 0xFF (NaN) give NaN.
- *   Requirements: K % 256 == 0 and K <= 2^24, M and N below 2^31
+ *   Requirements: K % 128 == 0 and K <= 2^24, M and N below 2^31
  *   (MXQ_ERR_SHAPE); a_codes, b_codes 16-byte aligned, a_scales, b_scales
  *   2-byte aligned, y aligned to its element (MXQ_ERR_ALIGN); ldy >= N
  *   (MXQ_ERR_STRIDE).  M == 0 or N == 0 is an empty call; K == 0 writes

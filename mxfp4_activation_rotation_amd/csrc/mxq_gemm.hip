@@ -16,17 +16,25 @@
 // are stored, low nibble first, which is exactly one MXFP4 group, plus that
 // group's scale byte.  Each operand fragment is therefore a plain 16-byte
 // load per lane straight from the stored codes, with no repacking.  The sum
-// over K does not care which group sits in which MFMA, so a lane loads 32
-// contiguous bytes (two groups) per fragment per iteration and the two MFMAs
-// of an iteration take its first and its second group; A and B use the same
-// assignment, so every product pairs the same k.
+// over K does not care which group sits in which MFMA, so within a stage of
+// 256 K positions lane l takes groups 2 (l / 16) and 2 (l / 16) + 1 (32
+// contiguous code bytes, 2 contiguous scale bytes) for the stage's two MFMAs;
+// A and B use the same assignment, so every product pairs the same k.
 //
-// Tiling: a block of kWM x kWN waves computes a (16 kFM kWM) x (16 kFN kWN)
-// tile of y; each wave holds kFM x kFN accumulator fragments.  Operands are
-// loaded per wave through buffer resources bounded to the block's rows, so
-// rows past M or N read as zero (codes 0, scale 2^-127: products 0) and
-// ragged edges need no branches in the loop.  Two register sets alternate:
-// the loads of iteration i + 1 are in flight while iteration i computes.
+// Tiling (MI355X-first): a block of 8 waves (2 per SIMD) computes a
+// 256 x 256 tile of y, each wave 128 x 64 (8 x 4 accumulator fragments, 128
+// VGPRs).  K advances 256 positions per stage.  A stage of both operands
+// (2 x 32 KB of codes, 2 x 2 KB of scales) goes straight from global memory
+// into LDS (buffer loads with the lds modifier: no staging registers),
+// double-buffered (136 KB of the CU's 160 KB): the loads of stage s + 1 are
+// in flight while stage s computes, and one barrier per stage separates them
+// from the reads of stage s - 1 in the same buffer.  In LDS every fragment
+// is stored in the order the MFMA lanes consume it (lane l's 16 bytes at
+// offset 16 l of a 1 KB slot, which is also where a direct load puts lane
+// l's data), so the operand reads are contiguous ds_read_b128 without bank
+// conflicts.  Global loads go through buffer resources bounded to the
+// tile's rows, so rows past M or N read as zero (codes 0, scale 2^-127:
+// products 0) and ragged edges need no branches in the loop.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -34,20 +42,11 @@
 #include "mxq.h"
 #include "mxq_internal.h"
 
-#ifndef MXQ_GEMM_FM
-#define MXQ_GEMM_FM 4  // 16-row A fragments per wave
-#endif
-#ifndef MXQ_GEMM_FN
-#define MXQ_GEMM_FN 4  // 16-row B fragments per wave
-#endif
-#ifndef MXQ_GEMM_WAVES_M
-#define MXQ_GEMM_WAVES_M 2
-#endif
-#ifndef MXQ_GEMM_WAVES_N
-#define MXQ_GEMM_WAVES_N 2
-#endif
 #ifndef MXQ_GEMM_GROUP_M
-#define MXQ_GEMM_GROUP_M 8  // tile rows per band of the block order
+#define MXQ_GEMM_GROUP_M 4  // tile rows per band of the block order
+#endif
+#ifndef MXQ_GEMM_STAGES
+#define MXQ_GEMM_STAGES 4  // LDS ring of K stages; loads run MXQ_GEMM_STAGES - 1 stages ahead
 #endif
 
 namespace mxq {
@@ -56,17 +55,33 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4g_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4g_t;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2g_t;
 
 constexpr int kWave = 64;
-constexpr int kFM = MXQ_GEMM_FM, kFN = MXQ_GEMM_FN;
-constexpr int kWM = MXQ_GEMM_WAVES_M, kWN = MXQ_GEMM_WAVES_N;
-constexpr int kThreads = kWave * kWM * kWN;
-constexpr int kBM = 16 * kFM * kWM;
-constexpr int kBN = 16 * kFN * kWN;
-constexpr int kKIter = 256;  // K positions per loop iteration
+constexpr int kWavesM = 2, kWavesN = 4;
+constexpr int kThreads = kWave * kWavesM * kWavesN;  // 512
+constexpr int kFragM = 8, kFragN = 4;                // 16-row fragments per wave
+constexpr int kBM = 16 * kFragM * kWavesM;           // 256
+constexpr int kBN = 16 * kFragN * kWavesN;           // 256
+constexpr int kStageK = 128;                         // K positions per stage: one MFMA deep
+constexpr int kRowBytes = kStageK / 2;               // code bytes per row per stage
+constexpr int kCodeTile = kBM * kRowBytes;           // 16 KB (kBM == kBN)
+constexpr int kSlots = kCodeTile / (16 * kWave);     // 1 KB slots per operand tile: 16
+constexpr int kLoadsPerThread = kSlots / (kThreads / kWave);  // 2
+constexpr int kChunkStages = 4;                      // stages per scale chunk
+constexpr int kChunkRowBytes = kChunkStages * kStageK / 32;  // 16 scale bytes per row per chunk
+constexpr int kScaleChunk = kBM * kChunkRowBytes;    // 4 KB per operand
+constexpr int kNst = MXQ_GEMM_STAGES;
+constexpr int kAhead = kNst - 1;
+constexpr int kLoadsPerStage = 2 * kLoadsPerThread + 1;  // direct loads per wave per stage
 constexpr int kFmtE2M1 = 4;  // operand format code of the scaled MFMA for FP4
 constexpr int kXcds = 8;     // MI355X: 8 accelerator dies, each with its own L2
 constexpr int64_t kMaxK = int64_t(1) << 24;
+static_assert(kBM == kBN, "one staging map serves both operands");
+static_assert(kThreads / 2 * 4 == kScaleChunk / kChunkStages,
+              "a quarter chunk of an operand is one dword per lane of half the waves");
+constexpr int kChunks = 3;  // scale chunk ring: the chunk in use, the next, and one being filled
+static_assert(kAhead >= 1 && kAhead <= 7 && kAhead * kLoadsPerStage < 64, "vmcnt is a 6-bit counter");
 
 struct GemmArgs {
     const uint8_t* a_codes;
@@ -79,22 +94,18 @@ struct GemmArgs {
     int32_t tiles_m, tiles_n;
 };
 
-// One operand fragment of one lane for one iteration: the 16 code bytes of
-// two consecutive groups and their two scale bytes (low byte first).
-struct Frag {
-    u32x4g_t c[2];
-    uint32_t s;
+struct Stage {
+    uint8_t a[kCodeTile];
+    uint8_t b[kCodeTile];
+};
+
+struct ScaleChunk {
+    uint8_t a[kScaleChunk];
+    uint8_t b[kScaleChunk];
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
-}
-
-__device__ __forceinline__ void load_frag(Frag& f, __amdgpu_buffer_rsrc_t codes, __amdgpu_buffer_rsrc_t scales,
-                                          uint32_t coff, uint32_t soff, int it) {
-    f.c[0] = __builtin_amdgcn_raw_buffer_load_b128(codes, coff, kKIter / 2 * it, 0);
-    f.c[1] = __builtin_amdgcn_raw_buffer_load_b128(codes, coff + 16, kKIter / 2 * it, 0);
-    f.s = __builtin_amdgcn_raw_buffer_load_b16(scales, soff, kKIter / 32 * it, 0);
 }
 
 __device__ __forceinline__ i32x8_t operand(const u32x4g_t& c) {
@@ -102,17 +113,44 @@ __device__ __forceinline__ i32x8_t operand(const u32x4g_t& c) {
                    0, 0, 0, 0};
 }
 
+// s_waitcnt vmcnt(n) (expcnt and lgkmcnt left unconstrained; vmcnt is
+// split into bits 3:0 and 15:14 of the immediate).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Wait until at most `later` stages' worth of this wave's direct loads are
+// outstanding (a smaller count than needed only waits longer).
+__device__ __forceinline__ void wait_stage_loads(int later) {
+    switch (later) {
+        case 1: wait_vmcnt<kLoadsPerStage>(); break;
+        case 2: wait_vmcnt<2 * kLoadsPerStage>(); break;
+        case 3: wait_vmcnt<3 * kLoadsPerStage>(); break;
+        case 4: wait_vmcnt<4 * kLoadsPerStage>(); break;
+        case 5: wait_vmcnt<5 * kLoadsPerStage>(); break;
+        case 6: wait_vmcnt<6 * kLoadsPerStage>(); break;
+        default: wait_vmcnt<0>(); break;
+    }
+}
+
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) Stage st[kNst];
+    __shared__ __attribute__((aligned(16))) ScaleChunk sc[kChunks];
+
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-    const int wm = wave / kWN;
-    const int wn = wave % kWN;
+    const int wm = wave / kWavesN;
+    const int wn = wave % kWavesN;
 
     // Block order: dispatch ids go round-robin over the dies, so renumber
     // them to give each die a contiguous range of tiles; then walk bands of
-    // kGroupM tile rows column by column, so the tiles resident at one time
-    // on a die share A rows and B rows in its L2.
+    // MXQ_GEMM_GROUP_M tile rows column by column, so the tiles resident at
+    // one time on a die share A rows and B rows in its L2.  (The tile indices
+    // are uniform; readfirstlane tells the compiler so, or it would wrap
+    // every buffer load in a loop over distinct descriptors.)
     const int nblk = static_cast<int>(gridDim.x);
     int bid = static_cast<int>(blockIdx.x);
     if (nblk % kXcds == 0) bid = (bid % kXcds) * (nblk / kXcds) + bid / kXcds;
@@ -120,8 +158,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     const int first_m = (bid / band) * MXQ_GEMM_GROUP_M;
     const int band_rows = min(g.tiles_m - first_m, MXQ_GEMM_GROUP_M);
     const int in_band = bid % band;
-    // (the tile indices are uniform; readfirstlane tells the compiler so, or
-    // it would wrap every buffer load in a loop over distinct descriptors)
     const int tm = __builtin_amdgcn_readfirstlane(first_m + in_band % band_rows);
     const int tn = __builtin_amdgcn_readfirstlane(in_band / band_rows);
 
@@ -132,79 +168,140 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     const uint32_t rows_a = static_cast<uint32_t>(min<int64_t>(kBM, g.M - m0));
     const uint32_t rows_b = static_cast<uint32_t>(min<int64_t>(kBN, g.N - n0));
     const auto ra = rsrc(g.a_codes + m0 * cpr, rows_a * cpr);
-    const auto rsa = rsrc(g.a_scales + m0 * spr, rows_a * spr);
     const auto rb = rsrc(g.b_codes + n0 * cpr, rows_b * cpr);
+    const auto rsa = rsrc(g.a_scales + m0 * spr, rows_a * spr);
     const auto rsb = rsrc(g.b_scales + n0 * spr, rows_b * spr);
 
-    const uint32_t r16 = static_cast<uint32_t>(lane & 15);
-    const uint32_t h = static_cast<uint32_t>(lane >> 4);
-    uint32_t ca[kFM], sa[kFM], cb[kFN], sb[kFN];
-#pragma unroll
-    for (int f = 0; f < kFM; ++f) {
-        const uint32_t row = static_cast<uint32_t>(wm * 16 * kFM + 16 * f) + r16;
-        ca[f] = row * cpr + 32 * h;
-        sa[f] = row * spr + 2 * h;
-    }
-#pragma unroll
-    for (int f = 0; f < kFN; ++f) {
-        const uint32_t row = static_cast<uint32_t>(wn * 16 * kFN + 16 * f) + r16;
-        cb[f] = row * cpr + 32 * h;
-        sb[f] = row * spr + 2 * h;
-    }
-
-    f32x4g_t acc[kFM][kFN];
-#pragma unroll
-    for (int i = 0; i < kFM; ++i)
-#pragma unroll
-        for (int j = 0; j < kFN; ++j) acc[i][j] = f32x4g_t{0.f, 0.f, 0.f, 0.f};
-
-    auto load = [&](Frag (&A)[kFM], Frag (&B)[kFN], int it) {
-#pragma unroll
-        for (int f = 0; f < kFM; ++f) load_frag(A[f], ra, rsa, ca[f], sa[f], it);
-#pragma unroll
-        for (int f = 0; f < kFN; ++f) load_frag(B[f], rb, rsb, cb[f], sb[f], it);
+    // Code staging (direct global -> LDS loads, no registers): wave w fills
+    // slots w and w + 8 of each operand tile, slot f holding the 16 x 64
+    // code bytes of rows 16 f .. 16 f + 15 for the stage, as 64 chunks of
+    // 16 bytes (chunk c of row r = the 32 K positions of group c).  A direct
+    // load puts lane l's 16 bytes at position l of the slot, so the lane
+    // decides the layout: lane l fetches row l / 4, chunk (l - l / 16) mod 4,
+    // i.e. position p(r, c) = 4 r + (c + r / 4) mod 4.  Each quad of lanes
+    // then reads one row's 64 contiguous bytes (one cache-line half per quad
+    // for the address unit), and the MFMA lane L, which needs row L % 16 and
+    // group L / 16, reads position p(L % 16, L / 16): every 16 lanes of a
+    // ds_read_b128 cover the 64 LDS banks once.
+    const uint32_t ld_r = static_cast<uint32_t>(lane >> 2);
+    const uint32_t ld_c = static_cast<uint32_t>((lane - (lane >> 4)) & 3);
+    const uint32_t goff = (static_cast<uint32_t>(16 * wave) + ld_r) * cpr + 16 * ld_c;
+    // Scale staging: chunk j holds the 16 scale bytes of stages 4 j .. 4 j + 3
+    // for every row ([row][16] per operand, a ring of three chunks in LDS).
+    // The loads of stage s carry a quarter of chunk s / 4 + 1: waves 0-3
+    // fetch A rows 64 q .. 64 q + 63 (q = s mod 4) and waves 4-7 the same
+    // rows of B, 4 lanes per row (one 16-byte row slice per quad).  Since
+    // stage s is loaded while stage s - 3 computes, the ring slot of chunk
+    // s / 4 + 1 last held chunk s / 4 - 2, whose final stage precedes s - 4.
+    const bool scale_of_b = wave >= kWavesM * kWavesN / 2;
+    const auto rs = scale_of_b ? rsb : rsa;
+    const uint32_t s_row = static_cast<uint32_t>(16 * (wave & 3)) + static_cast<uint32_t>(lane >> 2);
+    const uint32_t s_goff = s_row * spr + 4 * static_cast<uint32_t>(lane & 3);
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    auto load_scale_quarter = [&](int chunk, int q) {
+        uint8_t* dst = (scale_of_b ? sc[chunk % kChunks].b : sc[chunk % kChunks].a) + (64 * q + 16 * (wave & 3)) * kChunkRowBytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)dst, 4, s_goff,
+                                                 kChunkRowBytes * chunk + 64 * q * static_cast<int>(spr), 0, 0);
     };
-    auto compute = [&](const Frag (&A)[kFM], const Frag (&B)[kFN]) {
+    // Loads of stage kt: its codes, plus one quarter of scale chunk kt / 4 + 1.
+    auto load = [&](int kt, int buf) {
+        Stage& S = st[buf];
 #pragma unroll
-        for (int k = 0; k < 2; ++k)
-#pragma unroll
-            for (int i = 0; i < kFM; ++i)
-#pragma unroll
-                for (int j = 0; j < kFN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        operand(A[i].c[k]), operand(B[j].c[k]), acc[i][j], kFmtE2M1, kFmtE2M1, 0,
-                        static_cast<int>((A[i].s >> (8 * k)) & 0xffu), 0,
-                        static_cast<int>((B[j].s >> (8 * k)) & 0xffu));
+        for (int u = 0; u < kLoadsPerThread; ++u) {
+            // the slot's rows advance by 128 per u: the step goes into the
+            // scalar offset
+            const int so = kRowBytes * kt + u * 128 * static_cast<int>(cpr);
+            const int slot = wave + (kThreads / kWave) * u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(S.a + slot * 1024), 16, goff, so, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(S.b + slot * 1024), 16, goff, so, 0, 0);
+        }
+        load_scale_quarter(kt / kChunkStages + 1, kt % kChunkStages);
     };
 
-    const int nit = g.K / kKIter;
-    Frag A0[kFM], B0[kFN], A1[kFM], B1[kFN];
-    load(A0, B0, 0);
-    int it = 0;
-    for (; it + 2 <= nit; it += 2) {
-        load(A1, B1, it + 1);
-        compute(A0, B0);
-        if (it + 2 < nit) load(A0, B0, it + 2);
-        compute(A1, B1);
+    f32x4g_t acc[kFragM][kFragN];
+#pragma unroll
+    for (int i = 0; i < kFragM; ++i)
+#pragma unroll
+        for (int j = 0; j < kFragN; ++j) acc[i][j] = f32x4g_t{0.f, 0.f, 0.f, 0.f};
+
+    // Operand position of lane l in a slot (see the staging map) and its
+    // scale byte in a chunk row: group l / 16 of the stage.
+    const uint32_t op_off = 16 * static_cast<uint32_t>(4 * (lane & 15) + (((lane >> 4) + ((lane & 15) >> 2)) & 3));
+    const uint32_t sl = static_cast<uint32_t>((lane & 15) * kChunkRowBytes + (lane >> 4));
+    auto compute = [&](int kt) {
+        const Stage& S = st[kt % kNst];
+        const ScaleChunk& C = sc[(kt / kChunkStages) % kChunks];
+        const uint32_t sq = 4 * static_cast<uint32_t>(kt % kChunkStages);
+        // Every operand of the stage is read before the first MFMA issues
+        // (the scheduling barrier keeps the compiler from sinking the reads
+        // next to their uses): one LDS round trip per stage.
+        u32x4g_t bop[kFragN], aop[kFragM];
+        int sb[kFragN], sa[kFragM];
+#pragma unroll
+        for (int j = 0; j < kFragN; ++j) {
+            bop[j] = *reinterpret_cast<const u32x4g_t*>(S.b + (wn * kFragN + j) * 1024 + op_off);
+            sb[j] = C.b[(wn * kFragN + j) * 16 * kChunkRowBytes + sl + sq];
+        }
+#pragma unroll
+        for (int f = 0; f < kFragM; ++f) {
+            aop[f] = *reinterpret_cast<const u32x4g_t*>(S.a + (wm * kFragM + f) * 1024 + op_off);
+            sa[f] = C.a[(wm * kFragM + f) * 16 * kChunkRowBytes + sl + sq];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int f = 0; f < kFragM; ++f)
+#pragma unroll
+            for (int j = 0; j < kFragN; ++j)
+                acc[f][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    operand(aop[f]), operand(bop[j]), acc[f][j], kFmtE2M1, kFmtE2M1, 0, sa[f], 0, sb[j]);
+    };
+
+    // Pipeline: stage kt + kAhead is loaded into the ring slot that stage
+    // kt - 1 used, right after the barrier that ends its reads, and stage kt
+    // then computes while the loads of the next kAhead stages are in flight.
+    // Before the barrier each wave waits for its own loads of stage kt: all
+    // but the (at most kAhead - 1) later stages it has issued (vmcnt counts
+    // this wave's direct loads, which complete in order).
+    const int nk = g.K / kStageK;
+    if (nk > 0) {
+        // scale chunk 0 whole, then the first kAhead stages
+#pragma unroll
+        for (int q = 0; q < kChunkStages; ++q) load_scale_quarter(0, q);
     }
-    if (it < nit) compute(A0, B0);
+#pragma unroll
+    for (int s0 = 0; s0 < kAhead; ++s0)
+        if (s0 < nk) load(s0, s0);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int later = min(kAhead - 1, nk - 1 - kt);  // stages issued after kt
+        wait_stage_loads(later);
+        // A bare s_barrier: __syncthreads() would add a workgroup fence,
+        // which waits for every outstanding direct load (vmcnt(0)) and so
+        // would drain the stages in flight.  The "memory" clobber keeps the
+        // compiler from moving LDS accesses across it; the LDS reads of
+        // stage kt - 1 have all returned (their MFMAs consumed them).
+        asm volatile("s_barrier" ::: "memory");
+        if (kt + kAhead < nk) load(kt + kAhead, (kt + kAhead) % kNst);
+        compute(kt);
+    }
 
     // Accumulator layout: lane l, register r holds row 4 (l / 16) + r,
     // column l % 16 of its 16 x 16 fragment.
+    const int h = lane >> 4;
+    const int c16 = lane & 15;
 #pragma unroll
-    for (int i = 0; i < kFM; ++i) {
+    for (int f = 0; f < kFragM; ++f) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t row = m0 + wm * 16 * kFM + 16 * i + 4 * static_cast<int>(h) + r;
+            const int64_t row = m0 + (wm * kFragM + f) * 16 + 4 * h + r;
             if (row >= g.M) continue;
 #pragma unroll
-            for (int j = 0; j < kFN; ++j) {
-                const int64_t col = n0 + wn * 16 * kFN + 16 * j + static_cast<int>(r16);
+            for (int j = 0; j < kFragN; ++j) {
+                const int64_t col = n0 + (wn * kFragN + j) * 16 + c16;
                 if (col >= g.N) continue;
                 if constexpr (OUT_BF16)
-                    static_cast<__bf16*>(g.y)[row * g.ldy + col] = static_cast<__bf16>(acc[i][j][r]);
+                    static_cast<__bf16*>(g.y)[row * g.ldy + col] = static_cast<__bf16>(acc[f][j][r]);
                 else
-                    static_cast<float*>(g.y)[row * g.ldy + col] = acc[i][j][r];
+                    static_cast<float*>(g.y)[row * g.ldy + col] = acc[f][j][r];
             }
         }
     }
@@ -223,7 +320,7 @@ mxq_status mxq_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const
                           const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* y, int32_t y_dtype,
                           int64_t ldy, void* stream) {
     if (y_dtype != MXQ_FP32 && y_dtype != MXQ_BF16) return MXQ_ERR_DTYPE;
-    if (M < 0 || N < 0 || K < 0 || K % kKIter || K > kMaxK || M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31))
+    if (M < 0 || N < 0 || K < 0 || K % kStageK || K > kMaxK || M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31))
         return MXQ_ERR_SHAPE;
     if (M == 0 || N == 0) return MXQ_OK;
     if (!y) return MXQ_ERR_NULL;

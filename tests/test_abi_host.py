@@ -164,10 +164,11 @@ def gm(lib, a=P, sa=P, b=P, sb=P, M=8, N=8, K=256, y=P, dt=2, ldy=8):
 
 def test_gemm_validation(lib):
     assert gm(lib, dt=1) == DTYPE          # fp16 output is not offered
-    assert gm(lib, K=128) == SHAPE         # K must be a multiple of 256
+    assert gm(lib, K=64) == SHAPE          # K must be a multiple of 128
+    assert gm(lib, K=320) == SHAPE
     assert gm(lib, K=-256) == SHAPE
     assert gm(lib, M=-1) == SHAPE
-    assert gm(lib, K=(1 << 24) + 256) == SHAPE
+    assert gm(lib, K=(1 << 24) + 128) == SHAPE
     assert gm(lib, M=1 << 31) == SHAPE
     assert gm(lib, M=0, a=None, sa=None, b=None, sb=None, y=None) == OK
     assert gm(lib, N=0, y=None) == OK

@@ -51,7 +51,8 @@ def check_product(y, ref, s_abs, K, where=""):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 16, 256), (128, 128, 512), (1, 1, 256), (200, 130, 768),
-                                   (300, 257, 1024), (129, 383, 2048), (64, 640, 4096)])
+                                   (300, 257, 1024), (129, 383, 2048), (64, 640, 4096), (33, 70, 128),
+                                   (100, 300, 384), (513, 260, 1152)])
 def test_gemm_random_operands(dev, orc, M, N, K):
     rng = np.random.default_rng(M * 7919 + N * 31 + K)
     ac, asc = W.random_mxfp4(rng, M, K)
