@@ -37,6 +37,9 @@ BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0  # bf16/fp16 in, FP4 codes + E8M0 scales
 KERNEL_SOURCES = ("mxfp4_activation_rotation_amd/csrc/mxq.hip",
                   "mxfp4_activation_rotation_amd/csrc/mxq_device.h")
 COUNTERS = {3: "profiles/rotate_quant_bf16_8192x14336_hbm_counters.txt"}
+GEMM_SOURCES = ("mxfp4_activation_rotation_amd/csrc/mxq_gemm.hip",)
+GEMM_COUNTERS = "profiles/gemm_mxfp4_8192x4096x14336_hbm_counters.txt"
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 (E2M1) matrix-core peak
 WORKLOAD_NAMES = {
     2: "QKV-input shape: bf16 2048x4096, 0.5% outlier channels x20, lognormal lambda, seeded orthogonal R",
     3: "down_proj-input shape: bf16 8192x14336, Student-t(3) background, +-U(500,2000) on 1% of tokens "
@@ -47,21 +50,21 @@ WORKLOAD_NAMES = {
 }
 
 
-def kernel_source_hash() -> str:
-    """Hash of the quantize kernel's sources and compile flags."""
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
+    """Hash of a kernel's sources and the compile flags."""
     from mxfp4_activation_rotation_amd import _build
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     h.update(" ".join(_build.FLAGS).encode())
     return h.hexdigest()[:16]
 
 
-def read_counters(cfg: int):
+def read_counters(cfg: int, rel: str | None = None, sources=KERNEL_SOURCES):
     """Per-launch HBM bytes from the committed counter summary, or None when
     it is absent or was taken on a different kernel source."""
-    rel = COUNTERS.get(cfg)
+    rel = rel or COUNTERS.get(cfg)
     if not rel or not os.path.exists(os.path.join(ROOT, rel)):
         return None
     kv = {}
@@ -69,7 +72,7 @@ def read_counters(cfg: int):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_hash") != kernel_source_hash():
+    if kv.get("kernel_source_hash") != kernel_source_hash(sources):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -150,6 +153,91 @@ def bench_calibration(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_gemm(args):
+    """The consumer: W4A4 MXFP4 product of the quantized down_proj input
+    (8192 x 14336, from mxq_rotate_quant on the headline activations) with
+    absorbed, quantized synthetic weights (4096 x 14336), bf16 output.  The
+    operands (88 MB) are built once on the GPU before the timed region."""
+    import numpy as np
+    import torch
+
+    import mxfp4_activation_rotation_amd as mxq
+    import workloads
+
+    dev = torch.device("cuda:0")
+    wl = workloads.make_config(3)
+    w = workloads.linear_weights(workloads.DOWN_PROJ_OUT, wl.channels)
+    r = wl.r_hat.to(dev)
+    lam = torch.from_numpy(wl.lam).to(dev) if wl.lam is not None else None
+    ac, asc = mxq.rotate_quant(wl.x.to(dev), r, lam)
+    bc, bsc = mxq.absorb_quant(w.to(dev), r, lam)
+    M, K, N = wl.tokens, wl.channels, workloads.DOWN_PROJ_OUT
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    flop = 2.0 * M * N * K
+    for _ in range(args.warmup):
+        mxq.gemm_mxfp4(ac, asc, bc, bsc, out=y)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        mxq.gemm_mxfp4(ac, asc, bc, bsc, out=y)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
+    achieved = flop / mean_launch_s / 1e12
+    hbm = read_counters(0, GEMM_COUNTERS, GEMM_SOURCES)
+    result = {
+        "metric": "W4A4 MXFP4 GEMM throughput (consumer of the quantized activations): TFLOP/s",
+        "value": round(flop * args.steps / wall / 1e12, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4",
+        "data": "synthetic",
+        "config": {"workload": "down_proj product: activations bf16 8192x14336 (the headline batch) rotated and "
+                               "MXFP4-quantized, times absorbed MXFP4 weights 4096x14336 (seeded N(0, 1/14336)); "
+                               "fp32 accumulation, bf16 output",
+                   "M": M, "N": N, "K": K, "operands": "E2M1 codes + E8M0 scales per 32 along K",
+                   "parallelism": "single GPU", "launch": "eager launches"},
+        "launch_us_mean": round(mean_launch_s * 1e6, 3),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP4_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / FP4_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": None if hbm is None else round(hbm)},
+        "kernel_source_hash": kernel_source_hash(GEMM_SOURCES),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.default()
+        rows = 64
+        a_s, as_s = ac[:rows].cpu().numpy(), asc[:rows].cpu().numpy()
+        b_h, bs_h = bc.cpu().numpy(), bsc.cpu().numpy()
+        times = []
+        t_start = time.perf_counter()
+        while True:
+            t1 = time.perf_counter()
+            oracle.gemm_mxfp4(a_s, as_s, b_h, bs_h, orc)
+            times.append(time.perf_counter() - t1)
+            if time.perf_counter() - t_start >= args.cpu_seconds and len(times) >= 3:
+                break
+        med = statistics.median(times)
+        try:
+            from threadpoolctl import threadpool_info
+            blas = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                       default=1)
+        except Exception:  # pragma: no cover
+            blas = 1
+        result["cpu_baseline"] = {
+            "value": round(2.0 * rows * N * K / med / 1e12, 5), "unit": "TFLOP/s",
+            "cores": max(blas, orc.num_threads()), "kind": "oracle",
+            "sample": f"the first {rows} activation rows against all {N} weight rows (exact dequantization, "
+                      f"fp64 matmul), {len(times)} repetitions, median {med:.2f} s each"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,6 +252,9 @@ def main():
     ap.add_argument("--calibrate", action="store_true",
                     help="time the greedy block calibration (DuQuant++ page sec. 3.2) on a "
                          "page-scale block instead of the quantization path")
+    ap.add_argument("--gemm", action="store_true",
+                    help="time the consumer instead: the W4A4 MXFP4 product of the headline batch's codes "
+                         "with absorbed, quantized weights (8192x14336 by 4096x14336)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -187,6 +278,9 @@ def main():
     mxq.load()
     if args.calibrate:
         bench_calibration(args)
+        return
+    if args.gemm:
+        bench_gemm(args)
         return
     dev = torch.device("cuda:0")
     wl = workloads.make_config(args.workload)
