@@ -60,8 +60,10 @@ class Oracle:
         self.lib.oracle_rotate_quant.argtypes = [vp, i32, i64, i64, i64, vp, vp, i32, vp, vp, vp]
         self.lib.oracle_encode_groups.argtypes = [vp, i64, vp, vp]
         self.lib.oracle_dequant.argtypes = [vp, vp, i64, i64, vp]
+        self.lib.oracle_norm_rotate_quant.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, ctypes.c_double,
+                                                      vp, vp, i32, vp, vp, vp]
         for f in ("oracle_quant", "oracle_rotate_quant", "oracle_encode_groups",
-                  "oracle_dequant", "oracle_num_threads"):
+                  "oracle_dequant", "oracle_num_threads", "oracle_norm_rotate_quant"):
             getattr(self.lib, f).restype = ctypes.c_int
 
     # -- input marshalling ------------------------------------------------
@@ -153,6 +155,29 @@ class Oracle:
                                           self._ptr(codes), self._ptr(scales), self._ptr(y))
         if rc != 0:
             raise ValueError(f"oracle_rotate_quant rejected the shape (rc={rc})")
+        return (codes, scales, y) if want_y else (codes, scales)
+
+    def norm_rotate_quant(self, x, norm: str, gamma, beta, eps: float, lam, r_hat, want_y: bool = False):
+        """RMSNorm ("rms") or LayerNorm ("layer") of each row, times gamma plus
+        beta, then x / lam, the block rotation and MXFP4 (sec. 5.2 item 1 of
+        the DuQuant++ page: the smoothing folds into the norm's output)."""
+        arr, code, T, C, stride = self._raw(x)
+        kind = {"rms": 0, "layer": 1}[norm]
+        gamma = self._lambda(gamma, C)
+        beta = self._lambda(beta, C)
+        lam = self._lambda(lam, C)
+        r, r_code = self._r_hat(r_hat)
+        if r.shape != (GROUP, GROUP):
+            raise ValueError("r_hat must be 32x32")
+        codes = np.zeros((T, C // 2), np.uint8)
+        scales = np.zeros((T, C // GROUP), np.uint8)
+        y = np.zeros((T, C), np.float64) if want_y else None
+        rc = self.lib.oracle_norm_rotate_quant(self._ptr(arr), code, _i64(T), _i64(C), _i64(stride), kind,
+                                               self._ptr(gamma), self._ptr(beta), ctypes.c_double(eps),
+                                               self._ptr(lam), self._ptr(r), r_code,
+                                               self._ptr(codes), self._ptr(scales), self._ptr(y))
+        if rc != 0:
+            raise ValueError(f"oracle_norm_rotate_quant rejected the arguments (rc={rc})")
         return (codes, scales, y) if want_y else (codes, scales)
 
     def encode_groups(self, y):

@@ -25,11 +25,22 @@
  *                  scales [T][C/32] as E8M0 bytes (e + 127)
  *   dequant        (-1)^s * {0,.5,1,1.5,2,3,4,6}[m] * 2^(S-127)  (OCP MX v1.0
  *                  E2M1 and E8M0 tables; S = 255 is NaN)
+ *   norm in front  DuQuant++ page, sec. 5.2 item 1: the per-channel 1/lambda
+ *                  folds into the output of a preceding LayerNorm.  Textbook
+ *                  definitions, per token row of C channels:
+ *                  RMSNorm   n_c = x_c / sqrt(sum_c x_c^2 / C + eps)
+ *                  LayerNorm n_c = (x_c - mu) / sqrt(sum_c (x_c - mu)^2 / C + eps),
+ *                            mu = sum_c x_c / C (biased variance)
+ *                  then a_c = n_c * gamma_c + beta_c (beta optional) and the
+ *                  smoothing, rotation and encoding above applied to a.
  *
  * Parity status: every exported function is pinned by tests/test_oracle_pins.py
  * (worked example of sec. 2.1, brute-force nearest-code search, identity
  * rotation, dense block-diagonal product, norm preservation, scale and sign
- * equivariance, dequant exactness and idempotence). No function is unpinned.
+ * equivariance, dequant exactness and idempotence); oracle_norm_rotate_quant
+ * by tests/test_norm_oracle.py (closed forms of alternating rows, scale and
+ * shift invariance, power-of-two refactoring of gamma and lambda, eps on zero
+ * rows, reduction to oracle_rotate_quant).  No function is unpinned.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (no -ffast-math).
  */
@@ -165,6 +176,16 @@ int oracle_quant(const void *x, int dtype, int64_t tokens, int64_t channels, int
  *   codes, scales = MXFP4(y)                              sec. 2.1
  * r is the shared 32x32 block, row-major, y_n = sum_k x'_k r[k][n]; r_dtype
  * is OR_BF16 (bits) or OR_FP64.  y_out (fp64 [tokens][channels]) may be NULL. */
+/* y_n = sum_k x'_k R[k][n] for one 32-element group (row-vector product). */
+static void rotate_group(const double *xs, const double R[GROUP][GROUP], double *y) {
+    for (int n = 0; n < GROUP; ++n) {
+        double acc = 0.0;
+        for (int k = 0; k < GROUP; ++k)
+            acc += xs[k] * R[k][n];
+        y[n] = acc;
+    }
+}
+
 int oracle_rotate_quant(const void *x, int dtype, int64_t tokens, int64_t channels, int64_t stride,
                         const float *lambda, const void *r, int r_dtype,
                         uint8_t *codes, uint8_t *scales, double *y_out) {
@@ -183,12 +204,7 @@ int oracle_rotate_quant(const void *x, int dtype, int64_t tokens, int64_t channe
                 double v = load_elem(x, dtype, t * stride + c);
                 xs[k] = lambda ? v / (double)lambda[c] : v;
             }
-            for (int n = 0; n < GROUP; ++n) {
-                double acc = 0.0;
-                for (int k = 0; k < GROUP; ++k)
-                    acc += xs[k] * R[k][n];
-                y[n] = acc;
-            }
+            rotate_group(xs, R, y);
             if (y_out)
                 for (int n = 0; n < GROUP; ++n)
                     y_out[t * channels + g * GROUP + n] = y[n];
@@ -199,6 +215,54 @@ int oracle_rotate_quant(const void *x, int dtype, int64_t tokens, int64_t channe
 }
 
 /* Dequantize: value = (-1)^s * E2M1[m] * 2^(S - 127); S = 255 gives NaN. */
+/* RMSNorm (norm_kind 0) or LayerNorm (norm_kind 1) of every row, then
+ * gamma, beta, smoothing, rotation and encoding as in oracle_rotate_quant.
+ * y_out, when not NULL, receives the rotated values [tokens][channels]. */
+int oracle_norm_rotate_quant(const void *x, int dtype, int64_t tokens, int64_t channels, int64_t stride,
+                             int norm_kind, const float *gamma, const float *beta, double eps,
+                             const float *lambda, const void *r, int r_dtype,
+                             uint8_t *codes, uint8_t *scales, double *y_out) {
+    if (tokens < 0 || channels <= 0 || channels % GROUP != 0 || stride < channels) return 2;
+    if (norm_kind != 0 && norm_kind != 1) return 3;
+    if (!gamma) return 1;
+    double R[GROUP][GROUP];
+    for (int k = 0; k < GROUP; ++k)
+        for (int n = 0; n < GROUP; ++n)
+            R[k][n] = load_elem(r, r_dtype, k * GROUP + n);
+    const int64_t gpr = channels / GROUP;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < tokens; ++t) {
+        /* row statistics */
+        double mu = 0.0;
+        if (norm_kind == 1) {
+            double sum = 0.0;
+            for (int64_t c = 0; c < channels; ++c) sum += load_elem(x, dtype, t * stride + c);
+            mu = sum / (double)channels;
+        }
+        double sq = 0.0;
+        for (int64_t c = 0; c < channels; ++c) {
+            double d = load_elem(x, dtype, t * stride + c) - mu;
+            sq += d * d;
+        }
+        const double inv = 1.0 / sqrt(sq / (double)channels + eps);
+        double xs[GROUP], y[GROUP];
+        for (int64_t g = 0; g < gpr; ++g) {
+            for (int k = 0; k < GROUP; ++k) {
+                int64_t c = g * GROUP + k;
+                double n = (load_elem(x, dtype, t * stride + c) - mu) * inv;
+                double a = n * (double)gamma[c] + (beta ? (double)beta[c] : 0.0);
+                xs[k] = lambda ? a / (double)lambda[c] : a;
+            }
+            rotate_group(xs, R, y);
+            if (y_out)
+                for (int n = 0; n < GROUP; ++n)
+                    y_out[t * channels + g * GROUP + n] = y[n];
+            encode_group(y, codes + (t * gpr + g) * (GROUP / 2), scales + t * gpr + g);
+        }
+    }
+    return 0;
+}
+
 int oracle_dequant(const uint8_t *codes, const uint8_t *scales, int64_t tokens, int64_t channels,
                    double *out) {
     static const double e2m1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};

@@ -316,6 +316,121 @@ def pin_encode_groups_matches_quant(orc):
     assert np.array_equal(c.reshape(c0.shape), c0) and np.array_equal(s.reshape(s0.shape), s0)
 
 
+# ---- norm + smooth + rotate + quantize (DuQuant++ page sec. 5.2 item 1) -----
+
+def _unit_ms_rows(rng, T, C):
+    """Rows with sum x^2 = C and sum x = 0 exactly: C/64 copies of
+    {+-2 x 4, +-1.5 x 8, +-1 x 30, 0 x 22}, signs balanced, shuffled."""
+    base = np.array([2.0] * 2 + [-2.0] * 2 + [1.5] * 4 + [-1.5] * 4 + [1.0] * 15 + [-1.0] * 15 + [0.0] * 22)
+    x = np.array([rng.permutation(np.concatenate([base] * (C // 64))) for _ in range(T)])
+    assert np.all((x ** 2).sum(axis=1) == C) and np.all(x.sum(axis=1) == 0)
+    return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+
+
+def _f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+
+
+def pin_norm_alternating_closed_form(orc):
+    """x = (a, -a, a, ...): mean 0, mean square a^2, every normalized value
+    +-1; gamma = 1, R = I: scale 2^-2 (byte 125), codes +4 / -4 (0x6 / 0xE)."""
+    C = 128
+    for norm in ("rms", "layer"):
+        for a in (3.0, 0.375, 96.0):
+            x = torch.tensor([[a if c % 2 == 0 else -a for c in range(C)]], dtype=torch.bfloat16)
+            codes, scales = orc.norm_rotate_quant(x, norm, np.ones(C, np.float32), None, 0.0, None,
+                                                  W.identity_r())
+            assert np.all(scales == 125), (norm, a)
+            assert np.all(codes == 0xE6), (norm, a)
+
+
+def pin_norm_reduces_to_rotate_quant(orc):
+    """Rows of mean 0 and mean square 1 normalize to themselves (eps = 0);
+    with power-of-two gamma, dyadic beta and lambda the result is exactly
+    rotate_quant((x gamma + beta), lambda): smoothing after gamma and beta."""
+    rng = _rng(41)
+    T, C = 6, 128
+    x = _unit_ms_rows(rng, T, C)
+    r = W.bf16_matrix(W.qr_orthogonal(rng))
+    lam = (np.exp2(rng.integers(-2, 3, C)) * rng.choice([1.0, 1.25, 0.75], C)).astype(np.float32)
+    gamma = np.exp2(rng.integers(-1, 3, C)).astype(np.float32)
+    beta = (rng.integers(-8, 9, C) / 4.0).astype(np.float32)
+    for norm in ("rms", "layer"):
+        for b in (None, beta):
+            c1, s1, y1 = orc.norm_rotate_quant(x, norm, gamma, b, 0.0, lam, r, want_y=True)
+            a = x.to(torch.float32) * _f32(gamma)[None, :]
+            if b is not None:
+                a = a + _f32(b)[None, :]
+            c2, s2, y2 = orc.rotate_quant(a, lam, r, want_y=True)
+            assert np.array_equal(c1, c2) and np.array_equal(s1, s2) and np.array_equal(y1, y2), norm
+
+
+def pin_norm_eps_under_root(orc):
+    """Mean square 1 with eps = 3: 1 / sqrt(1 + 3) halves every value."""
+    rng = _rng(42)
+    x = _unit_ms_rows(rng, 4, 64)
+    gamma = np.ones(64, np.float32)
+    for norm in ("rms", "layer"):
+        c1, s1, y1 = orc.norm_rotate_quant(x, norm, gamma, None, 3.0, None, W.identity_r(), want_y=True)
+        c2, s2, y2 = orc.rotate_quant(x.to(torch.float32) * 0.5, None, W.identity_r(), want_y=True)
+        assert np.array_equal(c1, c2) and np.array_equal(s1, s2) and np.array_equal(y1, y2), norm
+
+
+def pin_norm_scale_invariance(orc):
+    """norm(2^k x) = norm(x) for eps = 0."""
+    rng = _rng(43)
+    x = W.random_activations(rng, 8, 256, torch.bfloat16, scale=3.0)
+    r = W.bf16_matrix(W.qr_orthogonal(rng))
+    gamma = rng.uniform(0.5, 2.0, 256).astype(np.float32)
+    for norm in ("rms", "layer"):
+        base = orc.norm_rotate_quant(x, norm, gamma, None, 0.0, None, r, want_y=True)
+        for k in (-6, 5):
+            got = orc.norm_rotate_quant(x * 2.0 ** k, norm, gamma, None, 0.0, None, r, want_y=True)
+            assert all(np.array_equal(u, v) for u, v in zip(got, base)), (norm, k)
+
+
+def pin_layernorm_shift_invariance(orc):
+    """LayerNorm removes the row mean (x + 5 normalizes like x); RMSNorm does not."""
+    rng = _rng(44)
+    grid = np.clip(np.round(rng.standard_normal((8, 256)) * 8) / 8, -4, 4)  # 1/8 grid: x + 5 stays exact
+    x = torch.from_numpy(grid.astype(np.float32)).to(torch.bfloat16)
+    shifted = (x.to(torch.float32) + 5.0).to(torch.bfloat16)
+    assert torch.equal(shifted.to(torch.float32) - 5.0, x.to(torch.float32))
+    gamma = np.ones(256, np.float32)
+    _, _, y0 = orc.norm_rotate_quant(x, "layer", gamma, None, 1e-6, None, W.identity_r(), want_y=True)
+    _, _, y1 = orc.norm_rotate_quant(shifted, "layer", gamma, None, 1e-6, None, W.identity_r(), want_y=True)
+    assert np.abs(y1 - y0).max() <= 1e-12 * np.abs(y0).max()
+    _, _, z1 = orc.norm_rotate_quant(shifted, "rms", gamma, None, 1e-6, None, W.identity_r(), want_y=True)
+    assert np.abs(z1 - y0).max() > 0.1
+
+
+def pin_norm_gamma_lambda_refactoring(orc):
+    """(gamma 2^k, lambda 2^k) smooths exactly like (gamma, lambda)."""
+    rng = _rng(45)
+    x = W.random_activations(rng, 4, 128, torch.float16)
+    r = W.bf16_matrix(W.qr_orthogonal(rng))
+    gamma = rng.uniform(0.5, 2.0, 128).astype(np.float32)
+    lam = rng.uniform(0.5, 4.0, 128).astype(np.float32)
+    a = orc.norm_rotate_quant(x, "rms", gamma, None, 1e-5, lam, r, want_y=True)
+    b = orc.norm_rotate_quant(x, "rms", gamma * 8, None, 1e-5, lam * 8, r, want_y=True)
+    assert all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
+def pin_norm_zero_row(orc):
+    """A zero row normalizes to zero: all codes 0 and scale byte 0, or the
+    encoding of beta alone."""
+    C = 64
+    x = torch.zeros((2, C), dtype=torch.bfloat16)
+    gamma = np.ones(C, np.float32)
+    beta = np.linspace(-1, 1, C).astype(np.float32)
+    for norm in ("rms", "layer"):
+        codes, scales = orc.norm_rotate_quant(x, norm, gamma, None, 1e-6, None, W.identity_r())
+        assert not codes.any() and not scales.any()
+        c1, s1 = orc.norm_rotate_quant(x, norm, gamma, beta, 1e-6, None, W.identity_r())
+        c2, s2 = orc.rotate_quant(_f32(np.tile(beta, (2, 1))), None, W.identity_r())
+        assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_config1_massive_value,
@@ -331,4 +446,11 @@ ALL_PINS = [
     pin_input_decoding,
     pin_dequant,
     pin_encode_groups_matches_quant,
+    pin_norm_alternating_closed_form,
+    pin_norm_reduces_to_rotate_quant,
+    pin_norm_eps_under_root,
+    pin_norm_scale_invariance,
+    pin_layernorm_shift_invariance,
+    pin_norm_gamma_lambda_refactoring,
+    pin_norm_zero_row,
 ]

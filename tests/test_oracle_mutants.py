@@ -15,8 +15,8 @@ from pins import ALL_PINS
 
 MUTANTS = {
     "transposed_block": ("acc += xs[k] * R[k][n];", "acc += xs[k] * R[n][k];"),
-    "dropped_term": ("for (int k = 0; k < GROUP; ++k)\n                    acc +=",
-                     "for (int k = 1; k < GROUP; ++k)\n                    acc +="),
+    "dropped_term": ("for (int k = 0; k < GROUP; ++k)\n            acc +=",
+                     "for (int k = 1; k < GROUP; ++k)\n            acc +="),
     "scale_off_by_one": ("int e = (q - 1) - 2;", "int e = (q - 1) - 1;"),
     "log2_ceil": ("int e = (q - 1) - 2;", "int e = q - 2;"),
     "tie_up_at_quarter": ("if (a <= 0.25) return 0;", "if (a < 0.25) return 0;"),
@@ -45,6 +45,19 @@ MUTANTS = {
     "rotate_ignores_stride": ("double v = load_elem(x, dtype, t * stride + c);",
                               "double v = load_elem(x, dtype, t * channels + c);"),
     "lambda_wrong_channel": ("v / (double)lambda[c]", "v / (double)lambda[k]"),
+    "norm_eps_outside_root": ("1.0 / sqrt(sq / (double)channels + eps)",
+                              "1.0 / (sqrt(sq / (double)channels) + eps)"),
+    "norm_no_root": ("1.0 / sqrt(sq / (double)channels + eps)", "1.0 / (sq / (double)channels + eps)"),
+    "norm_unbiased_variance": ("sqrt(sq / (double)channels + eps)", "sqrt(sq / (double)(channels - 1) + eps)"),
+    "layernorm_mean_ignored": ("mu = sum / (double)channels;", "mu = 0.0 * sum;"),
+    "norm_gamma_ignored": ("double a = n * (double)gamma[c] +", "double a = n +"),
+    "norm_beta_before_gamma": ("double a = n * (double)gamma[c] + (beta ? (double)beta[c] : 0.0);",
+                               "double a = (n + (beta ? (double)beta[c] : 0.0)) * (double)gamma[c];"),
+    "norm_smooth_before_beta": ("xs[k] = lambda ? a / (double)lambda[c] : a;",
+                                "xs[k] = lambda ? a / (double)lambda[c] + (beta ? (double)beta[c] : 0.0) "
+                                "- (beta ? (double)beta[c] / (double)lambda[c] : 0.0) : a;"),
+    "norm_lambda_multiplies": ("xs[k] = lambda ? a / (double)lambda[c] : a;",
+                               "xs[k] = lambda ? a * (double)lambda[c] : a;"),
 }
 
 
