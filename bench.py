@@ -238,6 +238,90 @@ def bench_gemm(args):
     print(json.dumps(result), flush=True)
 
 
+NORM_SOURCES = ("mxfp4_activation_rotation_amd/csrc/mxq_norm.hip", "mxfp4_activation_rotation_amd/csrc/mxq_device.h")
+NORM_COUNTERS = "profiles/norm_rotate_quant_bf16_8192x4096_hbm_counters.txt"
+
+
+def bench_norm(args):
+    """RMSNorm + smooth + rotate + MXFP4 in one pass (DuQuant++ page sec. 5.2
+    item 1) on the QKV/gate-input shape: bf16 8192 x 4096 residual stream."""
+    import numpy as np
+    import torch
+
+    import mxfp4_activation_rotation_amd as mxq
+    import workloads
+
+    dev = torch.device("cuda:0")
+    wl = workloads.norm_workload()
+    T, C = wl.x.shape
+    step_bytes = T * C * BYTES_PER_ELEM
+    n_buf = max(2, int(np.ceil(768e6 / step_bytes)) + 1)
+    x0 = wl.x.to(dev)
+    xs = [x0] + [x0.clone() for _ in range(n_buf - 1)]
+    gamma = torch.from_numpy(wl.gamma).to(dev)
+    lam = torch.from_numpy(wl.lam).to(dev)
+    r = wl.r_hat.to(dev)
+    outs = [(torch.empty((T, C // 2), dtype=torch.uint8, device=dev),
+             torch.empty((T, C // 32), dtype=torch.uint8, device=dev)) for _ in range(n_buf)]
+
+    def step(i):
+        c, s = outs[i % n_buf]
+        mxq.norm_rotate_quant(xs[i % n_buf], r, gamma, None, lam, norm="rms", eps=wl.eps, codes=c, scales=s)
+
+    for i in range(args.warmup):
+        step(i)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
+    achieved = step_bytes / mean_launch_s / 1e9
+    value = T * C * args.steps / wall / 1e9
+    hbm = read_counters(0, NORM_COUNTERS, NORM_SOURCES)
+    result = {
+        "metric": "RMSNorm+rotate+MXFP4-quant throughput: Gelem/s",
+        "value": round(value, 2), "unit": "Gelem/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "QKV-input shape after RMSNorm: bf16 8192x4096 residual stream (N(0,1), 4 channels "
+                               "+-U(50,200) on 0.5% of tokens), gamma U(0.5,1.5), lognormal lambda, seeded "
+                               "orthogonal R, eps 1e-5",
+                   "tokens": T, "channels": C, "norm": "rms", "lambda": True, "buffer_sets": n_buf,
+                   "parallelism": "single GPU", "launch": "eager launches"},
+        "hbm_gbps": round(value * BYTES_PER_ELEM, 1),
+        "launch_us_mean": round(mean_launch_s * 1e6, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None if hbm is None else round(hbm)},
+        "kernel_source_hash": kernel_source_hash(NORM_SOURCES),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.default()
+        rows = 1024
+        xs_h = wl.x[:rows]
+        times = []
+        t_start = time.perf_counter()
+        while True:
+            t1 = time.perf_counter()
+            orc.norm_rotate_quant(xs_h, "rms", wl.gamma, None, wl.eps, wl.lam, wl.r_hat)
+            times.append(time.perf_counter() - t1)
+            if time.perf_counter() - t_start >= args.cpu_seconds and len(times) >= 3:
+                break
+        med = statistics.median(times)
+        result["cpu_baseline"] = {"value": round(rows * C / med / 1e9, 4), "unit": "Gelem/s",
+                                  "cores": orc.num_threads(), "kind": "oracle",
+                                  "sample": f"the first {rows} rows of the batch, {len(times)} repetitions, "
+                                            f"median {med * 1e3:.0f} ms each"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,6 +339,8 @@ def main():
     ap.add_argument("--gemm", action="store_true",
                     help="time the consumer instead: the W4A4 MXFP4 product of the headline batch's codes "
                          "with absorbed, quantized weights (8192x14336 by 4096x14336)")
+    ap.add_argument("--norm", action="store_true",
+                    help="time the norm-fused path instead: RMSNorm + smooth + rotate + MXFP4 on bf16 8192x4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -281,6 +367,9 @@ def main():
         return
     if args.gemm:
         bench_gemm(args)
+        return
+    if args.norm:
+        bench_norm(args)
         return
     dev = torch.device("cuda:0")
     wl = workloads.make_config(args.workload)

@@ -78,6 +78,8 @@ typedef enum {
 
 typedef enum { MXQ_BF16 = 0, MXQ_FP16 = 1, MXQ_FP32 = 2 } mxq_dtype;
 
+typedef enum { MXQ_NORM_RMS = 0, MXQ_NORM_LAYER = 1 } mxq_norm_kind;
+
 /* Smooth + rotate + MXFP4-quantize in one pass over x.
  * DuQuant++ page sec. 3.3 (online transform X * Lambda^-1 * R) and sec. 2.1
  * (MXFP4 encoding); the smoothing factor is that of sec. 3.1.
@@ -118,6 +120,34 @@ mxq_status mxq_quant(const void *x, int32_t x_dtype, int64_t tokens, int64_t cha
  * the rotated X^ of sec. 3.3, not the original activations. */
 mxq_status mxq_dequant(const uint8_t *codes, const uint8_t *scales, int64_t tokens,
                        int64_t channels, void *y, int32_t y_dtype, void *stream);
+
+/* Norm + smooth + rotate + MXFP4-quantize in one pass over x.
+ * DuQuant++ page sec. 5.2 item 1: the per-channel 1/lambda folds into the
+ * output of the norm in front of the linear layer, and the online steps run
+ * as one kernel.  For every token row h of x (the norm's input):
+ *   RMSNorm   (MXQ_NORM_RMS)    n_c = h_c / sqrt(sum_c h_c^2 / C + eps)
+ *   LayerNorm (MXQ_NORM_LAYER)  n_c = (h_c - mu) / sqrt(sum_c (h_c - mu)^2 / C + eps),
+ *                               mu = sum_c h_c / C (biased variance)
+ *   a_c = n_c * gamma_c + beta_c,  x'_c = a_c / lambda_c
+ * then the rotation and encoding of mxq_rotate_quant.
+ *   x        BF16 or FP16, [tokens][x_row_stride], channels <= 16384
+ *   gamma    fp32 [channels], required; beta fp32 [channels] or NULL (zero);
+ *   lambda   fp32 [channels] or NULL (ones); eps >= 0 (MXQ_ERR_SHAPE if
+ *            negative or NaN).  A row of zeros with eps = 0 is outside the
+ *            contract (0 / 0).
+ *   y_rot    NULL, or fp32 [tokens][channels] receiving the rotated values
+ * Arithmetic: row sums in fp32 per 8 values, accumulated and reduced in
+ * fp64; 1/sqrt in fp64, rounded to fp32; x'_c = fma(n_c, gamma_c/lambda_c,
+ * beta_c/lambda_c) in fp32 (the two factors formed once per block with IEEE
+ * division); the product with the block as in mxq_rotate_quant (3 exact
+ * bf16 terms).  Same layout, alignment (gamma, beta, lambda: 4 bytes) and
+ * error rules as mxq_rotate_quant; norm_kind other than the two values gives
+ * MXQ_ERR_DTYPE. */
+mxq_status mxq_norm_rotate_quant(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
+                                 int64_t x_row_stride, int32_t norm_kind, const float *gamma,
+                                 const float *beta, float eps, const float *lambda,
+                                 const uint16_t *r_hat, uint8_t *codes, uint8_t *scales, float *y_rot,
+                                 void *stream);
 
 /* ---- the consumer: MXFP4 x MXFP4 linear layer ----------------------------
  * DuQuant++ page sec. 3.3 (weight absorption, W^ = R^T Lambda W, so that

@@ -24,7 +24,8 @@ STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_NULL", 2: "MXQ_ERR_SHAPE", 3: "MXQ_ERR_DTYPE"
           4: "MXQ_ERR_ALIGN", 5: "MXQ_ERR_STRIDE", 6: "MXQ_ERR_HIP"}
 EXPORTS = ("mxq_rotate_quant", "mxq_rotate_quant_ex", "mxq_quant", "mxq_dequant",
            "mxq_status_str", "mxq_plan", "mxq_version", "mxq_calib_workspace_bytes",
-           "mxq_calib_worst_group", "mxq_calib_givens", "mxq_absorb_quant", "mxq_gemm_mxfp4")
+           "mxq_calib_worst_group", "mxq_calib_givens", "mxq_absorb_quant", "mxq_gemm_mxfp4",
+           "mxq_norm_rotate_quant")
 
 _lib = None
 
@@ -64,9 +65,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.mxq_calib_givens.argtypes = [vp, i64, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.mxq_absorb_quant.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
     lib.mxq_gemm_mxfp4.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp]
+    lib.mxq_norm_rotate_quant.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, ctypes.c_float, vp, vp, vp, vp,
+                                          vp, vp]
     for f in ("mxq_rotate_quant", "mxq_rotate_quant_ex", "mxq_quant", "mxq_dequant", "mxq_plan",
               "mxq_version", "mxq_calib_worst_group", "mxq_calib_givens", "mxq_absorb_quant",
-              "mxq_gemm_mxfp4"):
+              "mxq_gemm_mxfp4", "mxq_norm_rotate_quant"):
         getattr(lib, f).restype = ctypes.c_int32
     if path is None:
         _lib = lib
@@ -231,6 +234,41 @@ def gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Ten
     if st != 0:
         raise MXQError("mxq_gemm_mxfp4", st)
     return out
+
+
+NORM_KINDS = {"rms": 0, "layer": 1}
+
+
+def norm_rotate_quant(x: torch.Tensor, r_hat: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor | None = None,
+                      lam: torch.Tensor | None = None, *, norm: str = "rms", eps: float = 1e-5, codes=None,
+                      scales=None, y_rot=None, stream=None):
+    """codes, scales = MXFP4(((norm(x) * gamma + beta) / lam) @ BlockDiag(r_hat)).
+
+    norm is "rms" (RMSNorm) or "layer" (LayerNorm); x is the norm's bf16/fp16
+    input [tokens, channels <= 16384]; gamma, beta, lam are contiguous fp32
+    [channels] tensors on x's device (beta and lam may be None).
+    """
+    lib = load()
+    T, C, stride = _check_x(x, (torch.bfloat16, torch.float16))
+    if r_hat.dtype != torch.bfloat16 or r_hat.shape != (32, 32) or not r_hat.is_contiguous() \
+            or r_hat.device != x.device:
+        raise ValueError("r_hat must be a contiguous bf16 [32, 32] tensor on x's device")
+    for name, t, required in (("gamma", gamma, True), ("beta", beta, False), ("lam", lam, False)):
+        if t is None and not required:
+            continue
+        if t is None or t.dtype != torch.float32 or t.shape != (C,) or not t.is_contiguous() or t.device != x.device:
+            raise ValueError(f"{name} must be a contiguous fp32 [channels] tensor on x's device")
+    if norm not in NORM_KINDS:
+        raise ValueError(f"norm must be one of {sorted(NORM_KINDS)}")
+    codes, scales = _outputs(x, T, C, codes, scales)
+    if y_rot is not None and (y_rot.dtype != torch.float32 or y_rot.shape != (T, C) or not y_rot.is_contiguous()):
+        raise ValueError("y_rot must be a contiguous fp32 [tokens, channels] tensor")
+    st = lib.mxq_norm_rotate_quant(_ptr(x), _DT[x.dtype], T, C, stride, NORM_KINDS[norm], _ptr(gamma), _ptr(beta),
+                                   ctypes.c_float(eps), _ptr(lam), _ptr(r_hat), _ptr(codes), _ptr(scales),
+                                   _ptr(y_rot), _stream(x, stream))
+    if st != 0:
+        raise MXQError("mxq_norm_rotate_quant", st)
+    return codes, scales
 
 
 def plan(tokens: int, channels: int, cu_count: int = 256):

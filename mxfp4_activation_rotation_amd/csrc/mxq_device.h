@@ -104,4 +104,35 @@ __device__ __forceinline__ void widen4_f32(u32x4_t q, float* f) {
     for (int i = 0; i < 4; ++i) f[i] = as_f32(q[i]);
 }
 
+// Buffer resource for `bytes` bytes at `base` (raw buffer, stride 0): loads
+// beyond `bytes` return zero and stores beyond it are dropped, which is how
+// lanes of groups past the end of a row are handled without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+constexpr int kAuxNT = 2;  // cache policy bits of buffer ops: non-temporal
+
+// 4x4 transpose of one register per sub-tile across the lanes j, j+16, j+32,
+// j+48: the word in lane 16 k + j, register s moves to lane 16 s + j,
+// register k.  Stage one exchanges lane bit 5 with register bit 1
+// (v_permlane32_swap swaps the upper 32 lanes of its first operand with the
+// lower 32 lanes of its second); stage two exchanges lane bit 4 with register
+// bit 0 (v_permlane16_swap swaps the odd 16-lane rows of its first operand
+// with the even rows of its second).
+__device__ __forceinline__ void transpose_words(uint32_t (&w)[4]) {
+#pragma unroll
+    for (int s0 = 0; s0 < 2; ++s0) {
+        const auto r = __builtin_amdgcn_permlane32_swap(w[s0], w[2 + s0], false, false);
+        w[s0] = r[0];
+        w[2 + s0] = r[1];
+    }
+#pragma unroll
+    for (int s1 = 0; s1 < 2; ++s1) {
+        const auto r = __builtin_amdgcn_permlane16_swap(w[2 * s1], w[2 * s1 + 1], false, false);
+        w[2 * s1] = r[0];
+        w[2 * s1 + 1] = r[1];
+    }
+}
+
 }  // namespace mxq

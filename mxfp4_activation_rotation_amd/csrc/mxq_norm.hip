@@ -1,0 +1,337 @@
+// Norm + smooth + rotate + MXFP4 in one pass over HBM.
+//
+// The DuQuant++ page (sec. 5.2 item 1) notes that the per-channel 1/lambda
+// of the online transform folds into the output of the LayerNorm in front of
+// the linear layer, and asks for the online operations to run as one kernel.
+// This kernel takes the norm's input h (the residual stream) and writes the
+// MXFP4 codes and scales of
+//     y = BlockDiag(R) applied to (norm(h) * gamma + beta) / lambda
+// for RMSNorm, n = h / sqrt(mean(h^2) + eps), or LayerNorm,
+// n = (h - mu) / sqrt(mean((h - mu)^2) + eps).  gamma / lambda and
+// beta / lambda are formed once per block into LDS, so per element the
+// smoothing costs one fused multiply-add.
+//
+// Work decomposition.  A norm needs the statistics of the whole row before
+// any output, so a wave owns whole rows: it loads a row into registers (NT
+// super-tiles of 64 groups, 16 bytes per lane per sub-tile of 16 groups, the
+// layout of the plain rotate kernel), reduces the row's sums across the wave
+// in fp64, and then runs every sub-tile through the same rotate + encode
+// steps as the plain kernel.  Waves walk the rows with a stride of the grid's
+// wave count; channels up to 2048 NT (NT = 1, 2, 4, 8).
+//
+// Row statistics.  The 8 values of a 16-byte load are exact in fp32; their
+// sum (LayerNorm) and sum of squares are formed in fp32 (8 terms) and
+// accumulated in fp64, then reduced across the wave in fp64, so the relative
+// error of the mean square stays near 8 ulp of fp32 whatever the row length.
+// LayerNorm takes the mean in a first sweep over the registers and the
+// centred sum of squares in a second (no cancellation).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "mxq.h"
+#include "mxq_device.h"
+#include "mxq_internal.h"
+
+namespace mxq {
+namespace norm {
+
+constexpr int kWave = 64;
+constexpr int kGroup = 32;
+constexpr int kSub = 4;            // sub-tiles of 16 groups per super-tile
+constexpr int kTileGroups = 64;    // groups per super-tile
+constexpr int kBlockWaves = 4;
+constexpr int kBlockThreads = kWave * kBlockWaves;
+constexpr int kMaxTiles = 8;       // channels <= 16384
+enum : int { kRms = 0, kLayer = 1 };
+
+struct NormArgs {
+    const void* x;
+    int64_t stride;  // elements
+    const float* gamma;
+    const float* beta;
+    const float* lambda;
+    const uint16_t* r_hat;
+    uint8_t* codes;
+    uint8_t* scales;
+    float* y;
+    float eps;
+    int32_t tokens;
+    int32_t channels;
+    int32_t gpr;
+    int32_t waves;  // waves in the grid (row stride)
+};
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+template <int XT, int NORM, int NT>
+__global__ __launch_bounds__(kBlockThreads) void norm_quant_kernel(NormArgs a) {
+    constexpr bool kFp16 = XT == MXQ_FP16;
+    constexpr int kUnits = NT * kSub * 2 * kWave;  // 16-byte factor units per table
+    // Per-channel factors in the order the lanes consume them: unit
+    // ((st * 4 + s) * 2 + h) * 64 + l holds the 4 factors of lane l's channels
+    // 8 q + 4 h .. + 3 of group 64 st + 16 s + j (q = l / 16, j = l % 16), so a
+    // wave reads 1 KB contiguously per ds_read_b128 (no bank conflicts).
+    __shared__ __attribute__((aligned(16))) f32x4_t fm[kUnits];  // gamma / lambda
+    __shared__ __attribute__((aligned(16))) f32x4_t fb[kUnits];  // beta / lambda
+
+    // Factor setup: consecutive threads take consecutive channels (coalesced
+    // loads of gamma, beta, lambda) and scatter the two factors to the lane
+    // order above.  Channels past the row end keep factor 0.
+    const int C = a.channels;
+    float* fmf = reinterpret_cast<float*>(fm);
+    float* fbf = reinterpret_cast<float*>(fb);
+    for (int c = threadIdx.x; c < NT * kTileGroups * kGroup; c += kBlockThreads) {
+        float mv = 0.0f, bv = 0.0f;
+        if (c < C) {
+            const float lam = a.lambda ? a.lambda[c] : 1.0f;
+            mv = a.gamma[c] / lam;
+            bv = a.beta ? a.beta[c] / lam : 0.0f;
+        }
+        const int p = c / kGroup;         // group: 16 ss + j
+        const int k = c % kGroup;         // channel in group: 8 q + 4 h + t
+        const int lane_c = 16 * (k >> 3) + (p & 15);
+        const int unit = ((p >> 4) * 2 + ((k >> 2) & 1)) * kWave + lane_c;
+        fmf[unit * 4 + (k & 3)] = mv;
+        fbf[unit * 4 + (k & 3)] = bv;
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int w = static_cast<int>(blockIdx.x) * kBlockWaves + wave;
+    const int j = lane & 15;
+    const int q = lane >> 4;
+    const uint32_t gpr = static_cast<uint32_t>(a.gpr);
+
+    // The block as the A operands of the two output halves (the layout of the
+    // plain rotate kernel): A_h[t] = R[8q + t][8 (j / 4) + 4 h + j % 4].
+    bf16x8_t A0, A1;
+    {
+        const int n0 = 8 * (j >> 2) + (j & 3);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            A0[t] = __builtin_bit_cast(__bf16, a.r_hat[(8 * q + t) * kGroup + n0]);
+            A1[t] = __builtin_bit_cast(__bf16, a.r_hat[(8 * q + t) * kGroup + n0 + 4]);
+        }
+    }
+
+    const uint32_t row_bytes = gpr * kGroup * 2;
+    const char* xb = static_cast<const char*>(a.x);
+    // (row indices are uniform; readfirstlane tells the compiler so, or it
+    // wraps every buffer access in a loop over distinct descriptors)
+    auto load_row = [&](u32x4_t (&buf)[NT][kSub], int64_t r_any) {
+        const int64_t r = __builtin_amdgcn_readfirstlane(static_cast<int>(r_any));
+        const auto rsrc = row_rsrc(xb + r * a.stride * 2, row_bytes);
+#pragma unroll
+        for (int st = 0; st < NT; ++st)
+#pragma unroll
+            for (int s = 0; s < kSub; ++s) {
+                const uint32_t off = (static_cast<uint32_t>(kTileGroups * st + 16 * s + j) * kGroup + 8 * q) * 2;
+                buf[st][s] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kAuxNT);
+            }
+    };
+    // Two row buffers alternate when they fit in registers (up to 4096
+    // channels): the next row is in flight while the current one computes.
+    constexpr bool kDouble = NT <= 2;
+    u32x4_t bufA[NT][kSub], bufB[NT][kSub];
+    if (w < a.tokens) load_row(bufA, w);
+    for (int64_t r_loop = w; r_loop < a.tokens; r_loop += a.waves) {
+        const int64_t r = __builtin_amdgcn_readfirstlane(static_cast<int>(r_loop));
+        u32x4_t (&buf)[NT][kSub] = bufA;
+        if constexpr (kDouble) {
+            if (r + a.waves < a.tokens) load_row(bufB, r + a.waves);
+        }
+        // ---- row statistics (groups past the row end loaded zeros)
+        float mu = 0.0f;
+        if constexpr (NORM == kLayer) {
+            double part = 0.0;
+#pragma unroll
+            for (int st = 0; st < NT; ++st)
+#pragma unroll
+                for (int s = 0; s < kSub; ++s) {
+                    float f[8];
+                    widen8<kFp16>(buf[st][s], f);
+                    float c8 = 0.0f;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) c8 += f[t];
+                    part += static_cast<double>(c8);
+                }
+            mu = static_cast<float>(wave_sum(part) / C);
+#pragma unroll
+            for (int st = 0; st < NT; ++st)
+#pragma unroll
+                for (int s = 0; s < kSub; ++s) asm volatile("" : "+v"(buf[st][s]));
+        }
+        double part = 0.0;
+#pragma unroll
+        for (int st = 0; st < NT; ++st)
+#pragma unroll
+            for (int s = 0; s < kSub; ++s) {
+                const bool valid = kTileGroups * st + 16 * s + j < a.gpr;
+                float f[8];
+                widen8<kFp16>(buf[st][s], f);
+                float c8 = 0.0f;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const float d = f[t] - mu;
+                    c8 += d * d;
+                }
+                part += valid ? static_cast<double>(c8) : 0.0;
+            }
+        const double var = wave_sum(part) / C;
+        const float inv = static_cast<float>(1.0 / sqrt(var + static_cast<double>(a.eps)));
+        // Keep only the packed row live across the statistics: an empty asm
+        // that claims to change the registers stops the compiler from holding
+        // the widened fp32 copies (twice the registers) until the second use.
+#pragma unroll
+        for (int st = 0; st < NT; ++st)
+#pragma unroll
+            for (int s = 0; s < kSub; ++s) asm volatile("" : "+v"(buf[st][s]));
+
+        // ---- normalize, smooth, rotate, encode
+        const auto crsrc = row_rsrc(a.codes + r * a.gpr * 16, gpr * 16);
+        const auto srsrc = row_rsrc(a.scales + r * a.gpr, gpr);
+#pragma unroll
+        for (int st = 0; st < NT; ++st) {
+            uint32_t word[kSub];
+            uint32_t sc[kSub];
+#pragma unroll
+            for (int s = 0; s < kSub; ++s) {
+                const int ss = st * kSub + s;
+                const f32x4_t m0 = fm[(ss * 2 + 0) * kWave + lane];
+                const f32x4_t m1 = fm[(ss * 2 + 1) * kWave + lane];
+                const f32x4_t b0 = fb[(ss * 2 + 0) * kWave + lane];
+                const f32x4_t b1 = fb[(ss * 2 + 1) * kWave + lane];
+                float f[8];
+                widen8<kFp16>(buf[st][s], f);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float d0 = NORM == kLayer ? (f[t] - mu) * inv : f[t] * inv;
+                    const float d1 = NORM == kLayer ? (f[4 + t] - mu) * inv : f[4 + t] * inv;
+                    f[t] = __builtin_fmaf(d0, m0[t], b0[t]);
+                    f[4 + t] = __builtin_fmaf(d1, m1[t], b1[t]);
+                }
+                // exact bf16 terms of the fp32 values (3 terms cover 24 bits)
+                f32x4_t d0 = {}, d1 = {};
+#pragma unroll
+                for (int term = 0; term < 3; ++term) {
+                    u32x4_t bt;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) bt[i] = bf16_pair_hi(f[2 * i], f[2 * i + 1]);
+                    const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bt);
+                    d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, b, d0, 0, 0, 0);
+                    d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b, d1, 0, 0, 0);
+                    if (term < 2) {
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) f[t] = bf16_residual(f[t]);
+                    }
+                }
+                float v[8];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    v[t] = d0[t];
+                    v[4 + t] = d1[t];
+                }
+                const uint32_t scale_bits = e8m0_scale_bits(group_amax8(v));
+                sc[s] = scale_bits >> 23;
+                word[s] = encode8(v, as_f32(scale_bits));
+                if (a.y) {
+                    const auto yrsrc = row_rsrc(a.y + r * a.gpr * kGroup, gpr * kGroup * 4);
+                    const uint32_t off = (static_cast<uint32_t>(kTileGroups * st + 16 * s + j) * kGroup + 8 * q) * 4;
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        u32x4_t{as_u32(v[0]), as_u32(v[1]), as_u32(v[2]), as_u32(v[3])}, yrsrc, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        u32x4_t{as_u32(v[4]), as_u32(v[5]), as_u32(v[6]), as_u32(v[7])}, yrsrc, off + 16, 0, 0);
+                }
+            }
+            transpose_words(word);
+            const uint32_t S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
+            const uint32_t g = static_cast<uint32_t>(kTileGroups * st + lane);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{word[0], word[1], word[2], word[3]}, crsrc, g * 16, 0,
+                                                   kAuxNT);
+            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, g, 0, 0);
+        }
+        if constexpr (kDouble) {
+#pragma unroll
+            for (int st = 0; st < NT; ++st)
+#pragma unroll
+                for (int s = 0; s < kSub; ++s) bufA[st][s] = bufB[st][s];
+        } else {
+            if (r + a.waves < a.tokens) load_row(bufA, r + a.waves);
+        }
+    }
+}
+
+bool aligned_to(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// Resident blocks per CU the instance allows (registers, LDS), queried once.
+template <int XT, int NORM, int NT>
+int blocks_per_cu() {
+    static std::atomic<int> cached{0};
+    int v = cached.load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, norm_quant_kernel<XT, NORM, NT>, kBlockThreads, 0) !=
+            hipSuccess ||
+        v <= 0)
+        v = 1;
+    cached.store(v, std::memory_order_relaxed);
+    return v;
+}
+
+template <int XT, int NORM, int NT>
+mxq_status launch_nt(NormArgs a, hipStream_t st) {
+    const int per_cu = blocks_per_cu<XT, NORM, NT>();
+    const int64_t want = (static_cast<int64_t>(a.tokens) + kBlockWaves - 1) / kBlockWaves;
+    const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
+    const int blocks = static_cast<int>(want < cap ? want : cap);
+    a.waves = blocks * kBlockWaves;
+    hipLaunchKernelGGL((norm_quant_kernel<XT, NORM, NT>), dim3(blocks), dim3(kBlockThreads), 0, st, a);
+    return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+}
+
+template <int XT, int NORM>
+mxq_status launch_norm(const NormArgs& a, hipStream_t st) {
+    const int tiles = (a.gpr + kTileGroups - 1) / kTileGroups;
+    if (tiles <= 1) return launch_nt<XT, NORM, 1>(a, st);
+    if (tiles <= 2) return launch_nt<XT, NORM, 2>(a, st);
+    if (tiles <= 4) return launch_nt<XT, NORM, 4>(a, st);
+    return launch_nt<XT, NORM, 8>(a, st);
+}
+
+}  // namespace norm
+}  // namespace mxq
+
+using namespace mxq::norm;
+
+extern "C" mxq_status mxq_norm_rotate_quant(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels,
+                                            int64_t x_row_stride, int32_t norm_kind, const float* gamma,
+                                            const float* beta, float eps, const float* lambda,
+                                            const uint16_t* r_hat, uint8_t* codes, uint8_t* scales, float* y_rot,
+                                            void* stream) {
+    if (x_dtype != MXQ_BF16 && x_dtype != MXQ_FP16) return MXQ_ERR_DTYPE;
+    if (norm_kind != MXQ_NORM_RMS && norm_kind != MXQ_NORM_LAYER) return MXQ_ERR_DTYPE;
+    if (tokens < 0 || channels < 0 || channels % kGroup || channels > kMaxTiles * kTileGroups * kGroup ||
+        tokens >= (int64_t(1) << 31))
+        return MXQ_ERR_SHAPE;
+    if (!(eps >= 0.0f) || eps > 3.0e38f) return MXQ_ERR_SHAPE;
+    if (tokens == 0 || channels == 0) return MXQ_OK;
+    if (!x || !gamma || !r_hat || !codes || !scales) return MXQ_ERR_NULL;
+    if (x_row_stride < channels) return MXQ_ERR_STRIDE;
+    if (!aligned_to(x, 16) || (x_row_stride * 2) % 16 || !aligned_to(codes, 16) || !aligned_to(r_hat, 2) ||
+        !aligned_to(gamma, 4) || (beta && !aligned_to(beta, 4)) || (lambda && !aligned_to(lambda, 4)) ||
+        (y_rot && !aligned_to(y_rot, 16)))
+        return MXQ_ERR_ALIGN;
+    NormArgs a{x,      x_row_stride, gamma, beta, lambda, r_hat, codes, scales, y_rot, eps,
+               static_cast<int32_t>(tokens), static_cast<int32_t>(channels),
+               static_cast<int32_t>(channels / kGroup), 0};
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (x_dtype == MXQ_BF16)
+        return norm_kind == MXQ_NORM_RMS ? launch_norm<MXQ_BF16, kRms>(a, st) : launch_norm<MXQ_BF16, kLayer>(a, st);
+    return norm_kind == MXQ_NORM_RMS ? launch_norm<MXQ_FP16, kRms>(a, st) : launch_norm<MXQ_FP16, kLayer>(a, st);
+}

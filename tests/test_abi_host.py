@@ -180,3 +180,32 @@ def test_gemm_validation(lib):
     assert gm(lib, b=P_ODD) == ALIGN
     assert gm(lib, sa=ctypes.c_void_p(0x10001)) == ALIGN
     assert gm(lib, y=ctypes.c_void_p(0x10002)) == ALIGN            # fp32 output: 4-byte alignment
+
+
+def nq(lib, x=P, dt=0, T=8, C=64, stride=64, kind=0, g=P, b=None, eps=1e-5, lam=None, r=P, codes=P, scales=P,
+       y=None):
+    return lib.mxq_norm_rotate_quant(x, dt, T, C, stride, kind, g, b, ctypes.c_float(eps), lam, r, codes, scales,
+                                     y, None)
+
+
+def test_norm_rotate_quant_validation(lib):
+    assert nq(lib, dt=2) == DTYPE
+    assert nq(lib, kind=2) == DTYPE
+    assert nq(lib, kind=-1) == DTYPE
+    assert nq(lib, C=48, stride=48) == SHAPE
+    assert nq(lib, C=16384 + 32, stride=16384 + 32) == SHAPE   # rows live in registers: at most 16384
+    assert nq(lib, T=-1) == SHAPE
+    assert nq(lib, T=1 << 31) == SHAPE
+    assert nq(lib, eps=-1.0) == SHAPE
+    assert nq(lib, eps=float("nan")) == SHAPE
+    assert nq(lib, T=0, x=None, g=None, r=None, codes=None, scales=None) == OK
+    assert nq(lib, x=None) == NULL
+    assert nq(lib, g=None) == NULL
+    assert nq(lib, r=None) == NULL
+    assert nq(lib, scales=None) == NULL
+    assert nq(lib, stride=32) == STRIDE
+    assert nq(lib, x=P_ODD) == ALIGN
+    assert nq(lib, codes=P_ODD) == ALIGN
+    assert nq(lib, y=P_ODD) == ALIGN
+    assert nq(lib, g=ctypes.c_void_p(0x10002)) == ALIGN
+    assert nq(lib, stride=68) == ALIGN

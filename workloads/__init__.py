@@ -270,3 +270,43 @@ def random_mxfp4(rng: np.random.Generator, rows: int, k: int, scale_lo: int = 11
     codes = rng.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
     scales = rng.integers(scale_lo, scale_hi + 1, size=(rows, k // GROUP), dtype=np.uint8)
     return codes, scales
+
+
+# ---- the norm in front of the rotation ------------------------------------------
+
+NORM_SHAPE = (8192, 4096)  # LLaMA-3-8B hidden size: the input of the QKV and gate/up norms
+
+
+@dataclasses.dataclass
+class NormWorkload:
+    """Residual-stream rows h (the norm's input) and the norm's parameters."""
+
+    x: torch.Tensor
+    gamma: np.ndarray
+    beta: np.ndarray | None
+    lam: np.ndarray
+    r_hat: torch.Tensor
+    eps: float
+    meta: dict
+
+
+def norm_workload(tokens: int = NORM_SHAPE[0], channels: int = NORM_SHAPE[1], seed: int = 4001,
+                  dtype: torch.dtype = torch.bfloat16, with_beta: bool = False) -> NormWorkload:
+    """Seeded stand-in for a pre-norm residual stream: N(0, 1) rows whose 4
+    seeded channels carry +-U(50, 200) on 0.5% of the tokens (the massive
+    residual-stream activations of LLaMA-type models), gamma ~ U(0.5, 1.5),
+    beta ~ N(0, 0.1) when asked for (LayerNorm), lambda lognormal(0, 0.5),
+    seeded orthogonal block, eps 1e-5."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((tokens, channels))
+    ch = np.sort(rng.choice(channels, size=min(4, channels), replace=False))
+    n_tok = max(1, int(round(0.005 * tokens)))
+    toks = np.sort(rng.choice(tokens, size=n_tok, replace=False))
+    x[np.ix_(toks, ch)] = rng.uniform(50.0, 200.0, (n_tok, ch.size)) * rng.choice(np.array([-1.0, 1.0]),
+                                                                                  (n_tok, ch.size))
+    gamma = rng.uniform(0.5, 1.5, channels).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(channels)).astype(np.float32) if with_beta else None
+    lam = np.exp(0.5 * rng.standard_normal(channels)).astype(np.float32)
+    r = qr_orthogonal(rng)
+    return NormWorkload(to_dtype(x, dtype), gamma, beta, lam, bf16_matrix(r), 1e-5,
+                        {"seed": seed, "massive_channels": ch.tolist(), "massive_tokens": int(n_tok)})
