@@ -60,6 +60,8 @@ class Oracle:
         self.lib.oracle_rotate_quant.argtypes = [vp, i32, i64, i64, i64, vp, vp, i32, vp, vp, vp]
         self.lib.oracle_encode_groups.argtypes = [vp, i64, vp, vp]
         self.lib.oracle_dequant.argtypes = [vp, vp, i64, i64, vp]
+        self.lib.oracle_rotate_quant_block.argtypes = [vp, i32, i64, i64, i64, vp, vp, i32, i32, vp, vp, vp]
+        self.lib.oracle_rotate_quant_block.restype = ctypes.c_int
         self.lib.oracle_norm_rotate_quant.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, ctypes.c_double,
                                                       vp, vp, i32, vp, vp, vp]
         for f in ("oracle_quant", "oracle_rotate_quant", "oracle_encode_groups",
@@ -155,6 +157,26 @@ class Oracle:
                                           self._ptr(codes), self._ptr(scales), self._ptr(y))
         if rc != 0:
             raise ValueError(f"oracle_rotate_quant rejected the shape (rc={rc})")
+        return (codes, scales, y) if want_y else (codes, scales)
+
+    def rotate_quant_block(self, x, lam, r_block, want_y: bool = False):
+        """Rotation by a B x B block (B = 16, 32, 64, 128: the block sizes of
+        the DuQuant++ page's ablation, sec. 4.3), then MXFP4 of every 32-wide
+        group.  ``r_block`` is B x B (bf16 torch tensor or fp64 array)."""
+        arr, code, T, C, stride = self._raw(x)
+        lam = self._lambda(lam, C)
+        r, r_code = self._r_hat(r_block)
+        B = r.shape[0]
+        if r.shape != (B, B):
+            raise ValueError("r_block must be square")
+        codes = np.zeros((T, C // 2), np.uint8)
+        scales = np.zeros((T, C // GROUP), np.uint8)
+        y = np.zeros((T, C), np.float64) if want_y else None
+        rc = self.lib.oracle_rotate_quant_block(self._ptr(arr), code, _i64(T), _i64(C), _i64(stride),
+                                                self._ptr(lam), self._ptr(r), r_code, B,
+                                                self._ptr(codes), self._ptr(scales), self._ptr(y))
+        if rc != 0:
+            raise ValueError(f"oracle_rotate_quant_block rejected the arguments (rc={rc})")
         return (codes, scales, y) if want_y else (codes, scales)
 
     def norm_rotate_quant(self, x, norm: str, gamma, beta, eps: float, lam, r_hat, want_y: bool = False):

@@ -54,21 +54,24 @@ def smoothed(x, lam=None) -> np.ndarray:
     return xs
 
 
-def worst_group(x, lam=None):
-    """(group index, its L-infinity norm, X_worst [T, 32] fp64)."""
+def worst_group(x, lam=None, block: int = GROUP):
+    """(group index, its L-infinity norm, X_worst [T, block] fp64).  ``block``
+    is the rotation block width (32 on the page's main path; 16, 64 and 128
+    in its block-size ablation, sec. 4.3)."""
     xs = smoothed(x, lam)
     T, Cn = xs.shape
-    per_group = np.abs(xs).reshape(T, Cn // GROUP, GROUP).max(axis=(0, 2))
+    per_group = np.abs(xs).reshape(T, Cn // block, block).max(axis=(0, 2))
     g = int(np.argmax(per_group))  # first index among ties
-    return g, float(per_group[g]), np.ascontiguousarray(xs[:, g * GROUP:(g + 1) * GROUP])
+    return g, float(per_group[g]), np.ascontiguousarray(xs[:, g * block:(g + 1) * block])
 
 
 def greedy_givens(x_worst, steps: int = 128):
-    """Greedy outlier-aware search.  Returns (R [32, 32], X_worst * R,
-    norm history [steps_done + 1], chosen pairs [(d, j)])."""
+    """Greedy outlier-aware search.  Returns (R [n, n], X_worst * R, norm
+    history [steps_done + 1], chosen pairs [(d, j)]), n = X_worst's width."""
     cur = np.array(x_worst, dtype=np.float64, copy=True)
-    R = np.eye(GROUP)
-    colmax = np.abs(cur).max(axis=0) if cur.shape[0] else np.zeros(GROUP)
+    n = cur.shape[1]
+    R = np.eye(n)
+    colmax = np.abs(cur).max(axis=0) if cur.shape[0] else np.zeros(n)
     linf = float(colmax.max())
     history = [linf]
     pairs = []
@@ -78,7 +81,7 @@ def greedy_givens(x_worst, steps: int = 128):
         d = int(np.argmax(colmax))
         xd = cur[:, d]
         best = None
-        for j in range(GROUP):
+        for j in range(n):
             if j == d:
                 continue
             xj = cur[:, j]
@@ -86,7 +89,7 @@ def greedy_givens(x_worst, steps: int = 128):
             new_j = S * xd + C * xj
             m_d = float(np.abs(new_d).max())
             m_j = float(np.abs(new_j).max())
-            rest = max([float(colmax[k]) for k in range(GROUP) if k != d and k != j], default=0.0)
+            rest = max([float(colmax[k]) for k in range(n) if k != d and k != j], default=0.0)
             norm = max(m_d, m_j, rest)
             if best is None or norm < best[0]:
                 best = (norm, j, m_d, m_j, new_d, new_j)

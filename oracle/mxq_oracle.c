@@ -25,6 +25,10 @@
  *                  scales [T][C/32] as E8M0 bytes (e + 127)
  *   dequant        (-1)^s * {0,.5,1,1.5,2,3,4,6}[m] * 2^(S-127)  (OCP MX v1.0
  *                  E2M1 and E8M0 tables; S = 255 is NaN)
+ *   block size     DuQuant++ page, sec. 4.3 (ablation of the rotation block
+ *                  size B in {16, 32, 64, 128}; MXFP4 groups stay 32 wide):
+ *                  y_b = x'_b * R_B for every B-channel block b, then the
+ *                  encoding of every 32-element group of y
  *   norm in front  DuQuant++ page, sec. 5.2 item 1: the per-channel 1/lambda
  *                  folds into the output of a preceding LayerNorm.  Textbook
  *                  definitions, per token row of C channels:
@@ -38,15 +42,19 @@
  * (worked example of sec. 2.1, brute-force nearest-code search, identity
  * rotation, dense block-diagonal product, norm preservation, scale and sign
  * equivariance, dequant exactness and idempotence); oracle_norm_rotate_quant
- * by tests/test_norm_oracle.py (closed forms of alternating rows, scale and
- * shift invariance, power-of-two refactoring of gamma and lambda, eps on zero
- * rows, reduction to oracle_rotate_quant).  No function is unpinned.
+ * by the norm pins (closed forms of alternating rows, scale and shift
+ * invariance, power-of-two refactoring of gamma and lambda, eps on zero rows,
+ * reduction to oracle_rotate_quant); oracle_rotate_quant_block by the block
+ * pins (B = 32 equals oracle_rotate_quant, block-diagonal embeddings of
+ * smaller blocks, dense products, norm preservation).  No function is
+ * unpinned.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC (no -ffast-math).
  */
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -176,11 +184,17 @@ int oracle_quant(const void *x, int dtype, int64_t tokens, int64_t channels, int
  *   codes, scales = MXFP4(y)                              sec. 2.1
  * r is the shared 32x32 block, row-major, y_n = sum_k x'_k r[k][n]; r_dtype
  * is OR_BF16 (bits) or OR_FP64.  y_out (fp64 [tokens][channels]) may be NULL. */
-/* y_n = sum_k x'_k R[k][n] for one 32-element group (row-vector product). */
-static void rotate_group(const double *xs, const double R[GROUP][GROUP], double *y) {
-    for (int n = 0; n < GROUP; ++n) {
+/* Smoothing of one element: x' = x / lambda_c (lambda NULL: all ones). */
+static double smooth(double v, const float *lambda, int64_t c) {
+    return lambda ? v / (double)lambda[c] : v;
+}
+
+/* y_n = sum_k x'_k R[k][n], n, k < B, for one block of B channels
+ * (row-vector product; R holds the block in its top-left B x B corner). */
+static void rotate_block(const double *xs, const double R[128][128], int B, double *y) {
+    for (int n = 0; n < B; ++n) {
         double acc = 0.0;
-        for (int k = 0; k < GROUP; ++k)
+        for (int k = 0; k < B; ++k)
             acc += xs[k] * R[k][n];
         y[n] = acc;
     }
@@ -190,7 +204,7 @@ int oracle_rotate_quant(const void *x, int dtype, int64_t tokens, int64_t channe
                         const float *lambda, const void *r, int r_dtype,
                         uint8_t *codes, uint8_t *scales, double *y_out) {
     if (tokens < 0 || channels < 0 || channels % GROUP != 0 || stride < channels) return 2;
-    double R[GROUP][GROUP];
+    double R[128][128];
     for (int k = 0; k < GROUP; ++k)
         for (int n = 0; n < GROUP; ++n)
             R[k][n] = load_elem(r, r_dtype, k * GROUP + n);
@@ -202,9 +216,9 @@ int oracle_rotate_quant(const void *x, int dtype, int64_t tokens, int64_t channe
             for (int k = 0; k < GROUP; ++k) {
                 int64_t c = g * GROUP + k;
                 double v = load_elem(x, dtype, t * stride + c);
-                xs[k] = lambda ? v / (double)lambda[c] : v;
+                xs[k] = smooth(v, lambda, c);
             }
-            rotate_group(xs, R, y);
+            rotate_block(xs, R, GROUP, y);
             if (y_out)
                 for (int n = 0; n < GROUP; ++n)
                     y_out[t * channels + g * GROUP + n] = y[n];
@@ -215,6 +229,50 @@ int oracle_rotate_quant(const void *x, int dtype, int64_t tokens, int64_t channe
 }
 
 /* Dequantize: value = (-1)^s * E2M1[m] * 2^(S - 127); S = 255 gives NaN. */
+/* Rotation by a B x B block (B = 16, 32, 64 or 128; r is B x B, row-major,
+ * y_n = sum_k x'_k r[k][n] within each block of B channels), then MXFP4 of
+ * every 32-element group of the rotated row.  channels must be a multiple
+ * of B and of 32.  y_out, when not NULL, receives the rotated values. */
+int oracle_rotate_quant_block(const void *x, int dtype, int64_t tokens, int64_t channels, int64_t stride,
+                              const float *lambda, const void *r, int r_dtype, int block,
+                              uint8_t *codes, uint8_t *scales, double *y_out) {
+    if (block != 16 && block != 32 && block != 64 && block != 128) return 3;
+    if (tokens < 0 || channels < 0 || channels % block != 0 || channels % GROUP != 0 || stride < channels)
+        return 2;
+    double R[128][128];
+    for (int k = 0; k < block; ++k)
+        for (int n = 0; n < block; ++n)
+            R[k][n] = load_elem(r, r_dtype, k * block + n);
+    const int64_t gpr = channels / GROUP;
+    int status = 0;
+#pragma omp parallel
+    {
+        double *row = (double *)malloc((size_t)(channels > 0 ? channels : 1) * sizeof(double));
+        if (!row) {
+#pragma omp atomic write
+            status = 4;
+        }
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < tokens; ++t) {
+            if (!row) continue;
+            double xs[128];
+            for (int64_t b0 = 0; b0 < channels; b0 += block) {
+                for (int k = 0; k < block; ++k) {
+                    int64_t c = b0 + k;
+                    xs[k] = smooth(load_elem(x, dtype, t * stride + c), lambda, c);
+                }
+                rotate_block(xs, R, block, row + b0);
+            }
+            for (int64_t g = 0; g < gpr; ++g)
+                encode_group(row + g * GROUP, codes + (t * gpr + g) * (GROUP / 2), scales + t * gpr + g);
+            if (y_out)
+                for (int64_t c = 0; c < channels; ++c) y_out[t * channels + c] = row[c];
+        }
+        free(row);
+    }
+    return status;
+}
+
 /* RMSNorm (norm_kind 0) or LayerNorm (norm_kind 1) of every row, then
  * gamma, beta, smoothing, rotation and encoding as in oracle_rotate_quant.
  * y_out, when not NULL, receives the rotated values [tokens][channels]. */
@@ -225,7 +283,7 @@ int oracle_norm_rotate_quant(const void *x, int dtype, int64_t tokens, int64_t c
     if (tokens < 0 || channels <= 0 || channels % GROUP != 0 || stride < channels) return 2;
     if (norm_kind != 0 && norm_kind != 1) return 3;
     if (!gamma) return 1;
-    double R[GROUP][GROUP];
+    double R[128][128];
     for (int k = 0; k < GROUP; ++k)
         for (int n = 0; n < GROUP; ++n)
             R[k][n] = load_elem(r, r_dtype, k * GROUP + n);
@@ -251,9 +309,9 @@ int oracle_norm_rotate_quant(const void *x, int dtype, int64_t tokens, int64_t c
                 int64_t c = g * GROUP + k;
                 double n = (load_elem(x, dtype, t * stride + c) - mu) * inv;
                 double a = n * (double)gamma[c] + (beta ? (double)beta[c] : 0.0);
-                xs[k] = lambda ? a / (double)lambda[c] : a;
+                xs[k] = smooth(a, lambda, c);
             }
-            rotate_group(xs, R, y);
+            rotate_block(xs, R, GROUP, y);
             if (y_out)
                 for (int n = 0; n < GROUP; ++n)
                     y_out[t * channels + g * GROUP + n] = y[n];

@@ -431,6 +431,70 @@ def pin_norm_zero_row(orc):
         assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
 
 
+# ---- rotation block sizes 16 / 64 / 128 (DuQuant++ page sec. 4.3) ----------
+
+def _block_diag(blocks):
+    n = sum(b.shape[0] for b in blocks)
+    out = np.zeros((n, n))
+    o = 0
+    for b in blocks:
+        k = b.shape[0]
+        out[o:o + k, o:o + k] = b
+        o += k
+    return out
+
+
+def pin_block32_is_rotate_quant(orc):
+    """B = 32 through the block entry is exactly the 32-wide rotation."""
+    rng = _rng(51)
+    x = W.random_activations(rng, 7, 256, torch.bfloat16, scale=4.0)
+    lam = rng.uniform(0.5, 2.0, 256).astype(np.float32)
+    r = W.bf16_matrix(W.qr_orthogonal(rng))
+    a = orc.rotate_quant_block(x, lam, r, want_y=True)
+    b = orc.rotate_quant(x, lam, r, want_y=True)
+    assert all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
+def pin_block_embeddings(orc):
+    """A B-block equals the 2B-block that holds it twice on the diagonal
+    (the zero entries add exact zeros): 16 in 32, 32 in 64, 64 in 128."""
+    rng = _rng(52)
+    x = W.random_activations(rng, 5, 512, torch.float16, scale=2.0)
+    lam = rng.uniform(0.5, 2.0, 512).astype(np.float32)
+    for B in (16, 32, 64):
+        rb = W.qr_orthogonal(rng, B)
+        small = orc.rotate_quant_block(x, lam, rb, want_y=True)
+        big = orc.rotate_quant_block(x, lam, _block_diag([rb, rb]), want_y=True)
+        assert all(np.array_equal(u, v) for u, v in zip(small, big)), B
+
+
+def pin_block_dense_product(orc):
+    """y = (x / lam) BlockDiag(R_B) as one dense fp64 product, for a
+    non-symmetric R at every block size."""
+    rng = _rng(53)
+    x = W.random_activations(rng, 4, 256, torch.bfloat16, scale=3.0)
+    lam = rng.uniform(0.5, 2.0, 256).astype(np.float32)
+    xs = x.to(torch.float64).numpy() / lam.astype(np.float64)[None, :]
+    for B in (16, 32, 64, 128):
+        rb = rng.standard_normal((B, B))
+        _, _, y = orc.rotate_quant_block(x, lam, rb, want_y=True)
+        dense = xs @ _block_diag([rb] * (256 // B))
+        assert np.abs(y - dense).max() <= 1e-12 * np.abs(dense).max(), B
+
+
+def pin_block_norm_preservation(orc):
+    """An orthogonal B-block keeps the norm of every B-channel block."""
+    rng = _rng(54)
+    x = W.random_activations(rng, 6, 512, torch.bfloat16, scale=5.0)
+    xs = x.to(torch.float64).numpy()
+    for B in (16, 64, 128):
+        rb = W.random_hadamard(rng, B)
+        _, _, y = orc.rotate_quant_block(x, None, rb, want_y=True)
+        ny = np.linalg.norm(y.reshape(6, -1, B), axis=2)
+        nx = np.linalg.norm(xs.reshape(6, -1, B), axis=2)
+        assert np.abs(ny - nx).max() <= 1e-12 * nx.max(), B
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_config1_massive_value,
@@ -453,4 +517,8 @@ ALL_PINS = [
     pin_layernorm_shift_invariance,
     pin_norm_gamma_lambda_refactoring,
     pin_norm_zero_row,
+    pin_block32_is_rotate_quant,
+    pin_block_embeddings,
+    pin_block_dense_product,
+    pin_block_norm_preservation,
 ]

@@ -96,3 +96,26 @@ def test_worst_group_with_and_without_lambda():
     x[2, 70] = 9.0     # tie with group 1 without lambda: lowest index
     g, _, _ = CAL.worst_group(x)
     assert g == 1
+
+
+@pytest.mark.parametrize("n", [16, 64, 128])
+def test_other_block_widths(n):
+    """The search at the ablation's block widths (DuQuant++ page sec. 4.3):
+    one step picks the candidate an explicit enumeration finds best, a flat
+    Hadamard block takes no step, and the worst block is found at width n."""
+    rng = np.random.default_rng(60 + n)
+    x = rng.standard_normal((9, n)) * np.exp(rng.standard_normal(n))
+    d = int(np.argmax(np.abs(x).max(axis=0)))
+    norms = [(np.abs(x @ givens_matrix(d, j, n)).max(), j) for j in range(n) if j != d]
+    best_norm, best_j = min(norms)
+    R, cur, hist, pairs = CAL.greedy_givens(x, steps=1)
+    assert R.shape == (n, n)
+    if best_norm <= np.abs(x).max():
+        assert pairs == [(d, best_j)]
+    h = W.sylvester_hadamard(n) / math.sqrt(n)
+    _, _, _, pairs = CAL.greedy_givens(h, steps=8)
+    assert pairs == []
+    big = np.zeros((3, 4 * n))
+    big[1, 2 * n + 5] = 7.0
+    g, linf, xw = CAL.worst_group(big, block=n)
+    assert g == 2 and linf == 7.0 and xw.shape == (3, n)

@@ -15,8 +15,6 @@ from pins import ALL_PINS
 
 MUTANTS = {
     "transposed_block": ("acc += xs[k] * R[k][n];", "acc += xs[k] * R[n][k];"),
-    "dropped_term": ("for (int k = 0; k < GROUP; ++k)\n            acc +=",
-                     "for (int k = 1; k < GROUP; ++k)\n            acc +="),
     "scale_off_by_one": ("int e = (q - 1) - 2;", "int e = (q - 1) - 1;"),
     "log2_ceil": ("int e = (q - 1) - 2;", "int e = q - 2;"),
     "tie_up_at_quarter": ("if (a <= 0.25) return 0;", "if (a < 0.25) return 0;"),
@@ -27,8 +25,6 @@ MUTANTS = {
     "negative_zero_kept": ("int neg = signbit(v) && mag != 0;", "int neg = signbit(v);"),
     "nibbles_swapped": ("codes16[j] = (uint8_t)(c[2 * j] | (c[2 * j + 1] << 4));",
                         "codes16[j] = (uint8_t)(c[2 * j + 1] | (c[2 * j] << 4));"),
-    "lambda_multiplies": ("xs[k] = lambda ? v / (double)lambda[c] : v;",
-                          "xs[k] = lambda ? v * (double)lambda[c] : v;"),
     "clamp_low_wrong": ("if (e < -127) e = -127;", "if (e < -126) e = -126;"),
     "clamp_high_wrong": ("if (e > 127) e = 127;", "if (e > 126) e = 126;"),
     "amax_skips_first": ("for (int n = 0; n < GROUP; ++n) {\n        double a = fabs(y[n]);",
@@ -44,7 +40,6 @@ MUTANTS = {
                              "y[k] = load_elem(x, dtype, t * channels + g * GROUP + k);"),
     "rotate_ignores_stride": ("double v = load_elem(x, dtype, t * stride + c);",
                               "double v = load_elem(x, dtype, t * channels + c);"),
-    "lambda_wrong_channel": ("v / (double)lambda[c]", "v / (double)lambda[k]"),
     "norm_eps_outside_root": ("1.0 / sqrt(sq / (double)channels + eps)",
                               "1.0 / (sqrt(sq / (double)channels) + eps)"),
     "norm_no_root": ("1.0 / sqrt(sq / (double)channels + eps)", "1.0 / (sq / (double)channels + eps)"),
@@ -53,11 +48,19 @@ MUTANTS = {
     "norm_gamma_ignored": ("double a = n * (double)gamma[c] +", "double a = n +"),
     "norm_beta_before_gamma": ("double a = n * (double)gamma[c] + (beta ? (double)beta[c] : 0.0);",
                                "double a = (n + (beta ? (double)beta[c] : 0.0)) * (double)gamma[c];"),
-    "norm_smooth_before_beta": ("xs[k] = lambda ? a / (double)lambda[c] : a;",
-                                "xs[k] = lambda ? a / (double)lambda[c] + (beta ? (double)beta[c] : 0.0) "
-                                "- (beta ? (double)beta[c] / (double)lambda[c] : 0.0) : a;"),
-    "norm_lambda_multiplies": ("xs[k] = lambda ? a / (double)lambda[c] : a;",
-                               "xs[k] = lambda ? a * (double)lambda[c] : a;"),
+    "block_groups_misaligned": ("encode_group(row + g * GROUP,", "encode_group(row + g * GROUP + (g > 0),"),
+    "dropped_term": ("for (int k = 0; k < B; ++k)\n            acc +=",
+                     "for (int k = 1; k < B; ++k)\n            acc +="),
+    "lambda_multiplies": ("return lambda ? v / (double)lambda[c] : v;",
+                          "return lambda ? v * (double)lambda[c] : v;"),
+    "lambda_wrong_channel": ("xs[k] = smooth(v, lambda, c);", "xs[k] = smooth(v, lambda, k);"),
+    "norm_smooth_before_beta": ("xs[k] = smooth(a, lambda, c);",
+                                "xs[k] = smooth(n * (double)gamma[c], lambda, c) + (beta ? (double)beta[c] : 0.0);"),
+    "norm_lambda_ignored": ("xs[k] = smooth(a, lambda, c);", "xs[k] = a;"),
+    "block_lambda_ignored": ("xs[k] = smooth(load_elem(x, dtype, t * stride + c), lambda, c);",
+                             "xs[k] = smooth(load_elem(x, dtype, t * stride + c), NULL, c);"),
+    "block_load_transposed": ("R[k][n] = load_elem(r, r_dtype, k * block + n);",
+                              "R[k][n] = load_elem(r, r_dtype, n * block + k);"),
 }
 
 
