@@ -341,6 +341,9 @@ def main():
                          "with absorbed, quantized weights (8192x14336 by 4096x14336)")
     ap.add_argument("--norm", action="store_true",
                     help="time the norm-fused path instead: RMSNorm + smooth + rotate + MXFP4 on bf16 8192x4096")
+    ap.add_argument("--block", type=int, default=0, choices=[0, 16, 32, 64, 128],
+                    help="time the block-size variant kernel (DuQuant++ page sec. 4.3 ablation) with a seeded "
+                         "random Hadamard block of this size instead of the workload's 32-wide block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -386,13 +389,19 @@ def main():
         else [x_all] + [x_all.clone() for _ in range(n_buf - 1)]
     lam = torch.from_numpy(wl.lam).to(dev) if wl.lam is not None else None
     r = wl.r_hat.to(dev)
+    if args.block:
+        r = workloads.bf16_matrix(workloads.random_hadamard(np.random.default_rng(2005 + args.block),
+                                                            args.block)).to(dev)
     outs = [(torch.empty((call_tokens, C // 2), dtype=torch.uint8, device=dev),
              torch.empty((call_tokens, C // 32), dtype=torch.uint8, device=dev)) for _ in range(n_buf)]
     torch.cuda.synchronize()
 
     def step(i):
         c, s = outs[i % n_buf]
-        mxq.rotate_quant(xs[i % n_buf], r, lam, codes=c, scales=s)
+        if args.block:
+            mxq.rotate_quant_block(xs[i % n_buf], r, lam, codes=c, scales=s)
+        else:
+            mxq.rotate_quant(xs[i % n_buf], r, lam, codes=c, scales=s)
 
     for i in range(args.warmup):
         step(i)
@@ -430,7 +439,7 @@ def main():
 
     achieved = step_bytes / mean_launch_s / 1e9
     value = elems * args.steps / wall / 1e9
-    hbm = read_counters(args.workload)
+    hbm = None if args.block else read_counters(args.workload)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -446,7 +455,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[args.workload], "tokens": call_tokens, "channels": C,
                    "x_dtype": str(wl.x.dtype).replace("torch.", ""), "lambda": wl.lam is not None,
-                   "r_hat": "bf16 32x32", "buffer_sets": n_buf, "parallelism": "single GPU",
+                   "r_hat": (f"seeded random Hadamard {args.block}x{args.block} (block-size variant kernel)"
+                             if args.block else "bf16 32x32"),
+                   "buffer_sets": n_buf, "parallelism": "single GPU",
                    "launch": "hip graph of the K launches" if args.graph else "eager launches"},
         "hbm_gbps": round(value * BYTES_PER_ELEM, 1),
         "pct_hbm_peak": round(100 * value * BYTES_PER_ELEM / HBM_PEAK_GBPS, 2),
@@ -470,7 +481,10 @@ def main():
             lat.append(e0.elapsed_time(e1) * 1e3)
         result["call_latency_us"] = {"p50": round(float(np.percentile(lat, 50)), 2),
                                      "p99": round(float(np.percentile(lat, 99)), 2), "calls": len(lat)}
-    if not args.no_cpu_baseline:
+    if args.block:
+        result["kernel_source_hash"] = kernel_source_hash(("mxfp4_activation_rotation_amd/csrc/mxq_block.hip",
+                                                           "mxfp4_activation_rotation_amd/csrc/mxq_device.h"))
+    if not args.no_cpu_baseline and not args.block:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

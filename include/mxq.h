@@ -121,6 +121,21 @@ mxq_status mxq_quant(const void *x, int32_t x_dtype, int64_t tokens, int64_t cha
 mxq_status mxq_dequant(const uint8_t *codes, const uint8_t *scales, int64_t tokens,
                        int64_t channels, void *y, int32_t y_dtype, void *stream);
 
+/* Rotation by a block of another size, for the block-size ablation of the
+ * DuQuant++ page (sec. 4.3: B = 16, 32, 64, 128 with MXFP4 groups kept 32
+ * wide): every block of B channels of x / lambda is multiplied by the B x B
+ * bf16 matrix r_block (row-major, y_n = sum_k x'_k r_block[k][n]), then
+ * every 32-element group of the result is MXFP4-encoded as in
+ * mxq_rotate_quant.  block must be 16, 32, 64 or 128 and divide channels
+ * (MXQ_ERR_SHAPE otherwise); y_rot may be NULL or fp32 [tokens][channels].
+ * B = 32 gives the same bits as mxq_rotate_quant (same arithmetic, a kernel
+ * not tuned for speed); otherwise the same arithmetic, layout and error
+ * rules: the product runs on the matrix cores with exact bf16 terms of x'. */
+mxq_status mxq_rotate_quant_block(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
+                                  int64_t x_row_stride, const float *lambda, const uint16_t *r_block,
+                                  int32_t block, uint8_t *codes, uint8_t *scales, float *y_rot,
+                                  void *stream);
+
 /* Norm + smooth + rotate + MXFP4-quantize in one pass over x.
  * DuQuant++ page sec. 5.2 item 1: the per-channel 1/lambda folds into the
  * output of the norm in front of the linear layer, and the online steps run

@@ -25,7 +25,7 @@ STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_NULL", 2: "MXQ_ERR_SHAPE", 3: "MXQ_ERR_DTYPE"
 EXPORTS = ("mxq_rotate_quant", "mxq_rotate_quant_ex", "mxq_quant", "mxq_dequant",
            "mxq_status_str", "mxq_plan", "mxq_version", "mxq_calib_workspace_bytes",
            "mxq_calib_worst_group", "mxq_calib_givens", "mxq_absorb_quant", "mxq_gemm_mxfp4",
-           "mxq_norm_rotate_quant")
+           "mxq_norm_rotate_quant", "mxq_rotate_quant_block")
 
 _lib = None
 
@@ -65,11 +65,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.mxq_calib_givens.argtypes = [vp, i64, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.mxq_absorb_quant.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
     lib.mxq_gemm_mxfp4.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp]
+    lib.mxq_rotate_quant_block.argtypes = [vp, i32, i64, i64, i64, vp, vp, i32, vp, vp, vp, vp]
     lib.mxq_norm_rotate_quant.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, ctypes.c_float, vp, vp, vp, vp,
                                           vp, vp]
     for f in ("mxq_rotate_quant", "mxq_rotate_quant_ex", "mxq_quant", "mxq_dequant", "mxq_plan",
               "mxq_version", "mxq_calib_worst_group", "mxq_calib_givens", "mxq_absorb_quant",
-              "mxq_gemm_mxfp4", "mxq_norm_rotate_quant"):
+              "mxq_gemm_mxfp4", "mxq_norm_rotate_quant", "mxq_rotate_quant_block"):
         getattr(lib, f).restype = ctypes.c_int32
     if path is None:
         _lib = lib
@@ -234,6 +235,29 @@ def gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Ten
     if st != 0:
         raise MXQError("mxq_gemm_mxfp4", st)
     return out
+
+
+def rotate_quant_block(x: torch.Tensor, r_block: torch.Tensor, lam: torch.Tensor | None = None, *,
+                       codes=None, scales=None, y_rot=None, stream=None):
+    """MXFP4 of x / lam rotated block by block with a B x B bf16 matrix
+    (B = 16, 32, 64, 128: the block sizes of the DuQuant++ page's ablation)."""
+    lib = load()
+    T, C, stride = _check_x(x, (torch.bfloat16, torch.float16))
+    B = r_block.shape[0]
+    if r_block.dtype != torch.bfloat16 or r_block.dim() != 2 or r_block.shape != (B, B) \
+            or not r_block.is_contiguous() or r_block.device != x.device:
+        raise ValueError("r_block must be a contiguous square bf16 tensor on x's device")
+    if lam is not None and (lam.dtype != torch.float32 or lam.shape != (C,) or not lam.is_contiguous()
+                            or lam.device != x.device):
+        raise ValueError("lam must be a contiguous fp32 [channels] tensor on x's device")
+    codes, scales = _outputs(x, T, C, codes, scales)
+    if y_rot is not None and (y_rot.dtype != torch.float32 or y_rot.shape != (T, C) or not y_rot.is_contiguous()):
+        raise ValueError("y_rot must be a contiguous fp32 [tokens, channels] tensor")
+    st = lib.mxq_rotate_quant_block(_ptr(x), _DT[x.dtype], T, C, stride, _ptr(lam), _ptr(r_block), B,
+                                    _ptr(codes), _ptr(scales), _ptr(y_rot), _stream(x, stream))
+    if st != 0:
+        raise MXQError("mxq_rotate_quant_block", st)
+    return codes, scales
 
 
 NORM_KINDS = {"rms": 0, "layer": 1}

@@ -7,7 +7,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("mxq.hip", "mxq_calib.hip", "mxq_gemm.hip", "mxq_norm.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("mxq.hip", "mxq_calib.hip", "mxq_gemm.hip", "mxq_norm.hip", "mxq_block.hip")]
 LIBRARY = os.path.join(PKG, "libmxq.so")
 ARCH = "gfx950"
 

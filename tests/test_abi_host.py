@@ -209,3 +209,24 @@ def test_norm_rotate_quant_validation(lib):
     assert nq(lib, y=P_ODD) == ALIGN
     assert nq(lib, g=ctypes.c_void_p(0x10002)) == ALIGN
     assert nq(lib, stride=68) == ALIGN
+
+
+def bq(lib, x=P, dt=0, T=8, C=128, stride=128, lam=None, r=P, B=64, codes=P, scales=P, y=None):
+    return lib.mxq_rotate_quant_block(x, dt, T, C, stride, lam, r, B, codes, scales, y, None)
+
+
+def test_rotate_quant_block_validation(lib):
+    assert bq(lib, dt=2) == DTYPE
+    for B in (8, 48, 256, 0, -32):
+        assert bq(lib, B=B) == SHAPE
+    assert bq(lib, C=96, stride=96, B=64) == SHAPE      # channels not a multiple of the block
+    assert bq(lib, C=48, stride=48, B=16) == SHAPE      # nor of the 32-wide group
+    assert bq(lib, T=-1) == SHAPE
+    assert bq(lib, T=0, x=None, r=None, codes=None, scales=None) == OK
+    assert bq(lib, x=None) == NULL
+    assert bq(lib, r=None) == NULL
+    assert bq(lib, codes=None) == NULL
+    assert bq(lib, stride=64) == STRIDE
+    assert bq(lib, x=P_ODD) == ALIGN
+    assert bq(lib, lam=P_ODD) == ALIGN
+    assert bq(lib, y=P_ODD) == ALIGN
