@@ -57,7 +57,7 @@ def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
-    h.update(" ".join(_build.FLAGS).encode())
+    h.update(" ".join(_build.flags_for(sources[0])).encode())
     return h.hexdigest()[:16]
 
 
