@@ -69,7 +69,7 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
-template <int XT, int NORM, int NT>
+template <int XT, int NORM, int NT, bool YOUT>
 __global__ __launch_bounds__(kBlockThreads) void norm_quant_kernel(NormArgs a) {
     constexpr bool kFp16 = XT == MXQ_FP16;
     constexpr int kUnits = NT * kSub * 2 * kWave;  // 16-byte factor units per table
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kBlockThreads) void norm_quant_kernel(NormArgs a) {
                 const uint32_t scale_bits = e8m0_scale_bits(group_amax8(v));
                 sc[s] = scale_bits >> 23;
                 word[s] = encode8(v, as_f32(scale_bits));
-                if (a.y) {
+                if constexpr (YOUT) {
                     const auto yrsrc = row_rsrc(a.y + r * a.gpr * kGroup, gpr * kGroup * 4);
                     const uint32_t off = (static_cast<uint32_t>(kTileGroups * st + 16 * s + j) * kGroup + 8 * q) * 4;
                     __builtin_amdgcn_raw_buffer_store_b128(
@@ -271,12 +271,12 @@ __global__ __launch_bounds__(kBlockThreads) void norm_quant_kernel(NormArgs a) {
 bool aligned_to(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 // Resident blocks per CU the instance allows (registers, LDS), queried once.
-template <int XT, int NORM, int NT>
+template <int XT, int NORM, int NT, bool YOUT>
 int blocks_per_cu() {
     static std::atomic<int> cached{0};
     int v = cached.load(std::memory_order_relaxed);
     if (v > 0) return v;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, norm_quant_kernel<XT, NORM, NT>, kBlockThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, norm_quant_kernel<XT, NORM, NT, YOUT>, kBlockThreads, 0) !=
             hipSuccess ||
         v <= 0)
         v = 1;
@@ -284,24 +284,32 @@ int blocks_per_cu() {
     return v;
 }
 
-template <int XT, int NORM, int NT>
+template <int XT, int NORM, int NT, bool YOUT>
 mxq_status launch_nt(NormArgs a, hipStream_t st) {
-    const int per_cu = blocks_per_cu<XT, NORM, NT>();
+    const int per_cu = blocks_per_cu<XT, NORM, NT, YOUT>();
     const int64_t want = (static_cast<int64_t>(a.tokens) + kBlockWaves - 1) / kBlockWaves;
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
     const int blocks = static_cast<int>(want < cap ? want : cap);
     a.waves = blocks * kBlockWaves;
-    hipLaunchKernelGGL((norm_quant_kernel<XT, NORM, NT>), dim3(blocks), dim3(kBlockThreads), 0, st, a);
+    hipLaunchKernelGGL((norm_quant_kernel<XT, NORM, NT, YOUT>), dim3(blocks), dim3(kBlockThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 
+template <int XT, int NORM, bool YOUT>
+mxq_status launch_tiles(const NormArgs& a, hipStream_t st) {
+    const int tiles = (a.gpr + kTileGroups - 1) / kTileGroups;
+    if (tiles <= 1) return launch_nt<XT, NORM, 1, YOUT>(a, st);
+    if (tiles <= 2) return launch_nt<XT, NORM, 2, YOUT>(a, st);
+    if (tiles <= 4) return launch_nt<XT, NORM, 4, YOUT>(a, st);
+    return launch_nt<XT, NORM, 8, YOUT>(a, st);
+}
+
+// The rotated-value output is a template parameter: a runtime branch around
+// its stores would cut the unrolled sub-tiles into separate basic blocks
+// that the scheduler cannot interleave.
 template <int XT, int NORM>
 mxq_status launch_norm(const NormArgs& a, hipStream_t st) {
-    const int tiles = (a.gpr + kTileGroups - 1) / kTileGroups;
-    if (tiles <= 1) return launch_nt<XT, NORM, 1>(a, st);
-    if (tiles <= 2) return launch_nt<XT, NORM, 2>(a, st);
-    if (tiles <= 4) return launch_nt<XT, NORM, 4>(a, st);
-    return launch_nt<XT, NORM, 8>(a, st);
+    return a.y ? launch_tiles<XT, NORM, true>(a, st) : launch_tiles<XT, NORM, false>(a, st);
 }
 
 }  // namespace norm
