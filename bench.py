@@ -157,7 +157,9 @@ def bench_gemm(args):
     """The consumer: W4A4 MXFP4 product of the quantized down_proj input
     (8192 x 14336, from mxq_rotate_quant on the headline activations) with
     absorbed, quantized synthetic weights (4096 x 14336), bf16 output.  The
-    operands (88 MB) are built once on the GPU before the timed region."""
+    operands (88 MB) are built once on the GPU before the timed region.
+    With --decode, the activations are 16 tokens of the same batch: the
+    product is bound by reading the weights, so its roofline is HBM."""
     import numpy as np
     import torch
 
@@ -171,7 +173,9 @@ def bench_gemm(args):
     lam = torch.from_numpy(wl.lam).to(dev) if wl.lam is not None else None
     ac, asc = mxq.rotate_quant(wl.x.to(dev), r, lam)
     bc, bsc = mxq.absorb_quant(w.to(dev), r, lam)
-    M, K, N = wl.tokens, wl.channels, workloads.DOWN_PROJ_OUT
+    if args.decode:
+        ac, asc = ac[:16].contiguous(), asc[:16].contiguous()
+    M, K, N = ac.shape[0], wl.channels, workloads.DOWN_PROJ_OUT
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     flop = 2.0 * M * N * K
     for _ in range(args.warmup):
@@ -188,7 +192,8 @@ def bench_gemm(args):
     wall = time.perf_counter() - t0
     mean_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
     achieved = flop / mean_launch_s / 1e12
-    hbm = read_counters(0, GEMM_COUNTERS, GEMM_SOURCES)
+    weight_bytes = N * (K // 2 + K // 32)
+    hbm = None if args.decode else read_counters(0, GEMM_COUNTERS, GEMM_SOURCES)
     result = {
         "metric": "W4A4 MXFP4 GEMM throughput (consumer of the quantized activations): TFLOP/s",
         "value": round(flop * args.steps / wall / 1e12, 1),
@@ -209,10 +214,20 @@ def bench_gemm(args):
                      "traffic": None if hbm is None else round(hbm)},
         "kernel_source_hash": kernel_source_hash(GEMM_SOURCES),
     }
+    if args.decode:
+        algo = weight_bytes + M * (K // 2 + K // 32) + M * N * 2
+        gbps = algo / mean_launch_s / 1e9
+        result["metric"] = "decode-shaped W4A4 MXFP4 GEMM: GB/s of weights streamed"
+        result["value"] = round(algo * args.steps / wall / 1e9, 1)
+        result["unit"] = "GB/s"
+        result["config"]["workload"] = ("decode product: 16 tokens of the headline batch, rotated and MXFP4-"
+                                        "quantized, times absorbed MXFP4 weights 4096x14336, bf16 output")
+        result["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                              "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}
     if not args.no_cpu_baseline:
         import oracle
         orc = oracle.default()
-        rows = 64
+        rows = min(64, M)
         a_s, as_s = ac[:rows].cpu().numpy(), asc[:rows].cpu().numpy()
         b_h, bs_h = bc.cpu().numpy(), bsc.cpu().numpy()
         times = []
@@ -230,8 +245,10 @@ def bench_gemm(args):
                        default=1)
         except Exception:  # pragma: no cover
             blas = 1
+        cpu_value = (round((weight_bytes + rows * (K // 2 + K // 32) + rows * N * 2) / med / 1e9, 4)
+                     if args.decode else round(2.0 * rows * N * K / med / 1e12, 5))
         result["cpu_baseline"] = {
-            "value": round(2.0 * rows * N * K / med / 1e12, 5), "unit": "TFLOP/s",
+            "value": cpu_value, "unit": "GB/s" if args.decode else "TFLOP/s",
             "cores": max(blas, orc.num_threads()), "kind": "oracle",
             "sample": f"the first {rows} activation rows against all {N} weight rows (exact dequantization, "
                       f"fp64 matmul), {len(times)} repetitions, median {med:.2f} s each"}
@@ -339,6 +356,8 @@ def main():
     ap.add_argument("--gemm", action="store_true",
                     help="time the consumer instead: the W4A4 MXFP4 product of the headline batch's codes "
                          "with absorbed, quantized weights (8192x14336 by 4096x14336)")
+    ap.add_argument("--decode", action="store_true",
+                    help="with --gemm: 16 activation rows (decode), timed against HBM bandwidth")
     ap.add_argument("--norm", action="store_true",
                     help="time the norm-fused path instead: RMSNorm + smooth + rotate + MXFP4 on bf16 8192x4096")
     ap.add_argument("--block", type=int, default=0, choices=[0, 16, 32, 64, 128],

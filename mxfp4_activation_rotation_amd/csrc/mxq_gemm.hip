@@ -307,6 +307,106 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     }
 }
 
+// Decode-shaped products (M <= 64 activation rows).  The weights dominate
+// the bytes, and a 256 x 256 tile would leave most of the chip idle, so a
+// block owns 16 weight rows (output columns) and its 16 waves split K: wave
+// w walks stages w, w + 16, ... (128 K positions each) with the same
+// 16 x 16 x 128 scaled MFMA, loading its operands straight into registers
+// (lane l: row l % 16, group l / 16 of the stage; the activation rows are
+// re-read from L2 by every block).  The 16 partial tiles are summed through
+// LDS in wave order, so results are deterministic.
+constexpr int kSmallWaves = 16;
+constexpr int kAuxNonTemporal = 2;  // cache policy bits of buffer ops: the weights are read once
+constexpr int kSmallMaxM = 64;
+typedef __attribute__((ext_vector_type(4))) float f32x4s_t;
+
+template <bool OUT_BF16, int FM>
+__global__ __launch_bounds__(kWave * kSmallWaves) void gemm_small_kernel(GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) f32x4s_t red[kSmallWaves][FM][kWave];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+    const uint32_t cpr = static_cast<uint32_t>(g.K) / 2;
+    const uint32_t spr = static_cast<uint32_t>(g.K) / 32;
+    const uint32_t rows_b = static_cast<uint32_t>(min<int64_t>(16, g.N - n0));
+    const auto ra = rsrc(g.a_codes, static_cast<uint32_t>(g.M) * cpr);
+    const auto rsa = rsrc(g.a_scales, static_cast<uint32_t>(g.M) * spr);
+    const auto rb = rsrc(g.b_codes + n0 * cpr, rows_b * cpr);
+    const auto rsb = rsrc(g.b_scales + n0 * spr, rows_b * spr);
+    const uint32_t r16 = static_cast<uint32_t>(lane & 15);
+    const uint32_t q = static_cast<uint32_t>(lane >> 4);
+    f32x4s_t acc[FM];
+#pragma unroll
+    for (int f = 0; f < FM; ++f) acc[f] = f32x4s_t{0.f, 0.f, 0.f, 0.f};
+    const int nk = g.K / 128;
+    // Stages in flight per wave (all loads of a group issue before its
+    // MFMAs): as many as the 128 registers a 1024-thread block leaves each
+    // lane allow (8 for 16 rows, 4 for 32, 2 for 64).
+    constexpr int kDepth = FM >= 4 ? 2 : (FM == 2 ? 4 : 8);
+    for (int s0 = wave; s0 < nk; s0 += kSmallWaves * kDepth) {
+        u32x4g_t av[kDepth][FM], bv[kDepth];
+        uint32_t sav[kDepth][FM], sbv[kDepth];
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            const int st = s0 + d * kSmallWaves;  // uniform across the wave
+            if (st >= nk) break;
+            const uint32_t cb = static_cast<uint32_t>(st) * 64 + 16 * q;
+            const uint32_t sbyte = static_cast<uint32_t>(st) * 4 + q;
+#pragma unroll
+            for (int f = 0; f < FM; ++f) {
+                const uint32_t row = 16 * f + r16;
+                av[d][f] = __builtin_amdgcn_raw_buffer_load_b128(ra, row * cpr + cb, 0, 0);
+                sav[d][f] = __builtin_amdgcn_raw_buffer_load_b8(rsa, row * spr + sbyte, 0, 0);
+            }
+            bv[d] = __builtin_amdgcn_raw_buffer_load_b128(rb, r16 * cpr + cb, 0, kAuxNonTemporal);
+            sbv[d] = __builtin_amdgcn_raw_buffer_load_b8(rsb, r16 * spr + sbyte, 0, kAuxNonTemporal);
+        }
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            if (s0 + d * kSmallWaves >= nk) break;
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+                acc[f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    operand(av[d][f]), operand(bv[d]), acc[f], kFmtE2M1, kFmtE2M1, 0, static_cast<int>(sav[d][f]), 0,
+                    static_cast<int>(sbv[d]));
+        }
+    }
+#pragma unroll
+    for (int f = 0; f < FM; ++f) red[wave][f][lane] = acc[f];
+    __syncthreads();
+    // Thread t sums element t of the FM x 256 partial tiles over the waves
+    // (fixed order) and stores it: lane l, register r of fragment f is row
+    // 16 f + 4 (l / 16) + r, column l % 16.
+    for (int t = threadIdx.x; t < FM * kWave * 4; t += kWave * kSmallWaves) {
+        const int f = t / (kWave * 4);
+        const int l = (t / 4) % kWave;
+        const int r = t % 4;
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kSmallWaves; ++w) sum += red[w][f][l][r];
+        const int64_t row = 16 * f + 4 * (l >> 4) + r;
+        const int64_t col = n0 + (l & 15);
+        if (row < g.M && col < g.N) {
+            if constexpr (OUT_BF16)
+                static_cast<__bf16*>(g.y)[row * g.ldy + col] = static_cast<__bf16>(sum);
+            else
+                static_cast<float*>(g.y)[row * g.ldy + col] = sum;
+        }
+    }
+}
+
+template <bool OUT_BF16>
+void launch_small(const GemmArgs& g, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>((g.N + 15) / 16));
+    const dim3 block(kWave * kSmallWaves);
+    if (g.M <= 16)
+        hipLaunchKernelGGL((gemm_small_kernel<OUT_BF16, 1>), grid, block, 0, st, g);
+    else if (g.M <= 32)
+        hipLaunchKernelGGL((gemm_small_kernel<OUT_BF16, 2>), grid, block, 0, st, g);
+    else
+        hipLaunchKernelGGL((gemm_small_kernel<OUT_BF16, 4>), grid, block, 0, st, g);
+}
+
 bool aligned_to(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 }  // namespace
@@ -337,6 +437,13 @@ mxq_status mxq_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const
     GemmArgs g{a_codes, a_scales, b_codes, b_scales, y, ldy, static_cast<int32_t>(M), static_cast<int32_t>(N),
                static_cast<int32_t>(K), static_cast<int32_t>(tiles_m), static_cast<int32_t>(tiles_n)};
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (M <= kSmallMaxM) {
+        if (y_dtype == MXQ_BF16)
+            launch_small<true>(g, st);
+        else
+            launch_small<false>(g, st);
+        return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+    }
     const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n));
     if (y_dtype == MXQ_BF16)
         hipLaunchKernelGGL((gemm_kernel<true>), grid, dim3(kThreads), 0, st, g);

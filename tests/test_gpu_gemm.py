@@ -67,6 +67,24 @@ def test_gemm_random_operands(dev, orc, M, N, K):
     assert torch.equal(yb.view(torch.int16), torch.from_numpy(y).to(torch.bfloat16).view(torch.int16))
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 14336), (7, 100, 128), (16, 4096, 4096), (17, 300, 1152),
+                                   (40, 64, 2048), (64, 1000, 14336), (16, 16, 256)])
+def test_gemm_decode_shapes(dev, orc, M, N, K):
+    """Decode-shaped products (the path for M <= 64 splits K over the waves
+    of a block and sums the partial tiles in a fixed order)."""
+    rng = np.random.default_rng(M * 131 + N * 17 + K + 5)
+    ac, asc = W.random_mxfp4(rng, M, K)
+    bc, bsc = W.random_mxfp4(rng, N, K)
+    ref, s_abs = O.gemm_mxfp4(ac, asc, bc, bsc, orc)
+    y = gemm_gpu(ac, asc, bc, bsc, dev).cpu().numpy()
+    worst = check_product(y, ref, s_abs, K, f"{M}x{N}x{K}")
+    print(f"  decode gemm M={M} N={N} K={K}: worst |err| / sum|products| = {worst:.3g}", flush=True)
+    yb = gemm_gpu(ac, asc, bc, bsc, dev, torch.bfloat16).cpu()
+    assert torch.equal(yb.view(torch.int16), torch.from_numpy(y).to(torch.bfloat16).view(torch.int16))
+    y2 = gemm_gpu(ac, asc, bc, bsc, dev).cpu().numpy()
+    assert np.array_equal(y, y2)  # fixed reduction order
+
+
 def test_gemm_one_hot_products(dev, orc):
     """Each output picks exactly one product: codes one-hot along K with the
     extreme magnitudes and a wide spread of scales (exact results)."""
