@@ -159,7 +159,10 @@ def bench_gemm(args):
     absorbed, quantized synthetic weights (4096 x 14336), bf16 output.  The
     operands (88 MB) are built once on the GPU before the timed region.
     With --decode, the activations are 16 tokens of the same batch: the
-    product is bound by reading the weights, so its roofline is HBM."""
+    product is bound by reading the weights, so its roofline is HBM.  Both
+    operands are then in the fragment-tiled layout (the activations written
+    so by the quantizer, the weights repacked once offline); --row-layout
+    times the row-layout operands instead."""
     import numpy as np
     import torch
 
@@ -173,26 +176,45 @@ def bench_gemm(args):
     lam = torch.from_numpy(wl.lam).to(dev) if wl.lam is not None else None
     ac, asc = mxq.rotate_quant(wl.x.to(dev), r, lam)
     bc, bsc = mxq.absorb_quant(w.to(dev), r, lam)
-    if args.decode:
-        ac, asc = ac[:16].contiguous(), asc[:16].contiguous()
     M, K, N = ac.shape[0], wl.channels, workloads.DOWN_PROJ_OUT
+    weight_bytes = N * (K // 2 + K // 32)
+    weights = [(bc, bsc)]
+    tiled = args.decode and not args.row_layout
+    if args.decode:
+        # A decode step reads every layer's weights once: rotate through
+        # enough weight copies (> 768 MB) that none is still cached from its
+        # previous use, so the weights stream from HBM as they would there.
+        M = 16
+        ac, asc = ac[:M].contiguous(), asc[:M].contiguous()
+        if tiled:
+            ta, tsa = mxq.rotate_quant_tiled(wl.x[:M].contiguous().to(dev), r, lam)
+            weights = [mxq.tile_mxfp4(bc, bsc)]
+        weights += [(weights[0][0].clone(), weights[0][1].clone())
+                    for _ in range(int(np.ceil(768e6 / weight_bytes)))]
+    n_w = len(weights)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     flop = 2.0 * M * N * K
-    for _ in range(args.warmup):
-        mxq.gemm_mxfp4(ac, asc, bc, bsc, out=y)
+
+    def product(i):
+        if tiled:
+            mxq.gemm_mxfp4_tiled(ta, tsa, *weights[i % n_w], M, N, K, out=y)
+        else:
+            mxq.gemm_mxfp4(ac, asc, *weights[i % n_w], out=y)
+
+    for i in range(args.warmup):
+        product(i)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
-    for _ in range(args.steps):
-        mxq.gemm_mxfp4(ac, asc, bc, bsc, out=y)
+    for i in range(args.steps):
+        product(args.warmup + i)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     mean_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
     achieved = flop / mean_launch_s / 1e12
-    weight_bytes = N * (K // 2 + K // 32)
     hbm = None if args.decode else read_counters(0, GEMM_COUNTERS, GEMM_SOURCES)
     result = {
         "metric": "W4A4 MXFP4 GEMM throughput (consumer of the quantized activations): TFLOP/s",
@@ -222,6 +244,9 @@ def bench_gemm(args):
         result["unit"] = "GB/s"
         result["config"]["workload"] = ("decode product: 16 tokens of the headline batch, rotated and MXFP4-"
                                         "quantized, times absorbed MXFP4 weights 4096x14336, bf16 output")
+        result["config"]["weight_sets"] = n_w
+        result["config"]["operands"] += (", fragment-tiled records (16 rows x 128 positions)" if tiled
+                                         else ", row layout")
         result["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                               "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}
     if not args.no_cpu_baseline:
@@ -358,6 +383,8 @@ def main():
                          "with absorbed, quantized weights (8192x14336 by 4096x14336)")
     ap.add_argument("--decode", action="store_true",
                     help="with --gemm: 16 activation rows (decode), timed against HBM bandwidth")
+    ap.add_argument("--row-layout", action="store_true",
+                    help="with --gemm --decode: row-layout operands instead of fragment-tiled ones")
     ap.add_argument("--norm", action="store_true",
                     help="time the norm-fused path instead: RMSNorm + smooth + rotate + MXFP4 on bf16 8192x4096")
     ap.add_argument("--block", type=int, default=0, choices=[0, 16, 32, 64, 128],

@@ -205,6 +205,52 @@ mxq_status mxq_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales, const
                           const uint8_t *b_scales, int64_t M, int64_t N, int64_t K, void *y,
                           int32_t y_dtype, int64_t ldy, void *stream);
 
+/* ---- fragment-tiled MXFP4 operands -----------------------------------------
+ * A storage order of MXFP4 operands for the product above.  The DuQuant++
+ * page fixes no memory layout: sec. 5.4 items 2-3 leave the weight format to
+ * the target hardware and put the fused transform directly in front of the
+ * MXFP4 linear layer, and sec. 5.2 item 1 asks for no extra pass over
+ * intermediate tensors; here the quantizer can write the order in which the
+ * matrix cores read, so no repacking pass sits between them.  An operand of R rows and K positions
+ * (K % 128 == 0) is cut into records of 16 rows x 128 positions; record
+ * (t, s) -- rows 16t..16t+15, positions 128s..128s+127 -- has index
+ * t * (K/128) + s.  Its 64 slots follow the operand order of the
+ * 16 x 16 x 128 scaled MFMA: slot l is row 16t + l % 16, group 4s + l / 16
+ * (32 positions).  Codes: 1024-byte records, slot l's 16 code bytes (same
+ * byte order as the row layout) at byte 16 l.  Scales: 64-byte records,
+ * slot l's scale byte at byte l.  Buffers hold ceil(R/16) * (K/128)
+ * records, i.e. ceil(R/16) * 16 * K/2 code bytes and ceil(R/16) * 16 * K/32
+ * scale bytes.  Rows R..16*ceil(R/16)-1 are padding.
+ *
+ * mxq_tile_mxfp4: row layout (codes [rows][K/2], scales [rows][K/32]) to
+ *   the tiled layout, padding rows written as zero bytes.  Meant for the
+ *   weights, once, offline.  Requirements: K % 128 == 0, K <= 2^24,
+ *   rows < 2^31 (MXQ_ERR_SHAPE); codes and tiled_codes 16-byte aligned
+ *   (MXQ_ERR_ALIGN); rows == 0 or K == 0 is an empty call.  The output must
+ *   not overlap the input.
+ *
+ * mxq_rotate_quant_tiled: mxq_rotate_quant with its codes and scales written
+ *   in the tiled layout (bit-identical bytes, other positions); channels must
+ *   be a multiple of 128 (MXQ_ERR_SHAPE).  The padding rows of the last
+ *   record row are not written.  Other rules as mxq_rotate_quant.
+ *
+ * mxq_gemm_mxfp4_tiled: mxq_gemm_mxfp4 with both operands tiled (A from
+ *   mxq_rotate_quant_tiled or mxq_tile_mxfp4, B from mxq_tile_mxfp4 of
+ *   mxq_absorb_quant's output).  Outputs are bit-identical to those of
+ *   mxq_gemm_mxfp4 on the same operands in the row layout; the contents of
+ *   padding rows affect only outputs that are not written.  Same
+ *   requirements, with a_tscales and b_tscales 4-byte aligned. */
+mxq_status mxq_tile_mxfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K,
+                          uint8_t *tiled_codes, uint8_t *tiled_scales, void *stream);
+
+mxq_status mxq_rotate_quant_tiled(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
+                                  int64_t x_row_stride, const float *lambda, const uint16_t *r_hat,
+                                  uint8_t *tiled_codes, uint8_t *tiled_scales, void *stream);
+
+mxq_status mxq_gemm_mxfp4_tiled(const uint8_t *a_tcodes, const uint8_t *a_tscales, const uint8_t *b_tcodes,
+                                const uint8_t *b_tscales, int64_t M, int64_t N, int64_t K, void *y,
+                                int32_t y_dtype, int64_t ldy, void *stream);
+
 /* ---- offline calibration of the shared block (DuQuant++ page sec. 3.2) ----
  * Greedy outlier-aware construction of the 32x32 block R_b, in fp64 as the
  * page advises (sec. 3 pitfalls, item 3), on the GPU.  Two calls:

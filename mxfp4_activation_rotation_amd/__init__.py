@@ -25,7 +25,8 @@ STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_NULL", 2: "MXQ_ERR_SHAPE", 3: "MXQ_ERR_DTYPE"
 EXPORTS = ("mxq_rotate_quant", "mxq_rotate_quant_ex", "mxq_quant", "mxq_dequant",
            "mxq_status_str", "mxq_plan", "mxq_version", "mxq_calib_workspace_bytes",
            "mxq_calib_worst_group", "mxq_calib_givens", "mxq_absorb_quant", "mxq_gemm_mxfp4",
-           "mxq_norm_rotate_quant", "mxq_rotate_quant_block")
+           "mxq_norm_rotate_quant", "mxq_rotate_quant_block", "mxq_tile_mxfp4", "mxq_rotate_quant_tiled",
+           "mxq_gemm_mxfp4_tiled")
 
 _lib = None
 
@@ -65,12 +66,16 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.mxq_calib_givens.argtypes = [vp, i64, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.mxq_absorb_quant.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
     lib.mxq_gemm_mxfp4.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp]
+    lib.mxq_gemm_mxfp4_tiled.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp]
+    lib.mxq_tile_mxfp4.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+    lib.mxq_rotate_quant_tiled.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
     lib.mxq_rotate_quant_block.argtypes = [vp, i32, i64, i64, i64, vp, vp, i32, vp, vp, vp, vp]
     lib.mxq_norm_rotate_quant.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, ctypes.c_float, vp, vp, vp, vp,
                                           vp, vp]
     for f in ("mxq_rotate_quant", "mxq_rotate_quant_ex", "mxq_quant", "mxq_dequant", "mxq_plan",
               "mxq_version", "mxq_calib_worst_group", "mxq_calib_givens", "mxq_absorb_quant",
-              "mxq_gemm_mxfp4", "mxq_norm_rotate_quant", "mxq_rotate_quant_block"):
+              "mxq_gemm_mxfp4", "mxq_norm_rotate_quant", "mxq_rotate_quant_block", "mxq_tile_mxfp4",
+              "mxq_rotate_quant_tiled", "mxq_gemm_mxfp4_tiled"):
         getattr(lib, f).restype = ctypes.c_int32
     if path is None:
         _lib = lib
@@ -358,3 +363,87 @@ def calib_givens(x_worst: torch.Tensor, max_steps: int = 128, *, stream=None):
     if st != 0:
         raise MXQError("mxq_calib_givens", st)
     return r, hist, done, pairs
+
+
+# ---- fragment-tiled operands (records of 16 rows x 128 positions in the
+# operand order of the 16 x 16 x 128 scaled MFMA; layout in include/mxq.h) --
+
+def tiled_sizes(rows: int, K: int):
+    """Bytes of the tiled code and scale buffers of a rows x K operand."""
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    padded = (rows + 15) // 16 * 16
+    return padded * K // 2, padded * K // 32
+
+
+def _tiled_outputs(device, rows, K, tcodes, tscales):
+    nc, ns = tiled_sizes(rows, K)
+    if tcodes is None:
+        tcodes = torch.empty((nc,), dtype=torch.uint8, device=device)
+    if tscales is None:
+        tscales = torch.empty((ns,), dtype=torch.uint8, device=device)
+    for name, t, n in (("tcodes", tcodes, nc), ("tscales", tscales, ns)):
+        if t.dtype != torch.uint8 or t.numel() != n or not t.is_contiguous() or t.device != device:
+            raise ValueError(f"{name} must be a contiguous uint8 tensor of {n} bytes on {device}")
+    return tcodes, tscales
+
+
+def tile_mxfp4(codes: torch.Tensor, scales: torch.Tensor, *, tcodes=None, tscales=None, stream=None):
+    """Row-layout MXFP4 (codes [rows, K/2], scales [rows, K/32]) to the
+    fragment-tiled layout (flat uint8 tensors; padding rows zero)."""
+    lib = load()
+    if codes.dtype != torch.uint8 or codes.dim() != 2 or not codes.is_contiguous() or not codes.is_cuda:
+        raise ValueError("codes must be a contiguous uint8 2-D device tensor")
+    R, K = codes.shape[0], codes.shape[1] * 2
+    if scales.dtype != torch.uint8 or tuple(scales.shape) != (R, K // 32) or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous uint8 [rows, K/32] tensor")
+    tcodes, tscales = _tiled_outputs(codes.device, R, K, tcodes, tscales)
+    st = lib.mxq_tile_mxfp4(_ptr(codes), _ptr(scales), R, K, _ptr(tcodes), _ptr(tscales), _stream(codes, stream))
+    if st != 0:
+        raise MXQError("mxq_tile_mxfp4", st)
+    return tcodes, tscales
+
+
+def rotate_quant_tiled(x: torch.Tensor, r_hat: torch.Tensor, lam: torch.Tensor | None = None, *,
+                       tcodes=None, tscales=None, stream=None):
+    """:func:`rotate_quant` with its output in the fragment-tiled layout
+    (channels % 128 == 0); the A operand of :func:`gemm_mxfp4_tiled`."""
+    lib = load()
+    T, C, stride = _check_x(x, (torch.bfloat16, torch.float16))
+    if r_hat.dtype != torch.bfloat16 or r_hat.shape != (32, 32) or not r_hat.is_contiguous() \
+            or r_hat.device != x.device:
+        raise ValueError("r_hat must be a contiguous bf16 [32, 32] tensor on x's device")
+    if lam is not None and (lam.dtype != torch.float32 or lam.shape != (C,) or not lam.is_contiguous()
+                            or lam.device != x.device):
+        raise ValueError("lam must be a contiguous fp32 [channels] tensor on x's device")
+    tcodes, tscales = _tiled_outputs(x.device, T, C, tcodes, tscales)
+    st = lib.mxq_rotate_quant_tiled(_ptr(x), _DT[x.dtype], T, C, stride, _ptr(lam), _ptr(r_hat),
+                                    _ptr(tcodes), _ptr(tscales), _stream(x, stream))
+    if st != 0:
+        raise MXQError("mxq_rotate_quant_tiled", st)
+    return tcodes, tscales
+
+
+def gemm_mxfp4_tiled(a_tcodes: torch.Tensor, a_tscales: torch.Tensor, b_tcodes: torch.Tensor,
+                     b_tscales: torch.Tensor, M: int, N: int, K: int, out_dtype=torch.float32, *,
+                     out=None, stream=None):
+    """:func:`gemm_mxfp4` on fragment-tiled operands (A: M x K, B: N x K);
+    bit-identical results."""
+    lib = load()
+    for name, rows, codes, scales in (("a", M, a_tcodes, a_tscales), ("b", N, b_tcodes, b_tscales)):
+        nc, ns = tiled_sizes(rows, K)
+        for t, n in ((codes, nc), (scales, ns)):
+            if t.dtype != torch.uint8 or t.numel() != n or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError(f"{name} operand: tiled buffers must be contiguous uint8 device tensors "
+                                 f"of {nc} and {ns} bytes")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_tcodes.device)
+    if out.dtype not in (torch.bfloat16, torch.float32) or tuple(out.shape) != (M, N) or \
+            (M > 0 and N > 0 and out.stride(1) != 1):
+        raise ValueError("out must be a bf16/fp32 [M, N] tensor with unit column stride")
+    ldy = out.stride(0) if M > 1 else N
+    st = lib.mxq_gemm_mxfp4_tiled(_ptr(a_tcodes), _ptr(a_tscales), _ptr(b_tcodes), _ptr(b_tscales), M, N, K,
+                                  _ptr(out), _DT[out.dtype], ldy, _stream(a_tcodes, stream))
+    if st != 0:
+        raise MXQError("mxq_gemm_mxfp4_tiled", st)
+    return out

@@ -122,7 +122,7 @@ struct Args {
     int32_t waves;    // tcols * row_step
 };
 
-template <int XT, int MODE, int LAM, bool YOUT>
+template <int XT, int MODE, int LAM, bool YOUT, bool TILED = false>
 __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
     constexpr int kN = (XT == kFP32) ? 2 : 1;  // 16-byte loads per lane per sub-tile
     constexpr uint32_t esz = (XT == kFP32) ? 4 : 2;
@@ -275,12 +275,29 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
             transpose_words(word);
             // the scale of group 16 q + j is the one computed in sub-tile q
             const uint32_t S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
-            const auto crsrc = row_rsrc(a.codes + rr * a.gpr * 16, gpr * 16);
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{word[0], word[1], word[2], word[3]}, crsrc, code_off, 0,
-                                                   MXQ_NT_STORE ? kAuxNT : 0);
-            const auto srsrc = row_rsrc(a.scales + rr * a.gpr, gpr);
-            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, scale_off, 0,
-                                                 MXQ_NT_SCALE ? kAuxNT : 0);
+            if constexpr (TILED) {
+                // Fragment-tiled output: group g of row rr is slot
+                // 16 (g % 4) + rr % 16 of record (rr / 16, g / 4); a record
+                // row holds gpr / 4 records (1 KB of codes, 64 scale bytes
+                // each).  Groups past the row end land past the record row's
+                // range and are dropped.
+                const uint32_t nrec = gpr / 4;
+                const int64_t rrow = rr >> 4;
+                const uint32_t grp = static_cast<uint32_t>(p0 + lane);
+                const uint32_t slot = (grp >> 2) * 64 + (grp & 3) * 16 + static_cast<uint32_t>(rr & 15);
+                const auto crsrc = row_rsrc(a.codes + rrow * nrec * 1024, nrec * 1024);
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{word[0], word[1], word[2], word[3]}, crsrc,
+                                                       slot * 16, 0, 0);
+                const auto srsrc = row_rsrc(a.scales + rrow * nrec * 64, nrec * 64);
+                __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, slot, 0, 0);
+            } else {
+                const auto crsrc = row_rsrc(a.codes + rr * a.gpr * 16, gpr * 16);
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{word[0], word[1], word[2], word[3]}, crsrc,
+                                                       code_off, 0, MXQ_NT_STORE ? kAuxNT : 0);
+                const auto srsrc = row_rsrc(a.scales + rr * a.gpr, gpr);
+                __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, scale_off, 0,
+                                                     MXQ_NT_SCALE ? kAuxNT : 0);
+            }
         }
     };
 
@@ -433,14 +450,14 @@ static bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintp
 static size_t dtype_size(int32_t dt) { return dt == MXQ_FP32 ? 4 : 2; }
 
 // Resident waves per CU the kernel instance allows (registers), queried once.
-template <int XT, int MODE, int LAM, bool YOUT>
+template <int XT, int MODE, int LAM, bool YOUT, bool TILED>
 static int occupancy_waves_per_cu() {
     static std::atomic<int> cached{0};
     int v = cached.load(std::memory_order_relaxed);
     if (v > 0) return v;
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, quant_kernel<XT, MODE, LAM, YOUT>, kBlockThreads, 0) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, quant_kernel<XT, MODE, LAM, YOUT, TILED>,
+                                                     kBlockThreads, 0) != hipSuccess ||
         blocks <= 0)
         blocks = 1;
     v = blocks * kWavesPerBlock;
@@ -448,21 +465,25 @@ static int occupancy_waves_per_cu() {
     return v;
 }
 
-template <int XT, int MODE, int LAM, bool YOUT>
+template <int XT, int MODE, int LAM, bool YOUT, bool TILED = false>
 static mxq_status launch(Args a, int64_t tokens, int64_t channels, hipStream_t st) {
-    const int occ = occupancy_waves_per_cu<XT, MODE, LAM, YOUT>();
+    const int occ = occupancy_waves_per_cu<XT, MODE, LAM, YOUT, TILED>();
     Plan pl;
     constexpr int want = kWavesPerCuOf<XT, MODE, LAM>;
     if (!make_plan(tokens, channels, device_cu_count(), occ < want ? occ : want, &pl)) return MXQ_ERR_SHAPE;
     a.tcols = pl.tcols;
     a.row_step = pl.row_step;
     a.waves = pl.waves;
-    hipLaunchKernelGGL((quant_kernel<XT, MODE, LAM, YOUT>), dim3(pl.blocks), dim3(kBlockThreads), 0, st, a);
+    hipLaunchKernelGGL((quant_kernel<XT, MODE, LAM, YOUT, TILED>), dim3(pl.blocks), dim3(kBlockThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 
 template <int XT>
-static mxq_status dispatch_rotate(const Args& a, int64_t tokens, int64_t channels, hipStream_t st) {
+static mxq_status dispatch_rotate(const Args& a, int64_t tokens, int64_t channels, hipStream_t st, bool tiled) {
+    if (tiled) {
+        return a.lambda ? launch<XT, kRotate, kLamDiv, false, true>(a, tokens, channels, st)
+                        : launch<XT, kRotate, kLamNone, false, true>(a, tokens, channels, st);
+    }
     if (a.lambda) {
         return a.y ? launch<XT, kRotate, kLamDiv, true>(a, tokens, channels, st)
                    : launch<XT, kRotate, kLamDiv, false>(a, tokens, channels, st);
@@ -482,9 +503,10 @@ static mxq_status check_common(const void* x, int32_t x_dtype, int64_t tokens, i
 
 static mxq_status rotate_impl(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels,
                               int64_t stride, const float* lambda, const uint16_t* r_hat, uint8_t* codes,
-                              uint8_t* scales, float* y, void* stream) {
+                              uint8_t* scales, float* y, void* stream, bool tiled = false) {
     mxq_status s = check_common(x, x_dtype, tokens, channels, stride, false);
     if (s != MXQ_OK) return s;
+    if (tiled && channels % 128) return MXQ_ERR_SHAPE;
     if (tokens == 0 || channels == 0) return MXQ_OK;
     if (!x || !r_hat || !codes || !scales) return MXQ_ERR_NULL;
     if (stride < channels) return MXQ_ERR_STRIDE;
@@ -495,8 +517,8 @@ static mxq_status rotate_impl(const void* x, int32_t x_dtype, int64_t tokens, in
     Args a{x, stride, lambda, r_hat, codes, scales, y, static_cast<int32_t>(tokens),
            static_cast<int32_t>(channels / kGroup), 0, 0, 0};
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return x_dtype == MXQ_BF16 ? dispatch_rotate<kBF16>(a, tokens, channels, st)
-                               : dispatch_rotate<kFP16>(a, tokens, channels, st);
+    return x_dtype == MXQ_BF16 ? dispatch_rotate<kBF16>(a, tokens, channels, st, tiled)
+                               : dispatch_rotate<kFP16>(a, tokens, channels, st, tiled);
 }
 
 static mxq_status absorb_impl(const void* w, int32_t w_dtype, int64_t rows, int64_t cols, int64_t stride,
@@ -532,6 +554,13 @@ mxq_status mxq_rotate_quant(const void* x, int32_t x_dtype, int64_t tokens, int6
                             uint8_t* codes, uint8_t* scales, void* stream) {
     return rotate_impl(x, x_dtype, tokens, channels, x_row_stride, lambda, r_hat, codes, scales, nullptr,
                        stream);
+}
+
+mxq_status mxq_rotate_quant_tiled(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels,
+                                  int64_t x_row_stride, const float* lambda, const uint16_t* r_hat,
+                                  uint8_t* tiled_codes, uint8_t* tiled_scales, void* stream) {
+    return rotate_impl(x, x_dtype, tokens, channels, x_row_stride, lambda, r_hat, tiled_codes, tiled_scales,
+                       nullptr, stream, true);
 }
 
 mxq_status mxq_rotate_quant_ex(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels,

@@ -135,7 +135,7 @@ __device__ __forceinline__ void wait_stage_loads(int later) {
     }
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool TILED>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) Stage st[kNst];
     __shared__ __attribute__((aligned(16))) ScaleChunk sc[kChunks];
@@ -165,12 +165,24 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     const int64_t n0 = static_cast<int64_t>(tn) * kBN;
     const uint32_t cpr = static_cast<uint32_t>(g.K) / 2;   // code bytes per row
     const uint32_t spr = static_cast<uint32_t>(g.K) / 32;  // scale bytes per row
-    const uint32_t rows_a = static_cast<uint32_t>(min<int64_t>(kBM, g.M - m0));
-    const uint32_t rows_b = static_cast<uint32_t>(min<int64_t>(kBN, g.N - n0));
-    const auto ra = rsrc(g.a_codes + m0 * cpr, rows_a * cpr);
-    const auto rb = rsrc(g.b_codes + n0 * cpr, rows_b * cpr);
-    const auto rsa = rsrc(g.a_scales + m0 * spr, rows_a * spr);
-    const auto rsb = rsrc(g.b_scales + n0 * spr, rows_b * spr);
+    const uint32_t nk32 = static_cast<uint32_t>(g.K) / kStageK;  // stages = records per record row
+    __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
+    if constexpr (TILED) {
+        // the tile's 16 record rows (fewer at the bottom/right edge)
+        const uint32_t recs_a = static_cast<uint32_t>(min<int64_t>(kBM / 16, (g.M + 15) / 16 - m0 / 16));
+        const uint32_t recs_b = static_cast<uint32_t>(min<int64_t>(kBN / 16, (g.N + 15) / 16 - n0 / 16));
+        ra = rsrc(g.a_codes + (m0 / 16) * nk32 * 1024, recs_a * nk32 * 1024);
+        rb = rsrc(g.b_codes + (n0 / 16) * nk32 * 1024, recs_b * nk32 * 1024);
+        rsa = rsrc(g.a_scales + (m0 / 16) * nk32 * 64, recs_a * nk32 * 64);
+        rsb = rsrc(g.b_scales + (n0 / 16) * nk32 * 64, recs_b * nk32 * 64);
+    } else {
+        const uint32_t rows_a = static_cast<uint32_t>(min<int64_t>(kBM, g.M - m0));
+        const uint32_t rows_b = static_cast<uint32_t>(min<int64_t>(kBN, g.N - n0));
+        ra = rsrc(g.a_codes + m0 * cpr, rows_a * cpr);
+        rb = rsrc(g.b_codes + n0 * cpr, rows_b * cpr);
+        rsa = rsrc(g.a_scales + m0 * spr, rows_a * spr);
+        rsb = rsrc(g.b_scales + n0 * spr, rows_b * spr);
+    }
 
     // Code staging (direct global -> LDS loads, no registers): wave w fills
     // slots w and w + 8 of each operand tile, slot f holding the 16 x 64
@@ -183,9 +195,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     // for the address unit), and the MFMA lane L, which needs row L % 16 and
     // group L / 16, reads position p(L % 16, L / 16): every 16 lanes of a
     // ds_read_b128 cover the 64 LDS banks once.
+    // Fragment-tiled operands are stored in the MFMA lane order already:
+    // slot f of stage kt is the contiguous 1 KB record (f, kt), lane l loads
+    // its bytes 16 l .. 16 l + 15 and the MFMA lane L reads position L.
     const uint32_t ld_r = static_cast<uint32_t>(lane >> 2);
     const uint32_t ld_c = static_cast<uint32_t>((lane - (lane >> 4)) & 3);
-    const uint32_t goff = (static_cast<uint32_t>(16 * wave) + ld_r) * cpr + 16 * ld_c;
+    const uint32_t goff = TILED ? 16 * static_cast<uint32_t>(lane) + static_cast<uint32_t>(wave) * nk32 * 1024
+                                : (static_cast<uint32_t>(16 * wave) + ld_r) * cpr + 16 * ld_c;
     // Scale staging: chunk j holds the 16 scale bytes of stages 4 j .. 4 j + 3
     // for every row ([row][16] per operand, a ring of three chunks in LDS).
     // The loads of stage s carry a quarter of chunk s / 4 + 1: waves 0-3
@@ -193,15 +209,21 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     // rows of B, 4 lanes per row (one 16-byte row slice per quad).  Since
     // stage s is loaded while stage s - 3 computes, the ring slot of chunk
     // s / 4 + 1 last held chunk s / 4 - 2, whose final stage precedes s - 4.
+    // Tiled scales: the chunk of record row f is the 4 consecutive 64-byte
+    // scale records (f, 4 j .. 4 j + 3), 256 contiguous bytes, stored as
+    // [stage][lane] (the row layout stores [row][stage][group]); either way
+    // the chunk of fragment f occupies bytes 256 f .. 256 f + 255.
     const bool scale_of_b = wave >= kWavesM * kWavesN / 2;
     const auto rs = scale_of_b ? rsb : rsa;
     const uint32_t s_row = static_cast<uint32_t>(16 * (wave & 3)) + static_cast<uint32_t>(lane >> 2);
-    const uint32_t s_goff = s_row * spr + 4 * static_cast<uint32_t>(lane & 3);
+    const uint32_t s_goff = TILED ? 4 * static_cast<uint32_t>(lane) + static_cast<uint32_t>(wave & 3) * nk32 * 64
+                                  : s_row * spr + 4 * static_cast<uint32_t>(lane & 3);
     typedef __attribute__((address_space(3))) void* lds_ptr;
     auto load_scale_quarter = [&](int chunk, int q) {
         uint8_t* dst = (scale_of_b ? sc[chunk % kChunks].b : sc[chunk % kChunks].a) + (64 * q + 16 * (wave & 3)) * kChunkRowBytes;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)dst, 4, s_goff,
-                                                 kChunkRowBytes * chunk + 64 * q * static_cast<int>(spr), 0, 0);
+        const int so = TILED ? (4 * q * static_cast<int>(nk32) + kChunkStages * chunk) * 64
+                             : kChunkRowBytes * chunk + 64 * q * static_cast<int>(spr);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)dst, 4, s_goff, so, 0, 0);
     };
     // Loads of stage kt: its codes, plus one quarter of scale chunk kt / 4 + 1.
     auto load = [&](int kt, int buf) {
@@ -210,7 +232,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
         for (int u = 0; u < kLoadsPerThread; ++u) {
             // the slot's rows advance by 128 per u: the step goes into the
             // scalar offset
-            const int so = kRowBytes * kt + u * 128 * static_cast<int>(cpr);
+            const int so = TILED ? 1024 * kt + u * 8 * static_cast<int>(nk32) * 1024
+                                 : kRowBytes * kt + u * 128 * static_cast<int>(cpr);
             const int slot = wave + (kThreads / kWave) * u;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(S.a + slot * 1024), 16, goff, so, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(S.b + slot * 1024), 16, goff, so, 0, 0);
@@ -226,12 +249,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 
     // Operand position of lane l in a slot (see the staging map) and its
     // scale byte in a chunk row: group l / 16 of the stage.
-    const uint32_t op_off = 16 * static_cast<uint32_t>(4 * (lane & 15) + (((lane >> 4) + ((lane & 15) >> 2)) & 3));
-    const uint32_t sl = static_cast<uint32_t>((lane & 15) * kChunkRowBytes + (lane >> 4));
+    const uint32_t op_off = TILED ? 16 * static_cast<uint32_t>(lane)
+                                  : 16 * static_cast<uint32_t>(4 * (lane & 15) + (((lane >> 4) + ((lane & 15) >> 2)) & 3));
+    const uint32_t sl = TILED ? static_cast<uint32_t>(lane)
+                              : static_cast<uint32_t>((lane & 15) * kChunkRowBytes + (lane >> 4));
     auto compute = [&](int kt) {
         const Stage& S = st[kt % kNst];
         const ScaleChunk& C = sc[(kt / kChunkStages) % kChunks];
-        const uint32_t sq = 4 * static_cast<uint32_t>(kt % kChunkStages);
+        const uint32_t sq = (TILED ? 64 : 4) * static_cast<uint32_t>(kt % kChunkStages);
         // Every operand of the stage is read before the first MFMA issues
         // (the scheduling barrier keeps the compiler from sinking the reads
         // next to their uses): one LDS round trip per stage.
@@ -315,12 +340,20 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 // (lane l: row l % 16, group l / 16 of the stage; the activation rows are
 // re-read from L2 by every block).  The 16 partial tiles are summed through
 // LDS in wave order, so results are deterministic.
+//
+// In the row layout a fragment is 16 rows x 64 bytes, 16 separate pieces
+// per load instruction; in the fragment-tiled layout it is one contiguous
+// 1 KB record, which streams at a much higher rate (the activations, read
+// by every block, gain the most).  The tiled weights are read with the
+// non-temporal policy (each byte is used once); for the row layout the
+// default policy is faster, as the two halves of each 128-byte line are
+// fetched by different waves.
 constexpr int kSmallWaves = 16;
-constexpr int kAuxNonTemporal = 2;  // cache policy bits of buffer ops: the weights are read once
+constexpr int kAuxNonTemporal = 2;  // cache policy bits of buffer ops
 constexpr int kSmallMaxM = 64;
 typedef __attribute__((ext_vector_type(4))) float f32x4s_t;
 
-template <bool OUT_BF16, int FM>
+template <bool OUT_BF16, int FM, bool TILED>
 __global__ __launch_bounds__(kWave * kSmallWaves) void gemm_small_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) f32x4s_t red[kSmallWaves][FM][kWave];
     const int lane = threadIdx.x & (kWave - 1);
@@ -328,11 +361,22 @@ __global__ __launch_bounds__(kWave * kSmallWaves) void gemm_small_kernel(GemmArg
     const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
     const uint32_t cpr = static_cast<uint32_t>(g.K) / 2;
     const uint32_t spr = static_cast<uint32_t>(g.K) / 32;
-    const uint32_t rows_b = static_cast<uint32_t>(min<int64_t>(16, g.N - n0));
-    const auto ra = rsrc(g.a_codes, static_cast<uint32_t>(g.M) * cpr);
-    const auto rsa = rsrc(g.a_scales, static_cast<uint32_t>(g.M) * spr);
-    const auto rb = rsrc(g.b_codes + n0 * cpr, rows_b * cpr);
-    const auto rsb = rsrc(g.b_scales + n0 * spr, rows_b * spr);
+    const uint32_t nk32 = static_cast<uint32_t>(g.K) / 128;
+    __amdgpu_buffer_rsrc_t ra, rsa, rb, rsb;
+    if constexpr (TILED) {
+        const uint32_t recs_a = static_cast<uint32_t>((g.M + 15) / 16);
+        ra = rsrc(g.a_codes, recs_a * nk32 * 1024);
+        rsa = rsrc(g.a_scales, recs_a * nk32 * 64);
+        rb = rsrc(g.b_codes + (n0 / 16) * nk32 * 1024, nk32 * 1024);
+        rsb = rsrc(g.b_scales + (n0 / 16) * nk32 * 64, nk32 * 64);
+    } else {
+        const uint32_t rows_b = static_cast<uint32_t>(min<int64_t>(16, g.N - n0));
+        ra = rsrc(g.a_codes, static_cast<uint32_t>(g.M) * cpr);
+        rsa = rsrc(g.a_scales, static_cast<uint32_t>(g.M) * spr);
+        rb = rsrc(g.b_codes + n0 * cpr, rows_b * cpr);
+        rsb = rsrc(g.b_scales + n0 * spr, rows_b * spr);
+    }
+    constexpr int kAuxB = TILED ? kAuxNonTemporal : 0;
     const uint32_t r16 = static_cast<uint32_t>(lane & 15);
     const uint32_t q = static_cast<uint32_t>(lane >> 4);
     f32x4s_t acc[FM];
@@ -350,16 +394,29 @@ __global__ __launch_bounds__(kWave * kSmallWaves) void gemm_small_kernel(GemmArg
         for (int d = 0; d < kDepth; ++d) {
             const int st = s0 + d * kSmallWaves;  // uniform across the wave
             if (st >= nk) break;
-            const uint32_t cb = static_cast<uint32_t>(st) * 64 + 16 * q;
-            const uint32_t sbyte = static_cast<uint32_t>(st) * 4 + q;
+            if constexpr (TILED) {
+                // record (f, st) of A, record st of this block's B record row
 #pragma unroll
-            for (int f = 0; f < FM; ++f) {
-                const uint32_t row = 16 * f + r16;
-                av[d][f] = __builtin_amdgcn_raw_buffer_load_b128(ra, row * cpr + cb, 0, 0);
-                sav[d][f] = __builtin_amdgcn_raw_buffer_load_b8(rsa, row * spr + sbyte, 0, 0);
+                for (int f = 0; f < FM; ++f) {
+                    const uint32_t rec = static_cast<uint32_t>(f) * nk32 + static_cast<uint32_t>(st);
+                    av[d][f] = __builtin_amdgcn_raw_buffer_load_b128(ra, rec * 1024 + 16 * lane, 0, 0);
+                    sav[d][f] = __builtin_amdgcn_raw_buffer_load_b8(rsa, rec * 64 + lane, 0, 0);
+                }
+                bv[d] = __builtin_amdgcn_raw_buffer_load_b128(rb, static_cast<uint32_t>(st) * 1024 + 16 * lane, 0,
+                                                              kAuxB);
+                sbv[d] = __builtin_amdgcn_raw_buffer_load_b8(rsb, static_cast<uint32_t>(st) * 64 + lane, 0, kAuxB);
+            } else {
+                const uint32_t cb = static_cast<uint32_t>(st) * 64 + 16 * q;
+                const uint32_t sbyte = static_cast<uint32_t>(st) * 4 + q;
+#pragma unroll
+                for (int f = 0; f < FM; ++f) {
+                    const uint32_t row = 16 * f + r16;
+                    av[d][f] = __builtin_amdgcn_raw_buffer_load_b128(ra, row * cpr + cb, 0, 0);
+                    sav[d][f] = __builtin_amdgcn_raw_buffer_load_b8(rsa, row * spr + sbyte, 0, 0);
+                }
+                bv[d] = __builtin_amdgcn_raw_buffer_load_b128(rb, r16 * cpr + cb, 0, kAuxB);
+                sbv[d] = __builtin_amdgcn_raw_buffer_load_b8(rsb, r16 * spr + sbyte, 0, kAuxB);
             }
-            bv[d] = __builtin_amdgcn_raw_buffer_load_b128(rb, r16 * cpr + cb, 0, kAuxNonTemporal);
-            sbv[d] = __builtin_amdgcn_raw_buffer_load_b8(rsb, r16 * spr + sbyte, 0, kAuxNonTemporal);
         }
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
@@ -395,30 +452,61 @@ __global__ __launch_bounds__(kWave * kSmallWaves) void gemm_small_kernel(GemmArg
     }
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, bool TILED>
 void launch_small(const GemmArgs& g, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>((g.N + 15) / 16));
     const dim3 block(kWave * kSmallWaves);
     if (g.M <= 16)
-        hipLaunchKernelGGL((gemm_small_kernel<OUT_BF16, 1>), grid, block, 0, st, g);
+        hipLaunchKernelGGL((gemm_small_kernel<OUT_BF16, 1, TILED>), grid, block, 0, st, g);
     else if (g.M <= 32)
-        hipLaunchKernelGGL((gemm_small_kernel<OUT_BF16, 2>), grid, block, 0, st, g);
+        hipLaunchKernelGGL((gemm_small_kernel<OUT_BF16, 2, TILED>), grid, block, 0, st, g);
     else
-        hipLaunchKernelGGL((gemm_small_kernel<OUT_BF16, 4>), grid, block, 0, st, g);
+        hipLaunchKernelGGL((gemm_small_kernel<OUT_BF16, 4, TILED>), grid, block, 0, st, g);
+}
+
+template <bool TILED>
+mxq_status launch_gemm(const GemmArgs& g, bool out_bf16, hipStream_t st) {
+    if (g.M <= kSmallMaxM) {
+        if (out_bf16)
+            launch_small<true, TILED>(g, st);
+        else
+            launch_small<false, TILED>(g, st);
+    } else {
+        const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(g.tiles_m) * g.tiles_n));
+        if (out_bf16)
+            hipLaunchKernelGGL((gemm_kernel<true, TILED>), grid, dim3(kThreads), 0, st, g);
+        else
+            hipLaunchKernelGGL((gemm_kernel<false, TILED>), grid, dim3(kThreads), 0, st, g);
+    }
+    return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+}
+
+// Fragment-tiled storage: one thread per 16-byte slot, in record order, so
+// each wave writes one 1 KB code record; padding rows get zero bytes.
+__global__ __launch_bounds__(256) void tile_kernel(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                                   int32_t K, uint8_t* tcodes, uint8_t* tscales, int64_t slots) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= slots) return;
+    const int64_t nk = K / kStageK;
+    const int64_t rec = i >> 6;
+    const int l = static_cast<int>(i & 63);
+    const int64_t row = 16 * (rec / nk) + (l & 15);
+    const int64_t grp = 4 * (rec % nk) + (l >> 4);
+    u32x4g_t v = {0u, 0u, 0u, 0u};
+    uint8_t sc = 0;
+    if (row < rows) {
+        v = *reinterpret_cast<const u32x4g_t*>(codes + row * (K / 2) + 16 * grp);
+        sc = scales[row * (K / 32) + grp];
+    }
+    *reinterpret_cast<u32x4g_t*>(tcodes + 16 * i) = v;
+    tscales[i] = sc;
 }
 
 bool aligned_to(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
-}  // namespace
-}  // namespace mxq
-
-using namespace mxq;
-
-extern "C" {
-
-mxq_status mxq_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
-                          const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* y, int32_t y_dtype,
-                          int64_t ldy, void* stream) {
+mxq_status gemm_impl(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                            const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* y, int32_t y_dtype,
+                            int64_t ldy, void* stream, bool tiled) {
     if (y_dtype != MXQ_FP32 && y_dtype != MXQ_BF16) return MXQ_ERR_DTYPE;
     if (M < 0 || N < 0 || K < 0 || K % kStageK || K > kMaxK || M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31))
         return MXQ_ERR_SHAPE;
@@ -431,24 +519,48 @@ mxq_status mxq_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const
     const int64_t tiles_n = (N + kBN - 1) / kBN;
     // K == 0 is an empty reduction: the kernel reads nothing and writes zeros.
     if (K > 0 && (!a_codes || !a_scales || !b_codes || !b_scales)) return MXQ_ERR_NULL;
-    if (!aligned_to(a_codes, 16) || !aligned_to(b_codes, 16) || !aligned_to(a_scales, 2) || !aligned_to(b_scales, 2))
+    const uintptr_t salign = tiled ? 4 : 2;
+    if (!aligned_to(a_codes, 16) || !aligned_to(b_codes, 16) || !aligned_to(a_scales, salign) ||
+        !aligned_to(b_scales, salign))
         return MXQ_ERR_ALIGN;
     if (tiles_m * tiles_n >= (int64_t(1) << 31)) return MXQ_ERR_SHAPE;
     GemmArgs g{a_codes, a_scales, b_codes, b_scales, y, ldy, static_cast<int32_t>(M), static_cast<int32_t>(N),
                static_cast<int32_t>(K), static_cast<int32_t>(tiles_m), static_cast<int32_t>(tiles_n)};
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (M <= kSmallMaxM) {
-        if (y_dtype == MXQ_BF16)
-            launch_small<true>(g, st);
-        else
-            launch_small<false>(g, st);
-        return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
-    }
-    const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n));
-    if (y_dtype == MXQ_BF16)
-        hipLaunchKernelGGL((gemm_kernel<true>), grid, dim3(kThreads), 0, st, g);
-    else
-        hipLaunchKernelGGL((gemm_kernel<false>), grid, dim3(kThreads), 0, st, g);
+    return tiled ? launch_gemm<true>(g, y_dtype == MXQ_BF16, st) : launch_gemm<false>(g, y_dtype == MXQ_BF16, st);
+}
+
+}  // namespace
+}  // namespace mxq
+
+using namespace mxq;
+
+extern "C" {
+
+mxq_status mxq_gemm_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                          const uint8_t* b_scales, int64_t M, int64_t N, int64_t K, void* y, int32_t y_dtype,
+                          int64_t ldy, void* stream) {
+    return gemm_impl(a_codes, a_scales, b_codes, b_scales, M, N, K, y, y_dtype, ldy, stream, false);
+}
+
+mxq_status mxq_gemm_mxfp4_tiled(const uint8_t* a_tcodes, const uint8_t* a_tscales, const uint8_t* b_tcodes,
+                                const uint8_t* b_tscales, int64_t M, int64_t N, int64_t K, void* y,
+                                int32_t y_dtype, int64_t ldy, void* stream) {
+    return gemm_impl(a_tcodes, a_tscales, b_tcodes, b_tscales, M, N, K, y, y_dtype, ldy, stream, true);
+}
+
+mxq_status mxq_tile_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t K,
+                          uint8_t* tiled_codes, uint8_t* tiled_scales, void* stream) {
+    if (rows < 0 || K < 0 || K % kStageK || K > kMaxK || rows >= (int64_t(1) << 31)) return MXQ_ERR_SHAPE;
+    if (rows == 0 || K == 0) return MXQ_OK;
+    if (!codes || !scales || !tiled_codes || !tiled_scales) return MXQ_ERR_NULL;
+    if (!aligned_to(codes, 16) || !aligned_to(tiled_codes, 16)) return MXQ_ERR_ALIGN;
+    const int64_t slots = (rows + 15) / 16 * (K / kStageK) * 64;
+    const int64_t blocks = (slots + 255) / 256;
+    if (blocks >= (int64_t(1) << 31)) return MXQ_ERR_SHAPE;
+    hipLaunchKernelGGL(tile_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), codes, scales, rows, static_cast<int32_t>(K), tiled_codes,
+                       tiled_scales, slots);
     return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 

@@ -342,3 +342,56 @@ def absorb_quant(w_lin, lam, r, orc: "Oracle | None" = None):
     N, K = w.shape
     codes, scales = orc.encode_groups(w)
     return codes.reshape(N, K // 2), scales.reshape(N, K // GROUP)
+
+
+# ---- fragment-tiled storage of MXFP4 operands --------------------------------
+#
+# A storage order, not arithmetic: the pages fix no memory layout.  An MXFP4
+# operand of R rows and K reduction positions (codes [R, K/2], scales
+# [R, K/32], K a multiple of 128) is cut into records of 16 rows x 128
+# positions.  Record (t, s) -- rows 16 t .. 16 t + 15, positions 128 s ..
+# 128 s + 127 -- has index t * (K / 128) + s and 64 slots; slot l belongs to
+# row 16 t + l % 16 and group 4 s + l // 16 (32 positions).  The code record
+# holds the slots' 16 code bytes one after another (1024 bytes), the scale
+# record their scale bytes (64 bytes).  Rows past R in the last record row
+# are padding, written as zero bytes here.  The slot order is the operand
+# order of the 16 x 16 x 128 scaled matrix-core instruction (lane l: row
+# l % 16, group l // 16), so a record is one contiguous operand fragment.
+
+TILE_ROWS, TILE_K = 16, 128
+
+
+def _tile_dims(rows, K):
+    if K % TILE_K:
+        raise ValueError("K must be a multiple of 128")
+    return -(-rows // TILE_ROWS), K // TILE_K
+
+
+def tile_mxfp4(codes, scales):
+    """Row layout -> fragment-tiled layout; returns flat uint8 arrays of
+    ceil(R/16) * (K/128) * 1024 code bytes and * 64 scale bytes."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    R, half = codes.shape
+    K = 2 * half
+    if scales.shape != (R, K // GROUP):
+        raise ValueError("scales must be [rows, K/32]")
+    rt, nk = _tile_dims(R, K)
+    pc = np.zeros((rt * TILE_ROWS, half), np.uint8)
+    pc[:R] = codes
+    ps = np.zeros((rt * TILE_ROWS, K // GROUP), np.uint8)
+    ps[:R] = scales
+    # [t, row-in-tile, s, group-in-stage, byte] -> [t, s, group-in-stage, row-in-tile, byte]
+    tc = pc.reshape(rt, TILE_ROWS, nk, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
+    ts = ps.reshape(rt, TILE_ROWS, nk, 4).transpose(0, 2, 3, 1).reshape(-1)
+    return np.ascontiguousarray(tc), np.ascontiguousarray(ts)
+
+
+def untile_mxfp4(tcodes, tscales, rows, K):
+    """Inverse of :func:`tile_mxfp4` (padding rows dropped)."""
+    rt, nk = _tile_dims(rows, K)
+    tc = np.asarray(tcodes, np.uint8).reshape(rt, nk, 4, TILE_ROWS, 16)
+    ts = np.asarray(tscales, np.uint8).reshape(rt, nk, 4, TILE_ROWS)
+    codes = tc.transpose(0, 3, 1, 2, 4).reshape(rt * TILE_ROWS, K // 2)[:rows]
+    scales = ts.transpose(0, 3, 1, 2).reshape(rt * TILE_ROWS, K // GROUP)[:rows]
+    return np.ascontiguousarray(codes), np.ascontiguousarray(scales)

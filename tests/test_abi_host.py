@@ -230,3 +230,48 @@ def test_rotate_quant_block_validation(lib):
     assert bq(lib, x=P_ODD) == ALIGN
     assert bq(lib, lam=P_ODD) == ALIGN
     assert bq(lib, y=P_ODD) == ALIGN
+
+
+def gt(lib, a=P, sa=P, b=P, sb=P, M=8, N=8, K=256, y=P, dt=2, ldy=8):
+    return lib.mxq_gemm_mxfp4_tiled(a, sa, b, sb, M, N, K, y, dt, ldy, None)
+
+
+def test_tiled_entry_points_validation(lib):
+    # tiled product: same rules as the row layout, scales 4-byte aligned
+    assert gt(lib, dt=1) == DTYPE
+    assert gt(lib, K=64) == SHAPE
+    assert gt(lib, K=(1 << 24) + 128) == SHAPE
+    assert gt(lib, N=-1) == SHAPE
+    assert gt(lib, M=0, a=None, sa=None, b=None, sb=None, y=None) == OK
+    assert gt(lib, y=None) == NULL
+    assert gt(lib, sa=None) == NULL
+    assert gt(lib, ldy=7) == STRIDE
+    assert gt(lib, a=P_ODD) == ALIGN
+    assert gt(lib, sb=ctypes.c_void_p(0x10002)) == ALIGN
+    # repacking into records
+    tile = lib.mxq_tile_mxfp4
+    assert tile(P, P, 8, 192, P, P, None) == SHAPE
+    assert tile(P, P, -1, 128, P, P, None) == SHAPE
+    assert tile(P, P, 8, (1 << 24) + 128, P, P, None) == SHAPE
+    assert tile(P, P, 1 << 31, 128, P, P, None) == SHAPE
+    assert tile(None, None, 0, 128, None, None, None) == OK
+    assert tile(P, P, 8, 0, P, P, None) == OK
+    assert tile(P, None, 8, 128, P, P, None) == NULL
+    assert tile(P, P, 8, 128, P, None, None) == NULL
+    assert tile(P_ODD, P, 8, 128, P, P, None) == ALIGN
+    assert tile(P, P, 8, 128, P_ODD, P, None) == ALIGN
+    # quantizer with tiled output: channels must be a multiple of 128
+    rqt = lib.mxq_rotate_quant_tiled
+    assert rqt(P, 0, 8, 96, 96, None, P, P, P, None) == SHAPE
+    assert rqt(P, 2, 8, 128, 128, None, P, P, P, None) == DTYPE
+    assert rqt(P, 0, 8, 128, 128, None, None, P, P, None) == NULL
+    assert rqt(P, 0, 8, 128, 64, None, P, P, P, None) == STRIDE
+    assert rqt(P, 0, 8, 128, 128, None, P, P_ODD, P, None) == ALIGN
+    assert rqt(None, 0, 0, 128, 128, None, None, None, None, None) == OK
+
+
+def test_tiled_sizes():
+    assert mxq.tiled_sizes(1, 128) == (16 * 64, 16 * 4)
+    assert mxq.tiled_sizes(17, 256) == (32 * 128, 32 * 8)
+    with pytest.raises(ValueError):
+        mxq.tiled_sizes(4, 96)

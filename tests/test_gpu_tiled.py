@@ -1,0 +1,147 @@
+"""Fragment-tiled MXFP4 operands on an MI355X through the C ABI: the repack
+against the oracle's definition of the layout (bit-exact), the quantizer's
+tiled output against the repacked row output (bit-exact), and the tiled
+product against the row-layout product (bit-identical: same instruction
+sequence on the same operand bytes) and the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_activation_rotation_amd as mxq
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+U = 2.0 ** -24
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    mxq.load()
+    return torch.device("cuda:0")
+
+
+def _u8(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+@pytest.mark.parametrize("rows,K", [(1, 128), (16, 128), (37, 384), (200, 1152), (64, 14336)])
+def test_tile_matches_oracle(dev, rows, K):
+    rng = np.random.default_rng(9000 + rows + K)
+    codes, scales = W.random_mxfp4(rng, rows, K)
+    tc, ts = mxq.tile_mxfp4(_u8(codes, dev), _u8(scales, dev))
+    torch.cuda.synchronize()
+    rc, rs = O.tile_mxfp4(codes, scales)
+    assert np.array_equal(tc.cpu().numpy(), rc) and np.array_equal(ts.cpu().numpy(), rs)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (5, 40, 256), (16, 300, 1152), (17, 33, 384), (33, 70, 128),
+                                   (64, 130, 512), (65, 257, 1024), (300, 260, 768), (513, 129, 1152)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_tiled_product_same_bits(dev, M, N, K, out_dtype):
+    rng = np.random.default_rng(M * 131 + N * 7 + K)
+    a = [_u8(t, dev) for t in W.random_mxfp4(rng, M, K)]
+    b = [_u8(t, dev) for t in W.random_mxfp4(rng, N, K)]
+    print(f"  tiled gemm M={M} N={N} K={K} {out_dtype}", flush=True)
+    y_row = mxq.gemm_mxfp4(*a, *b, out_dtype)
+    ta = mxq.tile_mxfp4(*a)
+    tb = mxq.tile_mxfp4(*b)
+    y_t = mxq.gemm_mxfp4_tiled(*ta, *tb, M, N, K, out_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(y_t, y_row)
+    if out_dtype == torch.float32 and M * N <= 40000:
+        ref, s_abs = O.gemm_mxfp4(*[t.cpu().numpy() for t in a], *[t.cpu().numpy() for t in b])
+        err = np.abs(y_t.cpu().numpy().astype(np.float64) - ref)
+        assert (err <= 2.0 * K * U * s_abs).all()
+
+
+@pytest.mark.parametrize("M,N", [(20, 37), (300, 90)])
+def test_tiled_product_garbage_padding(dev, M, N):
+    """Padding rows of the records only reach outputs that are not written."""
+    rng = np.random.default_rng(9101 + M)
+    K = 256
+    a = [_u8(t, dev) for t in W.random_mxfp4(rng, M, K)]
+    b = [_u8(t, dev) for t in W.random_mxfp4(rng, N, K)]
+    ta = mxq.tile_mxfp4(*a)
+    tb = mxq.tile_mxfp4(*b)
+    y0 = mxq.gemm_mxfp4_tiled(*ta, *tb, M, N, K)
+    # overwrite every padding slot with NaN scales and random codes
+    for (tc, ts), rows in ((ta, M), (tb, N)):
+        nk = K // 128
+        rec = torch.arange(tc.numel() // 16, device=dev)
+        row = 16 * (rec // 64 // nk) + rec % 16
+        pad = row >= rows
+        tc.view(-1, 16)[pad] = torch.randint(0, 256, (int(pad.sum()), 16), dtype=torch.uint8, device=dev)
+        ts[pad] = 255
+    y1 = mxq.gemm_mxfp4_tiled(*ta, *tb, M, N, K)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.isfinite(y1).all()
+
+
+def test_tiled_product_empty_and_k0(dev):
+    e = torch.empty(0, dtype=torch.uint8, device=dev)
+    nc, ns = mxq.tiled_sizes(16, 128)
+    bc = torch.zeros(nc, dtype=torch.uint8, device=dev)
+    bs = torch.zeros(ns, dtype=torch.uint8, device=dev)
+    y = mxq.gemm_mxfp4_tiled(e, e, bc, bs, 0, 16, 128)
+    assert y.shape == (0, 16)
+    y = torch.full((3, 5), 7.0, device=dev)
+    mxq.gemm_mxfp4_tiled(e, e, e, e, 3, 5, 0, out=y)
+    torch.cuda.synchronize()
+    assert (y == 0).all()
+
+
+@pytest.mark.parametrize("T,C", [(1, 128), (16, 4096), (30, 14336), (130, 2048 + 4 * 128)])
+@pytest.mark.parametrize("dtype,with_lam", [(torch.bfloat16, False), (torch.bfloat16, True),
+                                            (torch.float16, True)])
+def test_rotate_quant_tiled_same_bytes(dev, T, C, dtype, with_lam):
+    rng = np.random.default_rng(9200 + T + C // 128 + 7 * with_lam)
+    x = W.random_activations(rng, T, C, dtype, scale=2.0).to(dev)
+    lam = torch.from_numpy(np.exp(0.5 * rng.standard_normal(C)).astype(np.float32)).to(dev) if with_lam else None
+    r = W.bf16_matrix(W.qr_orthogonal(rng)).to(dev)
+    codes, scales = mxq.rotate_quant(x, r, lam)
+    ref = mxq.tile_mxfp4(codes, scales)
+    nc, ns = mxq.tiled_sizes(T, C)
+    tc = torch.zeros(nc, dtype=torch.uint8, device=dev)  # padding rows stay zero, as in the repack
+    ts = torch.zeros(ns, dtype=torch.uint8, device=dev)
+    mxq.rotate_quant_tiled(x, r, lam, tcodes=tc, tscales=ts)
+    torch.cuda.synchronize()
+    assert torch.equal(tc, ref[0]) and torch.equal(ts, ref[1])
+    c2, s2 = O.untile_mxfp4(tc.cpu().numpy(), ts.cpu().numpy(), T, C)
+    assert np.array_equal(c2, codes.cpu().numpy()) and np.array_equal(s2, scales.cpu().numpy())
+
+
+def test_decode_pipeline_full_size(dev):
+    """16 tokens of the headline batch, rotated and quantized straight into
+    records, times the absorbed 4096 x 14336 weights in records: the same
+    bits as the row-layout pipeline."""
+    wl = W.make_config(3)
+    w = W.linear_weights(W.DOWN_PROJ_OUT, wl.channels)
+    r = wl.r_hat.to(dev)
+    lam = torch.from_numpy(wl.lam).to(dev) if wl.lam is not None else None
+    x16 = wl.x[:16].contiguous().to(dev)
+    bc, bsc = mxq.absorb_quant(w.to(dev), r, lam)
+    ac, asc = mxq.rotate_quant(x16, r, lam)
+    y_row = mxq.gemm_mxfp4(ac, asc, bc, bsc, torch.bfloat16)
+    ta = mxq.rotate_quant_tiled(x16, r, lam)
+    tb = mxq.tile_mxfp4(bc, bsc)
+    y_t = mxq.gemm_mxfp4_tiled(*ta, *tb, 16, W.DOWN_PROJ_OUT, wl.channels, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y_t, y_row)
+
+
+def test_large_product_full_size_same_bits(dev):
+    """8192 x 4096 x 14336 (the down_proj product of the headline batch):
+    tiled and row-layout products agree bit for bit."""
+    M, N, K = 8192, 4096, 14336
+    g = torch.Generator(device=dev)
+    g.manual_seed(9300)
+    a = (torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device=dev, generator=g),
+         torch.randint(115, 135, (M, K // 32), dtype=torch.uint8, device=dev, generator=g))
+    b = (torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=dev, generator=g),
+         torch.randint(115, 135, (N, K // 32), dtype=torch.uint8, device=dev, generator=g))
+    y_row = mxq.gemm_mxfp4(*a, *b, torch.bfloat16)
+    y_t = mxq.gemm_mxfp4_tiled(*mxq.tile_mxfp4(*a), *mxq.tile_mxfp4(*b), M, N, K, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y_t, y_row)
