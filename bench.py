@@ -38,7 +38,7 @@ KERNEL_SOURCES = ("mxfp4_activation_rotation_amd/csrc/mxq.hip",
                   "mxfp4_activation_rotation_amd/csrc/mxq_device.h")
 COUNTERS = {3: "profiles/rotate_quant_bf16_8192x14336_hbm_counters.txt"}
 GEMM_SOURCES = ("mxfp4_activation_rotation_amd/csrc/mxq_gemm.hip",)
-GEMM_COUNTERS = "profiles/gemm_mxfp4_8192x4096x14336_hbm_counters.txt"
+GEMM_COUNTERS = "profiles/gemm_mxfp4_tiled_8192x4096x14336_hbm_counters.txt"
 FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 (E2M1) matrix-core peak
 WORKLOAD_NAMES = {
     2: "QKV-input shape: bf16 2048x4096, 0.5% outlier channels x20, lognormal lambda, seeded orthogonal R",
@@ -160,9 +160,9 @@ def bench_gemm(args):
     operands (88 MB) are built once on the GPU before the timed region.
     With --decode, the activations are 16 tokens of the same batch: the
     product is bound by reading the weights, so its roofline is HBM.  Both
-    operands are then in the fragment-tiled layout (the activations written
-    so by the quantizer, the weights repacked once offline); --row-layout
-    times the row-layout operands instead."""
+    operands are in the fragment-tiled layout (the activations written so by
+    the quantizer, the weights repacked once offline); --row-layout times the
+    row-layout operands instead."""
     import numpy as np
     import torch
 
@@ -178,17 +178,17 @@ def bench_gemm(args):
     bc, bsc = mxq.absorb_quant(w.to(dev), r, lam)
     M, K, N = ac.shape[0], wl.channels, workloads.DOWN_PROJ_OUT
     weight_bytes = N * (K // 2 + K // 32)
-    weights = [(bc, bsc)]
-    tiled = args.decode and not args.row_layout
+    tiled = not args.row_layout
+    if args.decode:
+        M = 16
+        ac, asc = ac[:M].contiguous(), asc[:M].contiguous()
+    if tiled:
+        ta, tsa = mxq.rotate_quant_tiled(wl.x[:M].contiguous().to(dev), r, lam)
+    weights = [mxq.tile_mxfp4(bc, bsc) if tiled else (bc, bsc)]
     if args.decode:
         # A decode step reads every layer's weights once: rotate through
         # enough weight copies (> 768 MB) that none is still cached from its
         # previous use, so the weights stream from HBM as they would there.
-        M = 16
-        ac, asc = ac[:M].contiguous(), asc[:M].contiguous()
-        if tiled:
-            ta, tsa = mxq.rotate_quant_tiled(wl.x[:M].contiguous().to(dev), r, lam)
-            weights = [mxq.tile_mxfp4(bc, bsc)]
         weights += [(weights[0][0].clone(), weights[0][1].clone())
                     for _ in range(int(np.ceil(768e6 / weight_bytes)))]
     n_w = len(weights)
@@ -215,7 +215,7 @@ def bench_gemm(args):
     wall = time.perf_counter() - t0
     mean_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
     achieved = flop / mean_launch_s / 1e12
-    hbm = None if args.decode else read_counters(0, GEMM_COUNTERS, GEMM_SOURCES)
+    hbm = None if (args.decode or not tiled) else read_counters(0, GEMM_COUNTERS, GEMM_SOURCES)
     result = {
         "metric": "W4A4 MXFP4 GEMM throughput (consumer of the quantized activations): TFLOP/s",
         "value": round(flop * args.steps / wall / 1e12, 1),
@@ -228,7 +228,9 @@ def bench_gemm(args):
         "config": {"workload": "down_proj product: activations bf16 8192x14336 (the headline batch) rotated and "
                                "MXFP4-quantized, times absorbed MXFP4 weights 4096x14336 (seeded N(0, 1/14336)); "
                                "fp32 accumulation, bf16 output",
-                   "M": M, "N": N, "K": K, "operands": "E2M1 codes + E8M0 scales per 32 along K",
+                   "M": M, "N": N, "K": K,
+                   "operands": "E2M1 codes + E8M0 scales per 32 along K, " +
+                               ("fragment-tiled records (16 rows x 128 positions)" if tiled else "row layout"),
                    "parallelism": "single GPU", "launch": "eager launches"},
         "launch_us_mean": round(mean_launch_s * 1e6, 3),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP4_MFMA_PEAK_TFLOPS,
@@ -245,8 +247,6 @@ def bench_gemm(args):
         result["config"]["workload"] = ("decode product: 16 tokens of the headline batch, rotated and MXFP4-"
                                         "quantized, times absorbed MXFP4 weights 4096x14336, bf16 output")
         result["config"]["weight_sets"] = n_w
-        result["config"]["operands"] += (", fragment-tiled records (16 rows x 128 positions)" if tiled
-                                         else ", row layout")
         result["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                               "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}
     if not args.no_cpu_baseline:
@@ -384,12 +384,14 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="with --gemm: 16 activation rows (decode), timed against HBM bandwidth")
     ap.add_argument("--row-layout", action="store_true",
-                    help="with --gemm --decode: row-layout operands instead of fragment-tiled ones")
+                    help="with --gemm: row-layout operands instead of fragment-tiled ones")
     ap.add_argument("--norm", action="store_true",
                     help="time the norm-fused path instead: RMSNorm + smooth + rotate + MXFP4 on bf16 8192x4096")
     ap.add_argument("--block", type=int, default=0, choices=[0, 16, 32, 64, 128],
                     help="time the block-size variant kernel (DuQuant++ page sec. 4.3 ablation) with a seeded "
                          "random Hadamard block of this size instead of the workload's 32-wide block")
+    ap.add_argument("--tiled", action="store_true",
+                    help="quantizer output in the fragment-tiled layout (the tiled product's A operand)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -438,14 +440,21 @@ def main():
     if args.block:
         r = workloads.bf16_matrix(workloads.random_hadamard(np.random.default_rng(2005 + args.block),
                                                             args.block)).to(dev)
-    outs = [(torch.empty((call_tokens, C // 2), dtype=torch.uint8, device=dev),
-             torch.empty((call_tokens, C // 32), dtype=torch.uint8, device=dev)) for _ in range(n_buf)]
+    if args.tiled:
+        nc, ns = mxq.tiled_sizes(call_tokens, C)
+        outs = [(torch.empty((nc,), dtype=torch.uint8, device=dev), torch.empty((ns,), dtype=torch.uint8, device=dev))
+                for _ in range(n_buf)]
+    else:
+        outs = [(torch.empty((call_tokens, C // 2), dtype=torch.uint8, device=dev),
+                 torch.empty((call_tokens, C // 32), dtype=torch.uint8, device=dev)) for _ in range(n_buf)]
     torch.cuda.synchronize()
 
     def step(i):
         c, s = outs[i % n_buf]
         if args.block:
             mxq.rotate_quant_block(xs[i % n_buf], r, lam, codes=c, scales=s)
+        elif args.tiled:
+            mxq.rotate_quant_tiled(xs[i % n_buf], r, lam, tcodes=c, tscales=s)
         else:
             mxq.rotate_quant(xs[i % n_buf], r, lam, codes=c, scales=s)
 
@@ -485,7 +494,7 @@ def main():
 
     achieved = step_bytes / mean_launch_s / 1e9
     value = elems * args.steps / wall / 1e9
-    hbm = None if args.block else read_counters(args.workload)
+    hbm = None if (args.block or args.tiled) else read_counters(args.workload)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -504,6 +513,7 @@ def main():
                    "r_hat": (f"seeded random Hadamard {args.block}x{args.block} (block-size variant kernel)"
                              if args.block else "bf16 32x32"),
                    "buffer_sets": n_buf, "parallelism": "single GPU",
+                   "output_layout": "fragment-tiled records" if args.tiled else "row layout",
                    "launch": "hip graph of the K launches" if args.graph else "eager launches"},
         "hbm_gbps": round(value * BYTES_PER_ELEM, 1),
         "pct_hbm_peak": round(100 * value * BYTES_PER_ELEM / HBM_PEAK_GBPS, 2),

@@ -12,29 +12,29 @@
 //
 // v_mfma_scale_f32_16x16x128_f8f6f4 with E2M1 operands multiplies a 16 x 128
 // block of A by a 128 x 16 block of B^T.  Lane l supplies row l % 16 and the
-// 32 consecutive K positions of block l / 16: 16 code bytes in the order they
-// are stored, low nibble first, which is exactly one MXFP4 group, plus that
-// group's scale byte.  Each operand fragment is therefore a plain 16-byte
-// load per lane straight from the stored codes, with no repacking.  The sum
-// over K does not care which group sits in which MFMA, so within a stage of
-// 256 K positions lane l takes groups 2 (l / 16) and 2 (l / 16) + 1 (32
-// contiguous code bytes, 2 contiguous scale bytes) for the stage's two MFMAs;
-// A and B use the same assignment, so every product pairs the same k.
+// 32 consecutive K positions of group l / 16 of the 128: 16 code bytes in the
+// order they are stored, low nibble first, which is exactly one MXFP4 group,
+// plus that group's scale byte.  Each operand fragment is therefore 64 plain
+// 16-byte pieces of the stored codes, with no repacking.
 //
-// Tiling (MI355X-first): a block of 8 waves (2 per SIMD) computes a
-// 256 x 256 tile of y, each wave 128 x 64 (8 x 4 accumulator fragments, 128
-// VGPRs).  K advances 256 positions per stage.  A stage of both operands
-// (2 x 32 KB of codes, 2 x 2 KB of scales) goes straight from global memory
-// into LDS (buffer loads with the lds modifier: no staging registers),
-// double-buffered (136 KB of the CU's 160 KB): the loads of stage s + 1 are
-// in flight while stage s computes, and one barrier per stage separates them
-// from the reads of stage s - 1 in the same buffer.  In LDS every fragment
-// is stored in the order the MFMA lanes consume it (lane l's 16 bytes at
-// offset 16 l of a 1 KB slot, which is also where a direct load puts lane
-// l's data), so the operand reads are contiguous ds_read_b128 without bank
-// conflicts.  Global loads go through buffer resources bounded to the
-// tile's rows, so rows past M or N read as zero (codes 0, scale 2^-127:
-// products 0) and ragged edges need no branches in the loop.
+// Two storage layouts are accepted, and each kernel is one template over
+// them: the row layout the quantizer writes by default, and fragment-tiled
+// records (16 rows x 128 positions, slot l = row l % 16, group l / 16), in
+// which a fragment is one contiguous 1 KB record.  The MFMA sequence is the
+// same for both, so the outputs are bit-identical.
+//
+// Large products (M > 64): a block of 8 waves (2 per SIMD) computes a
+// 256 x 256 tile of y, each wave 128 x 64 (8 x 4 accumulator fragments).  K
+// advances 128 positions per stage through a 4-deep LDS ring filled three
+// stages ahead by buffer loads with the lds modifier (no staging registers),
+// with one bare s_barrier per stage; scales travel in a 3-chunk ring of 4
+// stages each.  In LDS every fragment sits in a 1 KB slot read by a
+// conflict-free ds_read_b128.  Global loads go through buffer resources
+// bounded to the tile's rows (or records), so rows past M or N read as zero
+// (codes 0, scale 2^-127: products 0) and ragged edges need no branches.
+//
+// Decode-shaped products (M <= 64): split-K over the 16 waves of a block
+// that owns 16 output columns (see gemm_small_kernel).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
