@@ -231,8 +231,10 @@ mxq_status mxq_gemm_mxfp4(const uint8_t *a_codes, const uint8_t *a_scales, const
  *
  * mxq_rotate_quant_tiled: mxq_rotate_quant with its codes and scales written
  *   in the tiled layout (bit-identical bytes, other positions); channels must
- *   be a multiple of 128 (MXQ_ERR_SHAPE).  The padding rows of the last
- *   record row are not written.  Other rules as mxq_rotate_quant.
+ *   be a multiple of 128 (MXQ_ERR_SHAPE) and tiled_scales 16-byte aligned
+ *   (MXQ_ERR_ALIGN).  The codes of the padding rows of the last record row
+ *   are not written; their scale bytes may be written as zero.  Other rules
+ *   as mxq_rotate_quant.
  *
  * mxq_gemm_mxfp4_tiled: mxq_gemm_mxfp4 with both operands tiled (A from
  *   mxq_rotate_quant_tiled or mxq_tile_mxfp4, B from mxq_tile_mxfp4 of

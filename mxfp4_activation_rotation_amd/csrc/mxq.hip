@@ -120,6 +120,7 @@ struct Args {
     int32_t tcols;    // super-tile columns = ceil(gpr / 64)
     int32_t row_step; // waves per super-tile column
     int32_t waves;    // tcols * row_step
+    int32_t unit;     // rows a wave takes back to back (1, or 16 for tiled output)
 };
 
 template <int XT, int MODE, int LAM, bool YOUT, bool TILED = false>
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
     const int w = static_cast<int>(blockIdx.x) * kWavesPerBlock + wave;
     if (w >= a.waves) return;
     const int tc = w % a.tcols;
-    const int64_t r0 = w / a.tcols;
+    const int64_t r0 = static_cast<int64_t>(w / a.tcols) * (TILED ? a.unit : 1);
     const int64_t rs = a.row_step;
     const int64_t T = a.tokens;
     const int j = lane & 15;
@@ -206,12 +207,9 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
         }
     }
 
-    auto process_rows = [&](const Rows& buf, int64_t r) {
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int64_t rr = r + u * rs;
-            if (rr >= T) break;
-            uint32_t word[kSub];
+    // Codes and scale of row rr (held in buf[u]): after the transpose lane l
+    // holds the 16 code bytes of group p0 + l, and S is that group's scale.
+    auto encode_row = [&](const Rows& buf, int u, int64_t rr, uint32_t (&word)[kSub], uint32_t& S) {
             uint32_t sc[kSub];
 #pragma unroll
             for (int s = 0; s < kSub; ++s) {
@@ -274,7 +272,9 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
             }
             transpose_words(word);
             // the scale of group 16 q + j is the one computed in sub-tile q
-            const uint32_t S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
+            S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
+    };
+    auto store_row = [&](int64_t rr, const uint32_t (&word)[kSub], uint32_t S) {
             if constexpr (TILED) {
                 // Fragment-tiled output: group g of row rr is slot
                 // 16 (g % 4) + rr % 16 of record (rr / 16, g / 4); a record
@@ -298,18 +298,98 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
                 __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, scale_off, 0,
                                                      MXQ_NT_SCALE ? kAuxNT : 0);
             }
+    };
+    auto process_rows = [&](const Rows& buf, int64_t r) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t rr = r + u * rs;
+            if (rr >= T) break;
+            uint32_t word[kSub];
+            uint32_t S;
+            encode_row(buf, u, rr, word, S);
+            store_row(rr, word, S);
         }
     };
 
     // Two row buffers alternate: the next batch is in flight while the
     // current one is computed.
-    const int64_t step = kBatch * rs;
-    for (int64_t r = r0; r < T; r += 2 * step) {
-        if (r + step < T) load_rows(bufB, r + step);
-        process_rows(bufA, r);
-        if (r + step >= T) break;
-        if (r + 2 * step < T) load_rows(bufA, r + 2 * step);
-        process_rows(bufB, r + step);
+    if constexpr (TILED) {
+        static_assert(kBatch == 1, "one row per step");
+        if (a.unit == 16) {
+            // Units of 16 consecutive rows (one record row), units
+            // r0 / 16 + k * rs, in two halves of 8 rows.  A half's codes go
+            // to a per-wave LDS tile ([row][group], padded) and leave it
+            // record by record, so each store instruction writes 1 KB
+            // contiguously (two records' 8-row halves: 8 full 128-byte
+            // lines); scattered 16-byte stores, one line per lane, cost
+            // half the bandwidth.  The 16 scale bytes of a lane's group are
+            // contiguous in its record and go out as one 16-byte store per
+            // unit.
+            __shared__ u32x4_t stg[kWavesPerBlock][8][kTileGroups + 1];
+            const uint32_t nrec = gpr / 4;
+            const uint32_t rec0 = static_cast<uint32_t>(p0) / 4;
+            const uint32_t grp = static_cast<uint32_t>(p0 + lane);
+            const uint32_t soff = (grp >> 2) * 64 + (grp & 3) * 16;
+            // store map: lane l carries row l % 8 of group (l / 8) % 4 of
+            // record 2 m + l / 32 of the super-tile column
+            const int st_row = lane & 7;
+            const int st_grp = (lane >> 3) & 3;
+            const int st_rec = lane >> 5;
+            for (int64_t unit = r0; unit < T; unit += 16 * rs) {
+                uint32_t spk[4] = {0u, 0u, 0u, 0u};
+                const auto crsrc = row_rsrc(a.codes + (unit >> 4) * nrec * 1024, nrec * 1024);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int k = 8 * hh + i;
+                        const int64_t r = unit + k;
+                        if (r < T) {
+                            const int64_t rn = k < 15 ? r + 1 : unit + 16 * rs;
+                            Rows& cur = (i & 1) ? bufB : bufA;
+                            Rows& nxt = (i & 1) ? bufA : bufB;
+                            if (rn < T) load_rows(nxt, rn);
+                            uint32_t word[kSub];
+                            uint32_t S;
+                            encode_row(cur, 0, r, word, S);
+                            stg[wave][i][lane] = u32x4_t{word[0], word[1], word[2], word[3]};
+                            spk[k / 4] |= S << (8 * (k % 4));
+                        }
+                    }
+                    const bool row_ok = unit + 8 * hh + st_row < T;
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        const int rec = 2 * m + st_rec;
+                        const u32x4_t v = stg[wave][st_row][4 * rec + st_grp];
+                        if (row_ok)
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                v, crsrc,
+                                (rec0 + static_cast<uint32_t>(rec)) * 1024 + static_cast<uint32_t>(st_grp) * 256 +
+                                    static_cast<uint32_t>(8 * hh + st_row) * 16,
+                                0, 0);
+                    }
+                }
+                const auto srsrc = row_rsrc(a.scales + (unit >> 4) * nrec * 64, nrec * 64);
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{spk[0], spk[1], spk[2], spk[3]}, srsrc, soff, 0, 0);
+            }
+        } else {
+            for (int64_t r = r0; r < T; r += 2 * rs) {
+                if (r + rs < T) load_rows(bufB, r + rs);
+                process_rows(bufA, r);
+                if (r + rs >= T) break;
+                if (r + 2 * rs < T) load_rows(bufA, r + 2 * rs);
+                process_rows(bufB, r + rs);
+            }
+        }
+    } else {
+        const int64_t step = kBatch * rs;
+        for (int64_t r = r0; r < T; r += 2 * step) {
+            if (r + step < T) load_rows(bufB, r + step);
+            process_rows(bufA, r);
+            if (r + step >= T) break;
+            if (r + 2 * step < T) load_rows(bufA, r + 2 * step);
+            process_rows(bufB, r + step);
+        }
     }
 }
 
@@ -470,7 +550,17 @@ static mxq_status launch(Args a, int64_t tokens, int64_t channels, hipStream_t s
     const int occ = occupancy_waves_per_cu<XT, MODE, LAM, YOUT, TILED>();
     Plan pl;
     constexpr int want = kWavesPerCuOf<XT, MODE, LAM>;
-    if (!make_plan(tokens, channels, device_cu_count(), occ < want ? occ : want, &pl)) return MXQ_ERR_SHAPE;
+    const int per_cu = occ < want ? occ : want;
+    const int cus = device_cu_count();
+    a.unit = 1;
+    if (TILED) {
+        // 16-row units when there are enough of them to fill the grid;
+        // short batches (decode) keep one row per unit, for parallelism.
+        const int64_t units = (tokens + 15) / 16;
+        const int64_t tcols = (channels / kGroup + kTileGroups - 1) / kTileGroups;
+        if (units * tcols >= static_cast<int64_t>(cus) * per_cu) a.unit = 16;
+    }
+    if (!make_plan(a.unit == 16 ? (tokens + 15) / 16 : tokens, channels, cus, per_cu, &pl)) return MXQ_ERR_SHAPE;
     a.tcols = pl.tcols;
     a.row_step = pl.row_step;
     a.waves = pl.waves;
@@ -507,6 +597,7 @@ static mxq_status rotate_impl(const void* x, int32_t x_dtype, int64_t tokens, in
     mxq_status s = check_common(x, x_dtype, tokens, channels, stride, false);
     if (s != MXQ_OK) return s;
     if (tiled && channels % 128) return MXQ_ERR_SHAPE;
+    if (tiled && scales && (reinterpret_cast<uintptr_t>(scales) % 16)) return MXQ_ERR_ALIGN;
     if (tokens == 0 || channels == 0) return MXQ_OK;
     if (!x || !r_hat || !codes || !scales) return MXQ_ERR_NULL;
     if (stride < channels) return MXQ_ERR_STRIDE;

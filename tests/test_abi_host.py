@@ -267,6 +267,7 @@ def test_tiled_entry_points_validation(lib):
     assert rqt(P, 0, 8, 128, 128, None, None, P, P, None) == NULL
     assert rqt(P, 0, 8, 128, 64, None, P, P, P, None) == STRIDE
     assert rqt(P, 0, 8, 128, 128, None, P, P_ODD, P, None) == ALIGN
+    assert rqt(P, 0, 8, 128, 128, None, P, P, ctypes.c_void_p(0x10004), None) == ALIGN
     assert rqt(None, 0, 0, 128, 128, None, None, None, None, None) == OK
 
 

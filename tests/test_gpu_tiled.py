@@ -145,3 +145,22 @@ def test_large_product_full_size_same_bits(dev):
     y_t = mxq.gemm_mxfp4_tiled(*mxq.tile_mxfp4(*a), *mxq.tile_mxfp4(*b), M, N, K, torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(y_t, y_row)
+
+
+@pytest.mark.parametrize("T,dtype,with_lam", [(5000, torch.bfloat16, False), (4700, torch.float16, True)])
+def test_rotate_quant_tiled_prefill_sizes(dev, T, dtype, with_lam):
+    """Batches long enough that the quantizer writes records a 16-row unit at
+    a time through LDS (a partial last unit included): the same bytes as the
+    repacked row-layout output."""
+    C = 14336
+    rng = np.random.default_rng(9400 + T)
+    x = W.random_activations(rng, T, C, dtype, scale=2.0).to(dev)
+    lam = torch.from_numpy(np.exp(0.5 * rng.standard_normal(C)).astype(np.float32)).to(dev) if with_lam else None
+    r = W.bf16_matrix(W.qr_orthogonal(rng)).to(dev)
+    ref = mxq.tile_mxfp4(*mxq.rotate_quant(x, r, lam))
+    nc, ns = mxq.tiled_sizes(T, C)
+    tc = torch.zeros(nc, dtype=torch.uint8, device=dev)
+    ts = torch.zeros(ns, dtype=torch.uint8, device=dev)
+    mxq.rotate_quant_tiled(x, r, lam, tcodes=tc, tscales=ts)
+    torch.cuda.synchronize()
+    assert torch.equal(tc, ref[0]) and torch.equal(ts, ref[1])
