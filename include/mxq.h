@@ -253,6 +253,18 @@ mxq_status mxq_gemm_mxfp4_tiled(const uint8_t *a_tcodes, const uint8_t *a_tscale
                                 const uint8_t *b_tscales, int64_t M, int64_t N, int64_t K, void *y,
                                 int32_t y_dtype, int64_t ldy, void *stream);
 
+/* mxq_norm_rotate_quant_tiled: mxq_norm_rotate_quant with its codes and
+ *   scales written in the tiled layout (bit-identical bytes, other
+ *   positions); channels must be a multiple of 128 (MXQ_ERR_SHAPE).  Each
+ *   row is stored on its own, which suits decode-sized batches; at prefill
+ *   sizes the row layout plus mxq_tile_mxfp4 moves fewer bytes.  The
+ *   padding rows of the last record row are not written.  Other rules as
+ *   mxq_norm_rotate_quant. */
+mxq_status mxq_norm_rotate_quant_tiled(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
+                                       int64_t x_row_stride, int32_t norm_kind, const float *gamma,
+                                       const float *beta, float eps, const float *lambda, const uint16_t *r_hat,
+                                       uint8_t *tiled_codes, uint8_t *tiled_scales, void *stream);
+
 /* ---- offline calibration of the shared block (DuQuant++ page sec. 3.2) ----
  * Greedy outlier-aware construction of the 32x32 block R_b, in fp64 as the
  * page advises (sec. 3 pitfalls, item 3), on the GPU.  Two calls:

@@ -26,7 +26,7 @@ EXPORTS = ("mxq_rotate_quant", "mxq_rotate_quant_ex", "mxq_quant", "mxq_dequant"
            "mxq_status_str", "mxq_plan", "mxq_version", "mxq_calib_workspace_bytes",
            "mxq_calib_worst_group", "mxq_calib_givens", "mxq_absorb_quant", "mxq_gemm_mxfp4",
            "mxq_norm_rotate_quant", "mxq_rotate_quant_block", "mxq_tile_mxfp4", "mxq_rotate_quant_tiled",
-           "mxq_gemm_mxfp4_tiled")
+           "mxq_gemm_mxfp4_tiled", "mxq_norm_rotate_quant_tiled")
 
 _lib = None
 
@@ -69,13 +69,15 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.mxq_gemm_mxfp4_tiled.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp]
     lib.mxq_tile_mxfp4.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     lib.mxq_rotate_quant_tiled.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
+    lib.mxq_norm_rotate_quant_tiled.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, ctypes.c_float, vp, vp, vp,
+                                                vp, vp]
     lib.mxq_rotate_quant_block.argtypes = [vp, i32, i64, i64, i64, vp, vp, i32, vp, vp, vp, vp]
     lib.mxq_norm_rotate_quant.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, ctypes.c_float, vp, vp, vp, vp,
                                           vp, vp]
     for f in ("mxq_rotate_quant", "mxq_rotate_quant_ex", "mxq_quant", "mxq_dequant", "mxq_plan",
               "mxq_version", "mxq_calib_worst_group", "mxq_calib_givens", "mxq_absorb_quant",
               "mxq_gemm_mxfp4", "mxq_norm_rotate_quant", "mxq_rotate_quant_block", "mxq_tile_mxfp4",
-              "mxq_rotate_quant_tiled", "mxq_gemm_mxfp4_tiled"):
+              "mxq_rotate_quant_tiled", "mxq_gemm_mxfp4_tiled", "mxq_norm_rotate_quant_tiled"):
         getattr(lib, f).restype = ctypes.c_int32
     if path is None:
         _lib = lib
@@ -268,16 +270,7 @@ def rotate_quant_block(x: torch.Tensor, r_block: torch.Tensor, lam: torch.Tensor
 NORM_KINDS = {"rms": 0, "layer": 1}
 
 
-def norm_rotate_quant(x: torch.Tensor, r_hat: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor | None = None,
-                      lam: torch.Tensor | None = None, *, norm: str = "rms", eps: float = 1e-5, codes=None,
-                      scales=None, y_rot=None, stream=None):
-    """codes, scales = MXFP4(((norm(x) * gamma + beta) / lam) @ BlockDiag(r_hat)).
-
-    norm is "rms" (RMSNorm) or "layer" (LayerNorm); x is the norm's bf16/fp16
-    input [tokens, channels <= 16384]; gamma, beta, lam are contiguous fp32
-    [channels] tensors on x's device (beta and lam may be None).
-    """
-    lib = load()
+def _check_norm_args(x, r_hat, gamma, beta, lam, norm):
     T, C, stride = _check_x(x, (torch.bfloat16, torch.float16))
     if r_hat.dtype != torch.bfloat16 or r_hat.shape != (32, 32) or not r_hat.is_contiguous() \
             or r_hat.device != x.device:
@@ -289,6 +282,20 @@ def norm_rotate_quant(x: torch.Tensor, r_hat: torch.Tensor, gamma: torch.Tensor,
             raise ValueError(f"{name} must be a contiguous fp32 [channels] tensor on x's device")
     if norm not in NORM_KINDS:
         raise ValueError(f"norm must be one of {sorted(NORM_KINDS)}")
+    return T, C, stride
+
+
+def norm_rotate_quant(x: torch.Tensor, r_hat: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor | None = None,
+                      lam: torch.Tensor | None = None, *, norm: str = "rms", eps: float = 1e-5, codes=None,
+                      scales=None, y_rot=None, stream=None):
+    """codes, scales = MXFP4(((norm(x) * gamma + beta) / lam) @ BlockDiag(r_hat)).
+
+    norm is "rms" (RMSNorm) or "layer" (LayerNorm); x is the norm's bf16/fp16
+    input [tokens, channels <= 16384]; gamma, beta, lam are contiguous fp32
+    [channels] tensors on x's device (beta and lam may be None).
+    """
+    lib = load()
+    T, C, stride = _check_norm_args(x, r_hat, gamma, beta, lam, norm)
     codes, scales = _outputs(x, T, C, codes, scales)
     if y_rot is not None and (y_rot.dtype != torch.float32 or y_rot.shape != (T, C) or not y_rot.is_contiguous()):
         raise ValueError("y_rot must be a contiguous fp32 [tokens, channels] tensor")
@@ -447,3 +454,19 @@ def gemm_mxfp4_tiled(a_tcodes: torch.Tensor, a_tscales: torch.Tensor, b_tcodes: 
     if st != 0:
         raise MXQError("mxq_gemm_mxfp4_tiled", st)
     return out
+
+
+def norm_rotate_quant_tiled(x: torch.Tensor, r_hat: torch.Tensor, gamma: torch.Tensor,
+                            beta: torch.Tensor | None = None, lam: torch.Tensor | None = None, *,
+                            norm: str = "rms", eps: float = 1e-5, tcodes=None, tscales=None, stream=None):
+    """:func:`norm_rotate_quant` with its output in the fragment-tiled
+    layout (channels % 128 == 0); the A operand of :func:`gemm_mxfp4_tiled`."""
+    lib = load()
+    T, C, stride = _check_norm_args(x, r_hat, gamma, beta, lam, norm)
+    tcodes, tscales = _tiled_outputs(x.device, T, C, tcodes, tscales)
+    st = lib.mxq_norm_rotate_quant_tiled(_ptr(x), _DT[x.dtype], T, C, stride, NORM_KINDS[norm], _ptr(gamma),
+                                         _ptr(beta), ctypes.c_float(eps), _ptr(lam), _ptr(r_hat), _ptr(tcodes),
+                                         _ptr(tscales), _stream(x, stream))
+    if st != 0:
+        raise MXQError("mxq_norm_rotate_quant_tiled", st)
+    return tcodes, tscales

@@ -69,7 +69,7 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
-template <int XT, int NORM, int NT, bool YOUT>
+template <int XT, int NORM, int NT, bool YOUT, bool TILED>
 __global__ __launch_bounds__(kBlockThreads) void norm_quant_kernel(NormArgs a) {
     constexpr bool kFp16 = XT == MXQ_FP16;
     constexpr int kUnits = NT * kSub * 2 * kWave;  // 16-byte factor units per table
@@ -195,8 +195,15 @@ __global__ __launch_bounds__(kBlockThreads) void norm_quant_kernel(NormArgs a) {
             for (int s = 0; s < kSub; ++s) asm volatile("" : "+v"(buf[st][s]));
 
         // ---- normalize, smooth, rotate, encode
-        const auto crsrc = row_rsrc(a.codes + r * a.gpr * 16, gpr * 16);
-        const auto srsrc = row_rsrc(a.scales + r * a.gpr, gpr);
+        // Row layout: the row's codes and scales.  Fragment-tiled layout
+        // (records of 16 rows x 4 groups): the row's record row; group g of
+        // row r is slot 16 (g % 4) + r % 16 of record g / 4.
+        const uint32_t nrec = gpr / 4;
+        const auto crsrc = TILED ? row_rsrc(a.codes + (r >> 4) * nrec * 1024, nrec * 1024)
+                                 : row_rsrc(a.codes + r * a.gpr * 16, gpr * 16);
+        const auto srsrc = TILED ? row_rsrc(a.scales + (r >> 4) * nrec * 64, nrec * 64)
+                                 : row_rsrc(a.scales + r * a.gpr, gpr);
+        const uint32_t r16 = static_cast<uint32_t>(r & 15);
 #pragma unroll
         for (int st = 0; st < NT; ++st) {
             uint32_t word[kSub];
@@ -253,9 +260,10 @@ __global__ __launch_bounds__(kBlockThreads) void norm_quant_kernel(NormArgs a) {
             transpose_words(word);
             const uint32_t S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
             const uint32_t g = static_cast<uint32_t>(kTileGroups * st + lane);
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{word[0], word[1], word[2], word[3]}, crsrc, g * 16, 0,
-                                                   kAuxNT);
-            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, g, 0, 0);
+            const uint32_t slot = TILED ? (g >> 2) * 64 + (g & 3) * 16 + r16 : g;
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{word[0], word[1], word[2], word[3]}, crsrc, slot * 16, 0,
+                                                   TILED ? 0 : kAuxNT);
+            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, slot, 0, 0);
         }
         if constexpr (kDouble) {
 #pragma unroll
@@ -271,61 +279,56 @@ __global__ __launch_bounds__(kBlockThreads) void norm_quant_kernel(NormArgs a) {
 bool aligned_to(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 // Resident blocks per CU the instance allows (registers, LDS), queried once.
-template <int XT, int NORM, int NT, bool YOUT>
+template <int XT, int NORM, int NT, bool YOUT, bool TILED>
 int blocks_per_cu() {
     static std::atomic<int> cached{0};
     int v = cached.load(std::memory_order_relaxed);
     if (v > 0) return v;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, norm_quant_kernel<XT, NORM, NT, YOUT>, kBlockThreads, 0) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, norm_quant_kernel<XT, NORM, NT, YOUT, TILED>, kBlockThreads,
+                                                     0) != hipSuccess ||
         v <= 0)
         v = 1;
     cached.store(v, std::memory_order_relaxed);
     return v;
 }
 
-template <int XT, int NORM, int NT, bool YOUT>
+template <int XT, int NORM, int NT, bool YOUT, bool TILED>
 mxq_status launch_nt(NormArgs a, hipStream_t st) {
-    const int per_cu = blocks_per_cu<XT, NORM, NT, YOUT>();
+    const int per_cu = blocks_per_cu<XT, NORM, NT, YOUT, TILED>();
     const int64_t want = (static_cast<int64_t>(a.tokens) + kBlockWaves - 1) / kBlockWaves;
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
     const int blocks = static_cast<int>(want < cap ? want : cap);
     a.waves = blocks * kBlockWaves;
-    hipLaunchKernelGGL((norm_quant_kernel<XT, NORM, NT, YOUT>), dim3(blocks), dim3(kBlockThreads), 0, st, a);
+    hipLaunchKernelGGL((norm_quant_kernel<XT, NORM, NT, YOUT, TILED>), dim3(blocks), dim3(kBlockThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 
-template <int XT, int NORM, bool YOUT>
+template <int XT, int NORM, bool YOUT, bool TILED>
 mxq_status launch_tiles(const NormArgs& a, hipStream_t st) {
     const int tiles = (a.gpr + kTileGroups - 1) / kTileGroups;
-    if (tiles <= 1) return launch_nt<XT, NORM, 1, YOUT>(a, st);
-    if (tiles <= 2) return launch_nt<XT, NORM, 2, YOUT>(a, st);
-    if (tiles <= 4) return launch_nt<XT, NORM, 4, YOUT>(a, st);
-    return launch_nt<XT, NORM, 8, YOUT>(a, st);
+    if (tiles <= 1) return launch_nt<XT, NORM, 1, YOUT, TILED>(a, st);
+    if (tiles <= 2) return launch_nt<XT, NORM, 2, YOUT, TILED>(a, st);
+    if (tiles <= 4) return launch_nt<XT, NORM, 4, YOUT, TILED>(a, st);
+    return launch_nt<XT, NORM, 8, YOUT, TILED>(a, st);
 }
 
 // The rotated-value output is a template parameter: a runtime branch around
 // its stores would cut the unrolled sub-tiles into separate basic blocks
 // that the scheduler cannot interleave.
 template <int XT, int NORM>
-mxq_status launch_norm(const NormArgs& a, hipStream_t st) {
-    return a.y ? launch_tiles<XT, NORM, true>(a, st) : launch_tiles<XT, NORM, false>(a, st);
+mxq_status launch_norm(const NormArgs& a, hipStream_t st, bool tiled) {
+    if (tiled) return launch_tiles<XT, NORM, false, true>(a, st);
+    return a.y ? launch_tiles<XT, NORM, true, false>(a, st) : launch_tiles<XT, NORM, false, false>(a, st);
 }
 
-}  // namespace norm
-}  // namespace mxq
-
-using namespace mxq::norm;
-
-extern "C" mxq_status mxq_norm_rotate_quant(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels,
-                                            int64_t x_row_stride, int32_t norm_kind, const float* gamma,
-                                            const float* beta, float eps, const float* lambda,
-                                            const uint16_t* r_hat, uint8_t* codes, uint8_t* scales, float* y_rot,
-                                            void* stream) {
+mxq_status norm_impl(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels, int64_t x_row_stride,
+                     int32_t norm_kind, const float* gamma, const float* beta, float eps, const float* lambda,
+                     const uint16_t* r_hat, uint8_t* codes, uint8_t* scales, float* y_rot, void* stream,
+                     bool tiled) {
     if (x_dtype != MXQ_BF16 && x_dtype != MXQ_FP16) return MXQ_ERR_DTYPE;
     if (norm_kind != MXQ_NORM_RMS && norm_kind != MXQ_NORM_LAYER) return MXQ_ERR_DTYPE;
     if (tokens < 0 || channels < 0 || channels % kGroup || channels > kMaxTiles * kTileGroups * kGroup ||
-        tokens >= (int64_t(1) << 31))
+        tokens >= (int64_t(1) << 31) || (tiled && channels % 128))
         return MXQ_ERR_SHAPE;
     if (!(eps >= 0.0f) || eps > 3.0e38f) return MXQ_ERR_SHAPE;
     if (tokens == 0 || channels == 0) return MXQ_OK;
@@ -340,6 +343,31 @@ extern "C" mxq_status mxq_norm_rotate_quant(const void* x, int32_t x_dtype, int6
                static_cast<int32_t>(channels / kGroup), 0};
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (x_dtype == MXQ_BF16)
-        return norm_kind == MXQ_NORM_RMS ? launch_norm<MXQ_BF16, kRms>(a, st) : launch_norm<MXQ_BF16, kLayer>(a, st);
-    return norm_kind == MXQ_NORM_RMS ? launch_norm<MXQ_FP16, kRms>(a, st) : launch_norm<MXQ_FP16, kLayer>(a, st);
+        return norm_kind == MXQ_NORM_RMS ? launch_norm<MXQ_BF16, kRms>(a, st, tiled)
+                                         : launch_norm<MXQ_BF16, kLayer>(a, st, tiled);
+    return norm_kind == MXQ_NORM_RMS ? launch_norm<MXQ_FP16, kRms>(a, st, tiled)
+                                     : launch_norm<MXQ_FP16, kLayer>(a, st, tiled);
+}
+
+}  // namespace norm
+}  // namespace mxq
+
+using namespace mxq::norm;
+
+extern "C" mxq_status mxq_norm_rotate_quant(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels,
+                                            int64_t x_row_stride, int32_t norm_kind, const float* gamma,
+                                            const float* beta, float eps, const float* lambda,
+                                            const uint16_t* r_hat, uint8_t* codes, uint8_t* scales, float* y_rot,
+                                            void* stream) {
+    return norm_impl(x, x_dtype, tokens, channels, x_row_stride, norm_kind, gamma, beta, eps, lambda, r_hat, codes,
+                     scales, y_rot, stream, false);
+}
+
+extern "C" mxq_status mxq_norm_rotate_quant_tiled(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels,
+                                                  int64_t x_row_stride, int32_t norm_kind, const float* gamma,
+                                                  const float* beta, float eps, const float* lambda,
+                                                  const uint16_t* r_hat, uint8_t* tiled_codes,
+                                                  uint8_t* tiled_scales, void* stream) {
+    return norm_impl(x, x_dtype, tokens, channels, x_row_stride, norm_kind, gamma, beta, eps, lambda, r_hat,
+                     tiled_codes, tiled_scales, nullptr, stream, true);
 }

@@ -276,3 +276,17 @@ def test_tiled_sizes():
     assert mxq.tiled_sizes(17, 256) == (32 * 128, 32 * 8)
     with pytest.raises(ValueError):
         mxq.tiled_sizes(4, 96)
+
+
+def test_norm_tiled_validation(lib):
+    def nqt(x=P, dt=0, T=8, C=128, stride=128, kind=0, g=P, b=None, eps=1e-5, lam=None, r=P, codes=P, scales=P):
+        return lib.mxq_norm_rotate_quant_tiled(x, dt, T, C, stride, kind, g, b, ctypes.c_float(eps), lam, r, codes,
+                                               scales, None)
+    assert nqt(C=96, stride=96) == SHAPE      # tiled output needs channels % 128 == 0
+    assert nqt(dt=2) == DTYPE
+    assert nqt(kind=5) == DTYPE
+    assert nqt(eps=-1.0) == SHAPE
+    assert nqt(g=None) == NULL
+    assert nqt(stride=64) == STRIDE
+    assert nqt(codes=P_ODD) == ALIGN
+    assert nqt(T=0, x=None, g=None, r=None, codes=None, scales=None) == OK

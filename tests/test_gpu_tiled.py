@@ -164,3 +164,43 @@ def test_rotate_quant_tiled_prefill_sizes(dev, T, dtype, with_lam):
     mxq.rotate_quant_tiled(x, r, lam, tcodes=tc, tscales=ts)
     torch.cuda.synchronize()
     assert torch.equal(tc, ref[0]) and torch.equal(ts, ref[1])
+
+
+@pytest.mark.parametrize("T,C", [(1, 128), (16, 4096), (37, 2432), (300, 4096)])
+@pytest.mark.parametrize("norm,dtype,with_beta,with_lam", [("rms", torch.bfloat16, False, True),
+                                                           ("layer", torch.float16, True, True),
+                                                           ("rms", torch.float16, False, False)])
+def test_norm_rotate_quant_tiled_same_bytes(dev, T, C, norm, dtype, with_beta, with_lam):
+    rng = np.random.default_rng(9500 + T + C // 128)
+    x = W.random_activations(rng, T, C, dtype, scale=2.0).to(dev)
+    gamma = torch.from_numpy(rng.uniform(0.5, 1.5, C).astype(np.float32)).to(dev)
+    beta = torch.from_numpy(rng.normal(0, 0.1, C).astype(np.float32)).to(dev) if with_beta else None
+    lam = torch.from_numpy(np.exp(0.5 * rng.standard_normal(C)).astype(np.float32)).to(dev) if with_lam else None
+    r = W.bf16_matrix(W.qr_orthogonal(rng)).to(dev)
+    ref = mxq.tile_mxfp4(*mxq.norm_rotate_quant(x, r, gamma, beta, lam, norm=norm))
+    nc, ns = mxq.tiled_sizes(T, C)
+    tc = torch.zeros(nc, dtype=torch.uint8, device=dev)
+    ts = torch.zeros(ns, dtype=torch.uint8, device=dev)
+    mxq.norm_rotate_quant_tiled(x, r, gamma, beta, lam, norm=norm, tcodes=tc, tscales=ts)
+    torch.cuda.synchronize()
+    assert torch.equal(tc, ref[0]) and torch.equal(ts, ref[1])
+
+
+def test_decode_qkv_pipeline(dev):
+    """RMSNorm + rotate + quantize 16 tokens straight into records, times
+    absorbed 4096 x 4096 weights in records: the same bits as the row-layout
+    pipeline."""
+    nw = W.norm_workload()
+    r = nw.r_hat.to(dev)
+    lam = torch.from_numpy(nw.lam).to(dev)
+    gamma = torch.from_numpy(nw.gamma).to(dev)
+    x16 = nw.x[:16].contiguous().to(dev)
+    C = nw.x.shape[1]
+    w = W.linear_weights(4096, C)
+    bc, bsc = mxq.absorb_quant(w.to(dev), r, lam)
+    ac, asc = mxq.norm_rotate_quant(x16, r, gamma, None, lam, eps=nw.eps)
+    y_row = mxq.gemm_mxfp4(ac, asc, bc, bsc, torch.bfloat16)
+    ta = mxq.norm_rotate_quant_tiled(x16, r, gamma, None, lam, eps=nw.eps)
+    y_t = mxq.gemm_mxfp4_tiled(*ta, *mxq.tile_mxfp4(bc, bsc), 16, 4096, C, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y_t, y_row)
