@@ -41,8 +41,13 @@ constexpr int kWave = 64;
 constexpr int kGroup = 32;
 constexpr int kSub = 4;            // sub-tiles of 16 groups per super-tile
 constexpr int kTileGroups = 64;    // groups per super-tile
-constexpr int kBlockWaves = 4;
-constexpr int kBlockThreads = kWave * kBlockWaves;
+// Waves per block.  Every block builds the factor tables once, so long
+// batches take blocks as large as the row buffers' registers allow (16
+// waves leave 128 VGPRs per lane, 8 waves 256); short batches take 4-wave
+// blocks, which spread their rows over more CUs.
+template <int NT>
+constexpr int kBigBlockWaves = NT <= 2 ? 16 : (NT == 4 ? 8 : 4);
+constexpr int kSmallBlockWaves = 4;
 constexpr int kMaxTiles = 8;       // channels <= 16384
 enum : int { kRms = 0, kLayer = 1 };
 
@@ -69,8 +74,10 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
-template <int XT, int NORM, int NT, bool YOUT, bool TILED>
-__global__ __launch_bounds__(kBlockThreads) void norm_quant_kernel(NormArgs a) {
+template <int XT, int NORM, int NT, bool YOUT, bool TILED, int BW>
+__global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
+    constexpr int kBlockWaves = BW;
+    constexpr int kBlockThreads = kWave * BW;
     constexpr bool kFp16 = XT == MXQ_FP16;
     constexpr int kUnits = NT * kSub * 2 * kWave;  // 16-byte factor units per table
     // Per-channel factors in the order the lanes consume them: unit
@@ -279,12 +286,12 @@ __global__ __launch_bounds__(kBlockThreads) void norm_quant_kernel(NormArgs a) {
 bool aligned_to(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
 // Resident blocks per CU the instance allows (registers, LDS), queried once.
-template <int XT, int NORM, int NT, bool YOUT, bool TILED>
+template <int XT, int NORM, int NT, bool YOUT, bool TILED, int BW>
 int blocks_per_cu() {
     static std::atomic<int> cached{0};
     int v = cached.load(std::memory_order_relaxed);
     if (v > 0) return v;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, norm_quant_kernel<XT, NORM, NT, YOUT, TILED>, kBlockThreads,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, norm_quant_kernel<XT, NORM, NT, YOUT, TILED, BW>, kWave * BW,
                                                      0) != hipSuccess ||
         v <= 0)
         v = 1;
@@ -292,15 +299,28 @@ int blocks_per_cu() {
     return v;
 }
 
-template <int XT, int NORM, int NT, bool YOUT, bool TILED>
-mxq_status launch_nt(NormArgs a, hipStream_t st) {
-    const int per_cu = blocks_per_cu<XT, NORM, NT, YOUT, TILED>();
+template <int XT, int NORM, int NT, bool YOUT, bool TILED, int BW>
+mxq_status launch_bw(NormArgs a, hipStream_t st) {
+    constexpr int kBlockWaves = BW;
+    const int per_cu = blocks_per_cu<XT, NORM, NT, YOUT, TILED, BW>();
     const int64_t want = (static_cast<int64_t>(a.tokens) + kBlockWaves - 1) / kBlockWaves;
     const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
     const int blocks = static_cast<int>(want < cap ? want : cap);
     a.waves = blocks * kBlockWaves;
-    hipLaunchKernelGGL((norm_quant_kernel<XT, NORM, NT, YOUT, TILED>), dim3(blocks), dim3(kBlockThreads), 0, st, a);
+    hipLaunchKernelGGL((norm_quant_kernel<XT, NORM, NT, YOUT, TILED, BW>), dim3(blocks), dim3(kWave * BW), 0, st, a);
     return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+}
+
+template <int XT, int NORM, int NT, bool YOUT, bool TILED>
+mxq_status launch_nt(const NormArgs& a, hipStream_t st) {
+    constexpr int kBig = kBigBlockWaves<NT>;
+    if constexpr (kBig == kSmallBlockWaves) {
+        return launch_bw<XT, NORM, NT, YOUT, TILED, kBig>(a, st);
+    } else {
+        if (a.tokens >= static_cast<int64_t>(device_cu_count()) * kBig)
+            return launch_bw<XT, NORM, NT, YOUT, TILED, kBig>(a, st);
+        return launch_bw<XT, NORM, NT, YOUT, TILED, kSmallBlockWaves>(a, st);
+    }
 }
 
 template <int XT, int NORM, bool YOUT, bool TILED>

@@ -116,3 +116,13 @@ def test_norm_bench_workload_sampled(dev, orc):
     check_rotated_values(y[rows], y_ref, norms)
     stats = check_against_oracle(codes[rows], scales[rows], c_ref, s_ref, lambda rr: y_ref[rr], norms)
     print(f"  bench workload, 256 sampled rows: {stats}", flush=True)
+
+
+@pytest.mark.parametrize("norm", ["rms", "layer"])
+def test_norm_block_sizes_same_bits(dev, norm):
+    """Long batches run in 16-wave blocks, short ones in 4-wave blocks: the
+    rows come out the same either way."""
+    wl = W.norm_workload(4608, 4096, seed=4205, with_beta=(norm == "layer"))
+    full = run_gpu(wl.x, wl.r_hat, wl.gamma, wl.beta, wl.lam, norm, wl.eps, dev, want_y=False)
+    part = run_gpu(wl.x[:300].contiguous(), wl.r_hat, wl.gamma, wl.beta, wl.lam, norm, wl.eps, dev, want_y=False)
+    assert np.array_equal(full[0][:300], part[0]) and np.array_equal(full[1][:300], part[1])
