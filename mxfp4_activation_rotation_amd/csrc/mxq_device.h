@@ -107,8 +107,17 @@ __device__ __forceinline__ void widen4_f32(u32x4_t q, float* f) {
 // Buffer resource for `bytes` bytes at `base` (raw buffer, stride 0): loads
 // beyond `bytes` return zero and stores beyond it are dropped, which is how
 // lanes of groups past the end of a row are handled without branches.
+// base and bytes must be the same in every lane of the wave (a resource
+// lives in scalar registers); they are read from the first active lane.
+// Without that the compiler, which cannot always prove a row address
+// uniform through 64-bit index arithmetic, wraps every buffer access in a
+// loop over the distinct values.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(p & 0xffffffffu)));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(p >> 32)));
+    void* u = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(u, 0, __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)), 0x00020000);
 }
 
 constexpr int kAuxNT = 2;  // cache policy bits of buffer ops: non-temporal

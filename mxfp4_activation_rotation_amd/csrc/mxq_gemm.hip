@@ -104,8 +104,16 @@ struct ScaleChunk {
     uint8_t b[kScaleChunk];
 };
 
+// Buffer resource over [base, base + bytes); base and bytes are the same in
+// every lane (a resource lives in scalar registers) and are read from the
+// first active lane, so the compiler never wraps an access in a loop over
+// distinct descriptors.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(p & 0xffffffffu)));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(p >> 32)));
+    void* u = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(u, 0, __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)), 0x00020000);
 }
 
 __device__ __forceinline__ i32x8_t operand(const u32x4g_t& c) {
