@@ -68,7 +68,7 @@
 #define MXQ_NT_SCALE 0
 #endif
 #ifndef MXQ_WAVES_PER_BLOCK
-#define MXQ_WAVES_PER_BLOCK 4
+#define MXQ_WAVES_PER_BLOCK 8
 #endif
 #ifndef MXQ_DEQUANT_WAVES_PER_CU
 #define MXQ_DEQUANT_WAVES_PER_CU 16
