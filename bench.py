@@ -392,6 +392,9 @@ def main():
                          "random Hadamard block of this size instead of the workload's 32-wide block")
     ap.add_argument("--tiled", action="store_true",
                     help="quantizer output in the fragment-tiled layout (the tiled product's A operand)")
+    ap.add_argument("--op", default="rotate", choices=["rotate", "quant", "dequant"],
+                    help="rotate: mxq_rotate_quant (the headline); quant: mxq_quant (no smoothing, no "
+                         "rotation); dequant: mxq_dequant of the batch's codes to bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -447,11 +450,21 @@ def main():
     else:
         outs = [(torch.empty((call_tokens, C // 2), dtype=torch.uint8, device=dev),
                  torch.empty((call_tokens, C // 32), dtype=torch.uint8, device=dev)) for _ in range(n_buf)]
+    if args.op == "dequant":
+        # codes and scales of every buffer set, decoded to bf16 (2.53125 B/elem moved as well:
+        # 0.53125 read, 2 written)
+        for i in range(n_buf):
+            mxq.rotate_quant(xs[i], r, lam, codes=outs[i][0], scales=outs[i][1])
+        ys = [torch.empty((call_tokens, C), dtype=torch.bfloat16, device=dev) for _ in range(n_buf)]
     torch.cuda.synchronize()
 
     def step(i):
         c, s = outs[i % n_buf]
-        if args.block:
+        if args.op == "quant":
+            mxq.quant(xs[i % n_buf], codes=c, scales=s)
+        elif args.op == "dequant":
+            mxq.dequant(c, s, torch.bfloat16, out=ys[i % n_buf])
+        elif args.block:
             mxq.rotate_quant_block(xs[i % n_buf], r, lam, codes=c, scales=s)
         elif args.tiled:
             mxq.rotate_quant_tiled(xs[i % n_buf], r, lam, tcodes=c, tscales=s)
@@ -494,7 +507,7 @@ def main():
 
     achieved = step_bytes / mean_launch_s / 1e9
     value = elems * args.steps / wall / 1e9
-    hbm = None if (args.block or args.tiled) else read_counters(args.workload)
+    hbm = None if (args.block or args.tiled or args.op != "rotate") else read_counters(args.workload)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -540,7 +553,12 @@ def main():
     if args.block:
         result["kernel_source_hash"] = kernel_source_hash(("mxfp4_activation_rotation_amd/csrc/mxq_block.hip",
                                                            "mxfp4_activation_rotation_amd/csrc/mxq_device.h"))
-    if not args.no_cpu_baseline and not args.block:
+    if args.op != "rotate":
+        result["metric"] = ("plain MXFP4 quantization (mxq_quant) throughput: Gelem/s" if args.op == "quant"
+                            else "MXFP4 dequantization to bf16 (mxq_dequant) throughput: Gelem/s")
+        result["config"]["op"] = args.op
+        result["kernel_source_hash"] = kernel_source_hash()
+    if not args.no_cpu_baseline and not args.block and args.op == "rotate":
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

@@ -67,11 +67,17 @@
 #ifndef MXQ_NT_SCALE
 #define MXQ_NT_SCALE 0
 #endif
+// Waves per block of the quantize kernels: the plan's waves (7 per CU on the
+// headline shape) then land as one block per CU rather than as one or two
+// 4-wave blocks.
 #ifndef MXQ_WAVES_PER_BLOCK
 #define MXQ_WAVES_PER_BLOCK 8
 #endif
 #ifndef MXQ_DEQUANT_WAVES_PER_CU
 #define MXQ_DEQUANT_WAVES_PER_CU 16
+#endif
+#ifndef MXQ_DEQUANT_WAVES_PER_BLOCK
+#define MXQ_DEQUANT_WAVES_PER_BLOCK 4
 #endif
 #ifndef MXQ_DEQUANT_UNROLL
 #define MXQ_DEQUANT_UNROLL 16
@@ -403,17 +409,19 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
 // in bf16, so fp32 output is the bf16 result widened.  (The fp32-output form
 // of the converter is not used: this compiler folds its second result into
 // the first.)
+constexpr int kDequantWaves = MXQ_DEQUANT_WAVES_PER_BLOCK;
+
 template <bool OUT_BF16>
-__global__ __launch_bounds__(kBlockThreads) void dequant_kernel(const uint8_t* codes, const uint8_t* scales,
-                                                               void* y, int64_t elems) {
+__global__ __launch_bounds__(kWave * kDequantWaves) void dequant_kernel(const uint8_t* codes, const uint8_t* scales,
+                                                                       void* y, int64_t elems) {
     constexpr int kPerLane = OUT_BF16 ? 8 : 4;
     constexpr int64_t kChunk = kWave * kPerLane;              // elements per wave store
     constexpr int kUnroll = MXQ_DEQUANT_UNROLL;               // chunks per wave iteration
     constexpr uint32_t osz = OUT_BF16 ? 2 : 4;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock +
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * kDequantWaves +
                          __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-    const int64_t waves = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+    const int64_t waves = static_cast<int64_t>(gridDim.x) * kDequantWaves;
     const uint32_t first = static_cast<uint32_t>(lane * kPerLane);  // lane's first element in a chunk
     for (int64_t base = wave * kUnroll * kChunk; base < elems; base += waves * kUnroll * kChunk) {
         const int64_t rem = elems - base;
@@ -698,16 +706,16 @@ mxq_status mxq_dequant(const uint8_t* codes, const uint8_t* scales, int64_t toke
     const int64_t elems = tokens * channels;
     const int64_t per_wave = (y_dtype == MXQ_BF16 ? 8 : 4) * kWave * MXQ_DEQUANT_UNROLL;
     const int64_t chunks = (elems + per_wave - 1) / per_wave;
-    int64_t blocks = (chunks + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t cap = static_cast<int64_t>(device_cu_count()) * (MXQ_DEQUANT_WAVES_PER_CU / kWavesPerBlock);
+    int64_t blocks = (chunks + kDequantWaves - 1) / kDequantWaves;
+    const int64_t cap = static_cast<int64_t>(device_cu_count()) * (MXQ_DEQUANT_WAVES_PER_CU / kDequantWaves);
     if (blocks > cap) blocks = cap;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (y_dtype == MXQ_BF16)
-        hipLaunchKernelGGL((dequant_kernel<true>), dim3(static_cast<unsigned>(blocks)), dim3(kBlockThreads), 0, st,
-                           codes, scales, y, elems);
+        hipLaunchKernelGGL((dequant_kernel<true>), dim3(static_cast<unsigned>(blocks)), dim3(kWave * kDequantWaves), 0,
+                           st, codes, scales, y, elems);
     else
-        hipLaunchKernelGGL((dequant_kernel<false>), dim3(static_cast<unsigned>(blocks)), dim3(kBlockThreads), 0, st,
-                           codes, scales, y, elems);
+        hipLaunchKernelGGL((dequant_kernel<false>), dim3(static_cast<unsigned>(blocks)), dim3(kWave * kDequantWaves), 0,
+                           st, codes, scales, y, elems);
     return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 
