@@ -204,3 +204,23 @@ def test_decode_qkv_pipeline(dev):
     y_t = mxq.gemm_mxfp4_tiled(*ta, *mxq.tile_mxfp4(bc, bsc), 16, 4096, C, torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(y_t, y_row)
+
+
+def test_tiled_outputs_from_strided_rows(dev):
+    """Rows of x with a pitch larger than the row (a column slice of a wider
+    tensor) give the same records as the contiguous copy."""
+    rng = np.random.default_rng(9600)
+    wide = W.random_activations(rng, 40, 3 * 1024, torch.bfloat16, scale=2.0).to(dev)
+    x = wide[:, 512:512 + 2048]
+    assert x.stride(0) == 3 * 1024
+    r = W.bf16_matrix(W.qr_orthogonal(rng)).to(dev)
+    gamma = torch.from_numpy(rng.uniform(0.5, 1.5, 2048).astype(np.float32)).to(dev)
+    T, C = x.shape
+    for fn in (lambda t: mxq.rotate_quant_tiled(t, r), lambda t: mxq.norm_rotate_quant_tiled(t, r, gamma)):
+        a = fn(x)
+        b = fn(x.contiguous())
+        torch.cuda.synchronize()
+        # the padding rows of the last record row are not written: compare the 40 real rows
+        ua = O.untile_mxfp4(a[0].cpu().numpy(), a[1].cpu().numpy(), T, C)
+        ub = O.untile_mxfp4(b[0].cpu().numpy(), b[1].cpu().numpy(), T, C)
+        assert np.array_equal(ua[0], ub[0]) and np.array_equal(ua[1], ub[1])
