@@ -28,7 +28,8 @@
 // advances 128 positions per stage through a 4-deep LDS ring filled three
 // stages ahead by buffer loads with the lds modifier (no staging registers),
 // with one bare s_barrier per stage; scales travel in a 3-chunk ring of 4
-// stages each.  In LDS every fragment sits in a 1 KB slot read by a
+// stages each.  The operands of the next stage are read from LDS between
+// the MFMAs of the current one (software pipelining in registers).  In LDS every fragment sits in a 1 KB slot read by a
 // conflict-free ds_read_b128.  Global loads go through buffer resources
 // bounded to the tile's rows (or records), so rows past M or N read as zero
 // (codes 0, scale 2^-127: products 0) and ragged edges need no branches.
@@ -261,40 +262,39 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
                                   : 16 * static_cast<uint32_t>(4 * (lane & 15) + (((lane >> 4) + ((lane & 15) >> 2)) & 3));
     const uint32_t sl = TILED ? static_cast<uint32_t>(lane)
                               : static_cast<uint32_t>((lane & 15) * kChunkRowBytes + (lane >> 4));
-    auto compute = [&](int kt) {
+    // Operand registers: A fragment f is refilled with the next stage's as
+    // soon as its last MFMA of the current stage has issued; B has two sets
+    // that alternate between stages.
+    u32x4g_t aop[kFragM], bop0[kFragN], bop1[kFragN];
+    int sa[kFragM], sb0[kFragN], sb1[kFragN];
+    auto read_a = [&](int kt, int f) {
         const Stage& S = st[kt % kNst];
         const ScaleChunk& C = sc[(kt / kChunkStages) % kChunks];
         const uint32_t sq = (TILED ? 64 : 4) * static_cast<uint32_t>(kt % kChunkStages);
-        // Every operand of the stage is read before the first MFMA issues
-        // (the scheduling barrier keeps the compiler from sinking the reads
-        // next to their uses): one LDS round trip per stage.
-        u32x4g_t bop[kFragN], aop[kFragM];
-        int sb[kFragN], sa[kFragM];
-#pragma unroll
-        for (int j = 0; j < kFragN; ++j) {
-            bop[j] = *reinterpret_cast<const u32x4g_t*>(S.b + (wn * kFragN + j) * 1024 + op_off);
-            sb[j] = C.b[(wn * kFragN + j) * 16 * kChunkRowBytes + sl + sq];
-        }
-#pragma unroll
-        for (int f = 0; f < kFragM; ++f) {
-            aop[f] = *reinterpret_cast<const u32x4g_t*>(S.a + (wm * kFragM + f) * 1024 + op_off);
-            sa[f] = C.a[(wm * kFragM + f) * 16 * kChunkRowBytes + sl + sq];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int f = 0; f < kFragM; ++f)
-#pragma unroll
-            for (int j = 0; j < kFragN; ++j)
-                acc[f][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    operand(aop[f]), operand(bop[j]), acc[f][j], kFmtE2M1, kFmtE2M1, 0, sa[f], 0, sb[j]);
+        aop[f] = *reinterpret_cast<const u32x4g_t*>(S.a + (wm * kFragM + f) * 1024 + op_off);
+        sa[f] = C.a[(wm * kFragM + f) * 16 * kChunkRowBytes + sl + sq];
+    };
+    auto read_b = [&](int kt, int j, u32x4g_t* bop, int* sb) {
+        const Stage& S = st[kt % kNst];
+        const ScaleChunk& C = sc[(kt / kChunkStages) % kChunks];
+        const uint32_t sq = (TILED ? 64 : 4) * static_cast<uint32_t>(kt % kChunkStages);
+        bop[j] = *reinterpret_cast<const u32x4g_t*>(S.b + (wn * kFragN + j) * 1024 + op_off);
+        sb[j] = C.b[(wn * kFragN + j) * 16 * kChunkRowBytes + sl + sq];
     };
 
-    // Pipeline: stage kt + kAhead is loaded into the ring slot that stage
-    // kt - 1 used, right after the barrier that ends its reads, and stage kt
-    // then computes while the loads of the next kAhead stages are in flight.
-    // Before the barrier each wave waits for its own loads of stage kt: all
-    // but the (at most kAhead - 1) later stages it has issued (vmcnt counts
-    // this wave's direct loads, which complete in order).
+    // Pipeline.  Stage kt + kAhead is loaded into the ring slot that stage
+    // kt - 1 used, and the operands of stage kt + 1 are read while stage kt
+    // computes.  Before the barrier of step kt each wave waits for its own
+    // loads of stage kt + 1: all but the (at most kAhead - 2) later stages it
+    // has issued (vmcnt counts this wave's direct loads, which complete in
+    // order).  After the barrier stage kt + 1 is in LDS for every wave, and
+    // every wave's reads of stage kt - 1 have returned (its MFMAs consumed
+    // them in step kt - 1), so that slot can be refilled.  The barrier is a
+    // bare s_barrier: __syncthreads() would add a workgroup fence, which
+    // waits for every outstanding direct load (vmcnt(0)) and so would drain
+    // the stages in flight; the "memory" clobber keeps the compiler from
+    // moving LDS accesses across it.
+    static_assert(kAhead >= 2, "stage kt + 1 is read during step kt");
     const int nk = g.K / kStageK;
     if (nk > 0) {
         // scale chunk 0 whole, then the first kAhead stages
@@ -304,17 +304,37 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int s0 = 0; s0 < kAhead; ++s0)
         if (s0 < nk) load(s0, s0);
-    for (int kt = 0; kt < nk; ++kt) {
-        const int later = min(kAhead - 1, nk - 1 - kt);  // stages issued after kt
-        wait_stage_loads(later);
-        // A bare s_barrier: __syncthreads() would add a workgroup fence,
-        // which waits for every outstanding direct load (vmcnt(0)) and so
-        // would drain the stages in flight.  The "memory" clobber keeps the
-        // compiler from moving LDS accesses across it; the LDS reads of
-        // stage kt - 1 have all returned (their MFMAs consumed them).
+    auto step = [&](int kt, const u32x4g_t* cb, const int* csb, u32x4g_t* nb, int* nsb) {
+        if (kt + 1 < nk) wait_stage_loads(min(kAhead - 2, nk - 2 - kt));
         asm volatile("s_barrier" ::: "memory");
         if (kt + kAhead < nk) load(kt + kAhead, (kt + kAhead) % kNst);
-        compute(kt);
+        // The scheduling barriers pin the order: four MFMAs of fragment row
+        // f, then the reads that refill its registers (and one B fragment).
+        // The reads are unconditional, so the step stays one basic block; in
+        // the last step they read an in-bounds slot whose values go unused.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int f = 0; f < kFragM; ++f) {
+#pragma unroll
+            for (int j = 0; j < kFragN; ++j)
+                acc[f][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    operand(aop[f]), operand(cb[j]), acc[f][j], kFmtE2M1, kFmtE2M1, 0, sa[f], 0, csb[j]);
+            read_a(kt + 1, f);
+            if (f < kFragN) read_b(kt + 1, f, nb, nsb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    if (nk > 0) {
+        wait_stage_loads(min(kAhead - 1, nk - 1));
+        asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+        for (int f = 0; f < kFragM; ++f) read_a(0, f);
+#pragma unroll
+        for (int j = 0; j < kFragN; ++j) read_b(0, j, bop0, sb0);
+    }
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, bop0, sb0, bop1, sb1);
+        if (kt + 1 < nk) step(kt + 1, bop1, sb1, bop0, sb0);
     }
 
     // Accumulator layout: lane l, register r holds row 4 (l / 16) + r,
