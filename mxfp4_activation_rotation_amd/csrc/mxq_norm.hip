@@ -19,12 +19,20 @@
 // steps as the plain kernel.  Waves walk the rows with a stride of the grid's
 // wave count; channels up to 2048 NT (NT = 1, 2, 4, 8).
 //
-// Row statistics.  The 8 values of a 16-byte load are exact in fp32; their
-// sum (LayerNorm) and sum of squares are formed in fp32 (8 terms) and
-// accumulated in fp64, then reduced across the wave in fp64, so the relative
-// error of the mean square stays near 8 ulp of fp32 whatever the row length.
+// Row statistics.  Per super-tile (4 x 32 values of each of a lane's
+// groups) a sum is formed in fp32 and the super-tiles are accumulated in
+// fp64, then reduced across the wave in fp64, so the relative error of the
+// mean square stays within ~128 ulp of fp32 at worst whatever the row
+// length.  The RMS sum of squares and the LayerNorm sum run
+// on the matrix cores, straight from the packed 16-bit elements: for the
+// 16 x 16 x 32 MFMA the A and B operand layouts agree (lane l holds positions
+// 8 (l / 16) .. + 7 of row, or column, l % 16), so the register that holds a
+// sub-tile (lane l: channels 8 q .. + 7 of group j) times itself gives the
+// Gram matrix of the sub-tile's 16 groups, whose diagonal holds the groups'
+// sums of squares; with an all-ones A operand every row of the product holds
+// the groups' sums.  The products are exact in fp32 (16-bit significands).
 // LayerNorm takes the mean in a first sweep over the registers and the
-// centred sum of squares in a second (no cancellation).
+// centred sum of squares on the VALU in a second (no cancellation).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -67,6 +75,20 @@ struct NormArgs {
     int32_t gpr;
     int32_t waves;  // waves in the grid (row stride)
 };
+
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+
+// c + the 16 x 16 x 32 product of two operands of packed 16-bit elements
+// (the format of x), accumulated in fp32.
+template <bool IS_FP16>
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t z) {
+    if constexpr (IS_FP16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), z,
+                                                      0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                       z, 0, 0, 0);
+}
 
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
@@ -157,18 +179,18 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
         // ---- row statistics (groups past the row end loaded zeros)
         float mu = 0.0f;
         if constexpr (NORM == kLayer) {
+            // all-ones A operand (packed 1.0 pairs): row 0 of the product
+            // (register 0 of lanes 0..15) holds the sums of groups j = lane
+            constexpr uint32_t kOne2 = kFp16 ? 0x3c003c00u : 0x3f803f80u;
+            const u32x4_t ones = {kOne2, kOne2, kOne2, kOne2};
             double part = 0.0;
 #pragma unroll
-            for (int st = 0; st < NT; ++st)
+            for (int st = 0; st < NT; ++st) {
+                f32x4_t sums = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int s = 0; s < kSub; ++s) {
-                    float f[8];
-                    widen8<kFp16>(buf[st][s], f);
-                    float c8 = 0.0f;
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) c8 += f[t];
-                    part += static_cast<double>(c8);
-                }
+                for (int s = 0; s < kSub; ++s) sums = mfma16<kFp16>(ones, buf[st][s], sums);
+                part += q == 0 ? static_cast<double>(sums[0]) : 0.0;
+            }
             mu = static_cast<float>(wave_sum(part) / C);
 #pragma unroll
             for (int st = 0; st < NT; ++st)
@@ -177,20 +199,34 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
         }
         double part = 0.0;
 #pragma unroll
-        for (int st = 0; st < NT; ++st)
+        for (int st = 0; st < NT; ++st) {
+            if constexpr (NORM == kLayer) {
 #pragma unroll
-            for (int s = 0; s < kSub; ++s) {
-                const bool valid = kTileGroups * st + 16 * s + j < a.gpr;
-                float f[8];
-                widen8<kFp16>(buf[st][s], f);
-                float c8 = 0.0f;
+                for (int s = 0; s < kSub; ++s) {
+                    // lanes of groups past the row end loaded zeros, which
+                    // are not zero once centred
+                    const bool valid = kTileGroups * st + 16 * s + j < a.gpr;
+                    float f[8];
+                    widen8<kFp16>(buf[st][s], f);
+                    float c8 = 0.0f;
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const float d = f[t] - mu;
-                    c8 += d * d;
+                    for (int t = 0; t < 8; ++t) {
+                        const float d = f[t] - mu;
+                        c8 += d * d;
+                    }
+                    part += valid ? static_cast<double>(c8) : 0.0;
                 }
-                part += valid ? static_cast<double>(c8) : 0.0;
+            } else {
+                // diagonal entry (j, j) of the super-tile's Gram matrices:
+                // lane 16 (j / 4) + j, register j % 4
+                f32x4_t gram = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int s = 0; s < kSub; ++s) gram = mfma16<kFp16>(buf[st][s], buf[st][s], gram);
+                const int r = j & 3;
+                const float dj = r == 0 ? gram[0] : r == 1 ? gram[1] : r == 2 ? gram[2] : gram[3];
+                part += q == (j >> 2) ? static_cast<double>(dj) : 0.0;
             }
+        }
         const double var = wave_sum(part) / C;
         const float inv = static_cast<float>(1.0 / sqrt(var + static_cast<double>(a.eps)));
         // Keep only the packed row live across the statistics: an empty asm
