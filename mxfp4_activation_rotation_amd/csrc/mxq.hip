@@ -330,8 +330,13 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
             // lines); scattered 16-byte stores, one line per lane, cost
             // half the bandwidth.  The 16 scale bytes of a lane's group are
             // contiguous in its record and go out as one 16-byte store per
-            // unit.
-            __shared__ u32x4_t stg[kWavesPerBlock][8][kTileGroups + 1];
+            // unit.  The tile's row pitch is 66 slots of 16 bytes: a
+            // ds_read_b128 serves 16 lanes per pass from 64 four-byte banks,
+            // and the 16 lanes of a pass read 8 rows x 2 groups, which a
+            // pitch of 2 (mod 16) slots spreads over all 16 bank quads (a
+            // pitch of 65 would put row r + 1 of group g on the banks of row
+            // r of group g + 1).
+            __shared__ u32x4_t stg[kWavesPerBlock][8][kTileGroups + 2];
             const uint32_t nrec = gpr / 4;
             const uint32_t rec0 = static_cast<uint32_t>(p0) / 4;
             const uint32_t grp = static_cast<uint32_t>(p0 + lane);
