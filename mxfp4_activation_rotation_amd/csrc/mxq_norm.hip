@@ -31,8 +31,11 @@
 // Gram matrix of the sub-tile's 16 groups, whose diagonal holds the groups'
 // sums of squares; with an all-ones A operand every row of the product holds
 // the groups' sums.  The products are exact in fp32 (16-bit significands).
-// LayerNorm takes the mean in a first sweep over the registers and the
-// centred sum of squares on the VALU in a second (no cancellation).
+// LayerNorm takes a shift near the mean in a first sweep over the registers
+// and the sums of x - shift and of its square on the VALU in a second, which
+// gives the mean and variance with errors relative to the row's spread (a
+// mean rounded to fp32 would be off by up to half an fp32 ulp of the mean,
+// 3e-5 sd at mean / sd = 1000).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -177,7 +180,12 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
             if (r + a.waves < a.tokens) load_row(bufB, r + a.waves);
         }
         // ---- row statistics (groups past the row end loaded zeros)
-        float mu = 0.0f;
+        // LayerNorm: the first sweep gives a shift mu0 (an fp32 value near
+        // the mean); the second accumulates x - mu0 and its square, so that
+        // mean = mu0 + E[x - mu0] and var = E[(x - mu0)^2] - E[x - mu0]^2
+        // carry errors relative to the spread of the row, not to its mean.
+        // The mean is then applied as an fp32 pair mu + mu_lo.
+        float mu = 0.0f, mu_lo = 0.0f;
         if constexpr (NORM == kLayer) {
             // all-ones A operand (packed 1.0 pairs): row 0 of the product
             // (register 0 of lanes 0..15) holds the sums of groups j = lane
@@ -197,7 +205,7 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
 #pragma unroll
                 for (int s = 0; s < kSub; ++s) asm volatile("" : "+v"(buf[st][s]));
         }
-        double part = 0.0;
+        double part = 0.0, part1 = 0.0;
 #pragma unroll
         for (int st = 0; st < NT; ++st) {
             if constexpr (NORM == kLayer) {
@@ -208,13 +216,15 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
                     const bool valid = kTileGroups * st + 16 * s + j < a.gpr;
                     float f[8];
                     widen8<kFp16>(buf[st][s], f);
-                    float c8 = 0.0f;
+                    float c8 = 0.0f, s8 = 0.0f;
 #pragma unroll
                     for (int t = 0; t < 8; ++t) {
                         const float d = f[t] - mu;
+                        s8 += d;
                         c8 += d * d;
                     }
                     part += valid ? static_cast<double>(c8) : 0.0;
+                    part1 += valid ? static_cast<double>(s8) : 0.0;
                 }
             } else {
                 // diagonal entry (j, j) of the super-tile's Gram matrices:
@@ -227,7 +237,14 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
                 part += q == (j >> 2) ? static_cast<double>(dj) : 0.0;
             }
         }
-        const double var = wave_sum(part) / C;
+        double var = wave_sum(part) / C;
+        if constexpr (NORM == kLayer) {
+            const double d1 = wave_sum(part1) / C;  // E[x - mu0]
+            var -= d1 * d1;
+            const double mean = static_cast<double>(mu) + d1;
+            mu = static_cast<float>(mean);
+            mu_lo = static_cast<float>(mean - static_cast<double>(mu));
+        }
         const float inv = static_cast<float>(1.0 / sqrt(var + static_cast<double>(a.eps)));
         // Keep only the packed row live across the statistics: an empty asm
         // that claims to change the registers stops the compiler from holding
@@ -262,8 +279,8 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
                 widen8<kFp16>(buf[st][s], f);
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const float d0 = NORM == kLayer ? (f[t] - mu) * inv : f[t] * inv;
-                    const float d1 = NORM == kLayer ? (f[4 + t] - mu) * inv : f[4 + t] * inv;
+                    const float d0 = NORM == kLayer ? ((f[t] - mu) - mu_lo) * inv : f[t] * inv;
+                    const float d1 = NORM == kLayer ? ((f[4 + t] - mu) - mu_lo) * inv : f[4 + t] * inv;
                     f[t] = __builtin_fmaf(d0, m0[t], b0[t]);
                     f[4 + t] = __builtin_fmaf(d1, m1[t], b1[t]);
                 }

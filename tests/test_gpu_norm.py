@@ -118,6 +118,24 @@ def test_norm_bench_workload_sampled(dev, orc):
     print(f"  bench workload, 256 sampled rows: {stats}", flush=True)
 
 
+@pytest.mark.parametrize("C,dtype,offset,sigma", [(4096, torch.bfloat16, 200.0, 8.0),
+                                                   (16384, torch.bfloat16, 200.0, 8.0),
+                                                   (4096, torch.float16, 1000.0, 1.0),
+                                                   (16384, torch.float16, 1000.0, 1.0)])
+def test_layernorm_large_mean_offset(dev, orc, C, dtype, offset, sigma):
+    """LayerNorm rows whose mean is large against their spread (mean / sd up
+    to 1000): the mean's absolute error scales with the mean, so this is the
+    case that tests the precision of the row sums."""
+    rng = np.random.default_rng(4206 + C)
+    T = 48
+    x = torch.from_numpy(offset + sigma * rng.standard_normal((T, C))).to(dtype)
+    gamma = rng.uniform(0.5, 1.5, C).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(C)).astype(np.float32)
+    lam = np.exp(0.5 * rng.standard_normal(C)).astype(np.float32)
+    stats = full_check(x, W.bf16_matrix(W.qr_orthogonal(rng)), gamma, beta, lam, "layer", 1e-5, dev, orc)
+    assert stats["worst_abs_err_over_norm"] < 2e-6
+
+
 @pytest.mark.parametrize("norm", ["rms", "layer"])
 def test_norm_block_sizes_same_bits(dev, norm):
     """Long batches run in 16-wave blocks, short ones in 4-wave blocks: the
