@@ -151,8 +151,12 @@ mxq_status mxq_rotate_quant_block(const void *x, int32_t x_dtype, int64_t tokens
  *            negative or NaN).  A row of zeros with eps = 0 is outside the
  *            contract (0 / 0).
  *   y_rot    NULL, or fp32 [tokens][channels] receiving the rotated values
- * Arithmetic: row sums in fp32 per 8 values, accumulated and reduced in
- * fp64; 1/sqrt in fp64, rounded to fp32; x'_c = fma(n_c, gamma_c/lambda_c,
+ * Arithmetic: row sums in fp32 per 128 values (exact products of the 16-bit
+ * inputs on the matrix cores; LayerNorm's centred sums per 8 values on the
+ * vector units, about a shift near the mean), accumulated and reduced in
+ * fp64; the LayerNorm mean is subtracted as an fp32 pair (hi + lo), so its
+ * error scales with the row's spread, not its mean; 1/sqrt in fp64,
+ * rounded to fp32; x'_c = fma(n_c, gamma_c/lambda_c,
  * beta_c/lambda_c) in fp32 (the two factors formed once per block with IEEE
  * division); the product with the block as in mxq_rotate_quant (3 exact
  * bf16 terms).  Same layout, alignment (gamma, beta, lambda: 4 bytes) and
