@@ -112,6 +112,22 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
     __shared__ __attribute__((aligned(16))) f32x4_t fm[kUnits];  // gamma / lambda
     __shared__ __attribute__((aligned(16))) f32x4_t fb[kUnits];  // beta / lambda
 
+    // Fragment-tiled output of long batches (blocks of 8 or 16 waves): the
+    // waves of a block hold BW consecutive rows (a record row, or half of
+    // one), so their codes and scales meet in a block-shared LDS tile (two
+    // of them, alternating) and the block stores whole records, 128-byte
+    // lines at least, instead of one 16-byte piece per line from each row.
+    // Row pitches in 16-byte slots: odd for 16 rows (a store lane l reads
+    // row l % 16 of one group), 2 mod 16 for 8 rows (row l % 8 of group
+    // (l / 8) % 4), so the 16 lanes of a ds_read_b128 pass hit distinct
+    // bank quads.
+    constexpr bool kStaged = TILED && BW >= 8;
+    constexpr int kGroups = NT * kTileGroups;
+    constexpr int kPitch = kGroups + (BW == 16 ? 1 : 2);
+    __shared__ __attribute__((aligned(16))) u32x4_t stg[kStaged ? 2 : 1][kStaged ? BW : 1][kStaged ? kPitch : 1];
+    __shared__ __attribute__((aligned(16))) uint8_t sstg[kStaged ? 2 : 1][kStaged ? kGroups * BW : 1];
+    static_assert(!kStaged || BW == 8 || BW == 16, "a staged tile is a record row or half of one");
+
     // Factor setup: consecutive threads take consecutive channels (coalesced
     // loads of gamma, beta, lambda) and scatter the two factors to the lane
     // order above.  Channels past the row end keep factor 0.
@@ -173,9 +189,20 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
     constexpr bool kDouble = NT <= 2;
     u32x4_t bufA[NT][kSub], bufB[NT][kSub];
     if (w < a.tokens) load_row(bufA, w);
-    for (int64_t r_loop = w; r_loop < a.tokens; r_loop += a.waves) {
-        const int64_t r = __builtin_amdgcn_readfirstlane(static_cast<int>(r_loop));
+    // Staged: the loop runs over the block's row groups, the same for every
+    // wave of the block (it meets a barrier each time); a wave whose row is
+    // past the end stages zeros, which become the padding rows.
+    int sb = 0;  // staging tile of this step
+    for (int64_t r_loop = kStaged ? w - wave : w; r_loop < a.tokens; r_loop += a.waves) {
+        const int64_t r = __builtin_amdgcn_readfirstlane(static_cast<int>(kStaged ? r_loop + wave : r_loop));
         u32x4_t (&buf)[NT][kSub] = bufA;
+        if (kStaged && r >= a.tokens) {
+#pragma unroll
+            for (int st = 0; st < NT; ++st) {
+                stg[sb][kStaged ? wave : 0][kTileGroups * st + lane] = u32x4_t{0u, 0u, 0u, 0u};
+                sstg[sb][(kTileGroups * st + lane) * BW + wave] = 0;
+            }
+        } else {
         if constexpr (kDouble) {
             if (r + a.waves < a.tokens) load_row(bufB, r + a.waves);
         }
@@ -320,10 +347,15 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
             transpose_words(word);
             const uint32_t S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
             const uint32_t g = static_cast<uint32_t>(kTileGroups * st + lane);
-            const uint32_t slot = TILED ? (g >> 2) * 64 + (g & 3) * 16 + r16 : g;
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{word[0], word[1], word[2], word[3]}, crsrc, slot * 16, 0,
-                                                   TILED ? 0 : kAuxNT);
-            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, slot, 0, 0);
+            if constexpr (kStaged) {
+                stg[sb][wave][g] = u32x4_t{word[0], word[1], word[2], word[3]};
+                sstg[sb][g * BW + wave] = static_cast<uint8_t>(S);
+            } else {
+                const uint32_t slot = TILED ? (g >> 2) * 64 + (g & 3) * 16 + r16 : g;
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{word[0], word[1], word[2], word[3]}, crsrc, slot * 16,
+                                                       0, TILED ? 0 : kAuxNT);
+                __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, slot, 0, 0);
+            }
         }
         if constexpr (kDouble) {
 #pragma unroll
@@ -332,6 +364,43 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
                 for (int s = 0; s < kSub; ++s) bufA[st][s] = bufB[st][s];
         } else {
             if (r + a.waves < a.tokens) load_row(bufA, r + a.waves);
+        }
+        }  // row of this wave
+        if constexpr (kStaged) {
+            // Every wave's LDS writes complete, then the block meets.  A bare
+            // s_barrier: __syncthreads() would also wait for the next rows'
+            // loads in flight.  The "memory" clobber keeps the compiler from
+            // moving LDS accesses across it.
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            const int64_t base = r_loop;  // first row of the block's group
+            const uint32_t nrec = gpr / 4;
+            const auto crt = row_rsrc(a.codes + (base >> 4) * nrec * 1024, nrec * 1024);
+            const auto srt = row_rsrc(a.scales + (base >> 4) * nrec * 64, nrec * 64);
+            if constexpr (BW == 16) {
+                // lane l: slot l of record s = row l % 16, group 4 s + l / 16
+                for (uint32_t s = static_cast<uint32_t>(wave); s < nrec; s += BW)
+                    __builtin_amdgcn_raw_buffer_store_b128(stg[sb][lane & 15][4 * s + (lane >> 4)], crt,
+                                                           s * 1024 + 16 * static_cast<uint32_t>(lane), 0, 0);
+                for (uint32_t g = static_cast<uint32_t>(wave * kWave + lane); g < gpr; g += BW * kWave)
+                    __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4_t*>(&sstg[sb][g * BW]), srt,
+                                                           (g >> 2) * 64 + (g & 3) * 16, 0, 0);
+            } else {
+                // half record rows: lane l carries row l % 8 of group (l / 8) % 4
+                // of record 2 m + l / 32
+                const uint32_t hb = static_cast<uint32_t>(base >> 3) & 1;
+                const uint32_t lr = static_cast<uint32_t>(lane & 7);
+                const uint32_t lg = static_cast<uint32_t>(lane >> 3) & 3;
+                for (uint32_t m = static_cast<uint32_t>(wave); 2 * m < nrec; m += BW) {
+                    const uint32_t s = 2 * m + static_cast<uint32_t>(lane >> 5);
+                    if (s < nrec)
+                        __builtin_amdgcn_raw_buffer_store_b128(stg[sb][lr][4 * s + lg], crt,
+                                                               s * 1024 + lg * 256 + (8 * hb + lr) * 16, 0, 0);
+                }
+                for (uint32_t g = static_cast<uint32_t>(wave * kWave + lane); g < gpr; g += BW * kWave)
+                    __builtin_amdgcn_raw_buffer_store_b64(*reinterpret_cast<const u32x2_t*>(&sstg[sb][g * BW]), srt,
+                                                          (g >> 2) * 64 + (g & 3) * 16 + 8 * hb, 0, 0);
+            }
+            sb ^= 1;
         }
     }
 }
