@@ -323,65 +323,56 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
         static_assert(kBatch == 1, "one row per step");
         if (a.unit == 16) {
             // Units of 16 consecutive rows (one record row), units
-            // r0 / 16 + k * rs, in two halves of 8 rows.  A half's codes go
-            // to a per-wave LDS tile ([row][group], padded) and leave it
-            // record by record, so each store instruction writes 1 KB
-            // contiguously (two records' 8-row halves: 8 full 128-byte
-            // lines); scattered 16-byte stores, one line per lane, cost
-            // half the bandwidth.  The 16 scale bytes of a lane's group are
-            // contiguous in its record and go out as one 16-byte store per
-            // unit.  The tile's row pitch is 66 slots of 16 bytes: a
-            // ds_read_b128 serves 16 lanes per pass from 64 four-byte banks,
-            // and the 16 lanes of a pass read 8 rows x 2 groups, which a
-            // pitch of 2 (mod 16) slots spreads over all 16 bank quads (a
-            // pitch of 65 would put row r + 1 of group g on the banks of row
-            // r of group g + 1).
-            __shared__ u32x4_t stg[kWavesPerBlock][8][kTileGroups + 2];
+            // r0 / 16 + k * rs.  The unit's codes go to a per-wave LDS tile
+            // ([row][group], padded) and leave it record by record: lane l
+            // carries slot l (row l % 16, group 4 rec + l / 16), so each
+            // store instruction writes one whole 1 KB record.  Scattered
+            // 16-byte stores (one line per lane) cost half the bandwidth,
+            // and records written as two 8-row halves at different times
+            // (every 256-byte group chunk in two pieces) cost 5 %.  The 16
+            // scale bytes of a lane's group are contiguous in its record and
+            // go out as one 16-byte store per unit.  Both stores are
+            // non-temporal (written once, read by the next kernel).  The
+            // tile's row pitch is 65 slots of 16 bytes: the 16 lanes of a
+            // ds_read_b128 pass read 16 rows of one group, which an odd pitch
+            // spreads over all 16 bank quads of the 64 four-byte banks.
+            __shared__ u32x4_t stg[kWavesPerBlock][16][kTileGroups + 1];
             const uint32_t nrec = gpr / 4;
             const uint32_t rec0 = static_cast<uint32_t>(p0) / 4;
             const uint32_t grp = static_cast<uint32_t>(p0 + lane);
             const uint32_t soff = (grp >> 2) * 64 + (grp & 3) * 16;
-            // store map: lane l carries row l % 8 of group (l / 8) % 4 of
-            // record 2 m + l / 32 of the super-tile column
-            const int st_row = lane & 7;
-            const int st_grp = (lane >> 3) & 3;
-            const int st_rec = lane >> 5;
+            const int st_row = lane & 15;
+            const int st_grp = lane >> 4;
             for (int64_t unit = r0; unit < T; unit += 16 * rs) {
                 uint32_t spk[4] = {0u, 0u, 0u, 0u};
                 const auto crsrc = row_rsrc(a.codes + (unit >> 4) * nrec * 1024, nrec * 1024);
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int k = 8 * hh + i;
-                        const int64_t r = unit + k;
-                        if (r < T) {
-                            const int64_t rn = k < 15 ? r + 1 : unit + 16 * rs;
-                            Rows& cur = (i & 1) ? bufB : bufA;
-                            Rows& nxt = (i & 1) ? bufA : bufB;
-                            if (rn < T) load_rows(nxt, rn);
-                            uint32_t word[kSub];
-                            uint32_t S;
-                            encode_row(cur, 0, r, word, S);
-                            stg[wave][i][lane] = u32x4_t{word[0], word[1], word[2], word[3]};
-                            spk[k / 4] |= S << (8 * (k % 4));
-                        }
-                    }
-                    const bool row_ok = unit + 8 * hh + st_row < T;
-#pragma unroll
-                    for (int m = 0; m < 8; ++m) {
-                        const int rec = 2 * m + st_rec;
-                        const u32x4_t v = stg[wave][st_row][4 * rec + st_grp];
-                        if (row_ok)
-                            __builtin_amdgcn_raw_buffer_store_b128(
-                                v, crsrc,
-                                (rec0 + static_cast<uint32_t>(rec)) * 1024 + static_cast<uint32_t>(st_grp) * 256 +
-                                    static_cast<uint32_t>(8 * hh + st_row) * 16,
-                                0, 0);
+                for (int k = 0; k < 16; ++k) {
+                    const int64_t r = unit + k;
+                    if (r < T) {
+                        const int64_t rn = k < 15 ? r + 1 : unit + 16 * rs;
+                        Rows& cur = (k & 1) ? bufB : bufA;
+                        Rows& nxt = (k & 1) ? bufA : bufB;
+                        if (rn < T) load_rows(nxt, rn);
+                        uint32_t word[kSub];
+                        uint32_t S;
+                        encode_row(cur, 0, r, word, S);
+                        stg[wave][k][lane] = u32x4_t{word[0], word[1], word[2], word[3]};
+                        spk[k / 4] |= S << (8 * (k % 4));
                     }
                 }
+                // rows past the end (the last unit's padding) are not written
+                const bool row_ok = unit + st_row < T;
+#pragma unroll
+                for (int rec = 0; rec < 16; ++rec) {
+                    const u32x4_t v = stg[wave][st_row][4 * rec + st_grp];
+                    if (row_ok)
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            v, crsrc, (rec0 + static_cast<uint32_t>(rec)) * 1024 + 16 * static_cast<uint32_t>(lane), 0,
+                            kAuxNT);
+                }
                 const auto srsrc = row_rsrc(a.scales + (unit >> 4) * nrec * 64, nrec * 64);
-                __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{spk[0], spk[1], spk[2], spk[3]}, srsrc, soff, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{spk[0], spk[1], spk[2], spk[3]}, srsrc, soff, 0, kAuxNT);
             }
         } else {
             for (int64_t r = r0; r < T; r += 2 * rs) {
