@@ -117,6 +117,7 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
     // one), so their codes and scales meet in a block-shared LDS tile (two
     // of them, alternating) and the block stores whole records, 128-byte
     // lines at least, instead of one 16-byte piece per line from each row.
+    // The stores are non-temporal (written once, read by the next kernel).
     // Row pitches in 16-byte slots: odd for 16 rows (a store lane l reads
     // row l % 16 of one group), 2 mod 16 for 8 rows (row l % 8 of group
     // (l / 8) % 4), so the 16 lanes of a ds_read_b128 pass hit distinct
@@ -380,10 +381,10 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
                 // lane l: slot l of record s = row l % 16, group 4 s + l / 16
                 for (uint32_t s = static_cast<uint32_t>(wave); s < nrec; s += BW)
                     __builtin_amdgcn_raw_buffer_store_b128(stg[sb][lane & 15][4 * s + (lane >> 4)], crt,
-                                                           s * 1024 + 16 * static_cast<uint32_t>(lane), 0, 0);
+                                                           s * 1024 + 16 * static_cast<uint32_t>(lane), 0, kAuxNT);
                 for (uint32_t g = static_cast<uint32_t>(wave * kWave + lane); g < gpr; g += BW * kWave)
                     __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4_t*>(&sstg[sb][g * BW]), srt,
-                                                           (g >> 2) * 64 + (g & 3) * 16, 0, 0);
+                                                           (g >> 2) * 64 + (g & 3) * 16, 0, kAuxNT);
             } else {
                 // half record rows: lane l carries row l % 8 of group (l / 8) % 4
                 // of record 2 m + l / 32
@@ -394,11 +395,11 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
                     const uint32_t s = 2 * m + static_cast<uint32_t>(lane >> 5);
                     if (s < nrec)
                         __builtin_amdgcn_raw_buffer_store_b128(stg[sb][lr][4 * s + lg], crt,
-                                                               s * 1024 + lg * 256 + (8 * hb + lr) * 16, 0, 0);
+                                                               s * 1024 + lg * 256 + (8 * hb + lr) * 16, 0, kAuxNT);
                 }
                 for (uint32_t g = static_cast<uint32_t>(wave * kWave + lane); g < gpr; g += BW * kWave)
                     __builtin_amdgcn_raw_buffer_store_b64(*reinterpret_cast<const u32x2_t*>(&sstg[sb][g * BW]), srt,
-                                                          (g >> 2) * 64 + (g & 3) * 16 + 8 * hb, 0, 0);
+                                                          (g >> 2) * 64 + (g & 3) * 16 + 8 * hb, 0, kAuxNT);
             }
             sb ^= 1;
         }
