@@ -170,7 +170,8 @@ def test_rotate_quant_tiled_prefill_sizes(dev, T, dtype, with_lam):
                                  # long batches: 16-wave blocks stage a record row in LDS
                                  # (>= 4096 rows up to 4096 channels), 8-wave blocks half
                                  # of one (>= 2048 rows up to 8192 channels); ragged ends
-                                 (4100, 4096), (4099, 2432), (2050, 8192), (2061, 5120)])
+                                 (4100, 4096), (4099, 2432), (2050, 8192), (2061, 5120),
+                                 (64, 16384)])
 @pytest.mark.parametrize("norm,dtype,with_beta,with_lam", [("rms", torch.bfloat16, False, True),
                                                            ("layer", torch.float16, True, True),
                                                            ("rms", torch.float16, False, False)])
