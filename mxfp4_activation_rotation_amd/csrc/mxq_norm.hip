@@ -204,168 +204,168 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
                 sstg[sb][(kTileGroups * st + lane) * BW + wave] = 0;
             }
         } else {
-        if constexpr (kDouble) {
-            if (r + a.waves < a.tokens) load_row(bufB, r + a.waves);
-        }
-        // ---- row statistics (groups past the row end loaded zeros)
-        // LayerNorm: the first sweep gives a shift mu0 (an fp32 value near
-        // the mean); the second accumulates x - mu0 and its square, so that
-        // mean = mu0 + E[x - mu0] and var = E[(x - mu0)^2] - E[x - mu0]^2
-        // carry errors relative to the spread of the row, not to its mean.
-        // The mean is then applied as an fp32 pair mu + mu_lo.
-        float mu = 0.0f, mu_lo = 0.0f;
-        if constexpr (NORM == kLayer) {
-            // all-ones A operand (packed 1.0 pairs): row 0 of the product
-            // (register 0 of lanes 0..15) holds the sums of groups j = lane
-            constexpr uint32_t kOne2 = kFp16 ? 0x3c003c00u : 0x3f803f80u;
-            const u32x4_t ones = {kOne2, kOne2, kOne2, kOne2};
-            double part = 0.0;
+            if constexpr (kDouble) {
+                if (r + a.waves < a.tokens) load_row(bufB, r + a.waves);
+            }
+            // ---- row statistics (groups past the row end loaded zeros)
+            // LayerNorm: the first sweep gives a shift mu0 (an fp32 value near
+            // the mean); the second accumulates x - mu0 and its square, so that
+            // mean = mu0 + E[x - mu0] and var = E[(x - mu0)^2] - E[x - mu0]^2
+            // carry errors relative to the spread of the row, not to its mean.
+            // The mean is then applied as an fp32 pair mu + mu_lo.
+            float mu = 0.0f, mu_lo = 0.0f;
+            if constexpr (NORM == kLayer) {
+                // all-ones A operand (packed 1.0 pairs): row 0 of the product
+                // (register 0 of lanes 0..15) holds the sums of groups j = lane
+                constexpr uint32_t kOne2 = kFp16 ? 0x3c003c00u : 0x3f803f80u;
+                const u32x4_t ones = {kOne2, kOne2, kOne2, kOne2};
+                double part = 0.0;
+#pragma unroll
+                for (int st = 0; st < NT; ++st) {
+                    f32x4_t sums = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int s = 0; s < kSub; ++s) sums = mfma16<kFp16>(ones, buf[st][s], sums);
+                    part += q == 0 ? static_cast<double>(sums[0]) : 0.0;
+                }
+                mu = static_cast<float>(wave_sum(part) / C);
+#pragma unroll
+                for (int st = 0; st < NT; ++st)
+#pragma unroll
+                    for (int s = 0; s < kSub; ++s) asm volatile("" : "+v"(buf[st][s]));
+            }
+            double part = 0.0, part1 = 0.0;
 #pragma unroll
             for (int st = 0; st < NT; ++st) {
-                f32x4_t sums = {0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (NORM == kLayer) {
 #pragma unroll
-                for (int s = 0; s < kSub; ++s) sums = mfma16<kFp16>(ones, buf[st][s], sums);
-                part += q == 0 ? static_cast<double>(sums[0]) : 0.0;
+                    for (int s = 0; s < kSub; ++s) {
+                        // lanes of groups past the row end loaded zeros, which
+                        // are not zero once centred
+                        const bool valid = kTileGroups * st + 16 * s + j < a.gpr;
+                        float f[8];
+                        widen8<kFp16>(buf[st][s], f);
+                        float c8 = 0.0f, s8 = 0.0f;
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) {
+                            const float d = f[t] - mu;
+                            s8 += d;
+                            c8 += d * d;
+                        }
+                        part += valid ? static_cast<double>(c8) : 0.0;
+                        part1 += valid ? static_cast<double>(s8) : 0.0;
+                    }
+                } else {
+                    // diagonal entry (j, j) of the super-tile's Gram matrices:
+                    // lane 16 (j / 4) + j, register j % 4
+                    f32x4_t gram = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int s = 0; s < kSub; ++s) gram = mfma16<kFp16>(buf[st][s], buf[st][s], gram);
+                    const int r = j & 3;
+                    const float dj = r == 0 ? gram[0] : r == 1 ? gram[1] : r == 2 ? gram[2] : gram[3];
+                    part += q == (j >> 2) ? static_cast<double>(dj) : 0.0;
+                }
             }
-            mu = static_cast<float>(wave_sum(part) / C);
+            double var = wave_sum(part) / C;
+            if constexpr (NORM == kLayer) {
+                const double d1 = wave_sum(part1) / C;  // E[x - mu0]
+                var -= d1 * d1;
+                const double mean = static_cast<double>(mu) + d1;
+                mu = static_cast<float>(mean);
+                mu_lo = static_cast<float>(mean - static_cast<double>(mu));
+            }
+            const float inv = static_cast<float>(1.0 / sqrt(var + static_cast<double>(a.eps)));
+            // Keep only the packed row live across the statistics: an empty asm
+            // that claims to change the registers stops the compiler from holding
+            // the widened fp32 copies (twice the registers) until the second use.
 #pragma unroll
             for (int st = 0; st < NT; ++st)
 #pragma unroll
                 for (int s = 0; s < kSub; ++s) asm volatile("" : "+v"(buf[st][s]));
-        }
-        double part = 0.0, part1 = 0.0;
+
+            // ---- normalize, smooth, rotate, encode
+            // Row layout: the row's codes and scales.  Fragment-tiled layout
+            // (records of 16 rows x 4 groups): the row's record row; group g of
+            // row r is slot 16 (g % 4) + r % 16 of record g / 4.
+            const uint32_t nrec = gpr / 4;
+            const auto crsrc = TILED ? row_rsrc(a.codes + (r >> 4) * nrec * 1024, nrec * 1024)
+                                     : row_rsrc(a.codes + r * a.gpr * 16, gpr * 16);
+            const auto srsrc = TILED ? row_rsrc(a.scales + (r >> 4) * nrec * 64, nrec * 64)
+                                     : row_rsrc(a.scales + r * a.gpr, gpr);
+            const uint32_t r16 = static_cast<uint32_t>(r & 15);
 #pragma unroll
-        for (int st = 0; st < NT; ++st) {
-            if constexpr (NORM == kLayer) {
+            for (int st = 0; st < NT; ++st) {
+                uint32_t word[kSub];
+                uint32_t sc[kSub];
 #pragma unroll
                 for (int s = 0; s < kSub; ++s) {
-                    // lanes of groups past the row end loaded zeros, which
-                    // are not zero once centred
-                    const bool valid = kTileGroups * st + 16 * s + j < a.gpr;
+                    const int ss = st * kSub + s;
+                    const f32x4_t m0 = fm[(ss * 2 + 0) * kWave + lane];
+                    const f32x4_t m1 = fm[(ss * 2 + 1) * kWave + lane];
+                    const f32x4_t b0 = fb[(ss * 2 + 0) * kWave + lane];
+                    const f32x4_t b1 = fb[(ss * 2 + 1) * kWave + lane];
                     float f[8];
                     widen8<kFp16>(buf[st][s], f);
-                    float c8 = 0.0f, s8 = 0.0f;
 #pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        const float d = f[t] - mu;
-                        s8 += d;
-                        c8 += d * d;
+                    for (int t = 0; t < 4; ++t) {
+                        const float d0 = NORM == kLayer ? ((f[t] - mu) - mu_lo) * inv : f[t] * inv;
+                        const float d1 = NORM == kLayer ? ((f[4 + t] - mu) - mu_lo) * inv : f[4 + t] * inv;
+                        f[t] = __builtin_fmaf(d0, m0[t], b0[t]);
+                        f[4 + t] = __builtin_fmaf(d1, m1[t], b1[t]);
                     }
-                    part += valid ? static_cast<double>(c8) : 0.0;
-                    part1 += valid ? static_cast<double>(s8) : 0.0;
-                }
-            } else {
-                // diagonal entry (j, j) of the super-tile's Gram matrices:
-                // lane 16 (j / 4) + j, register j % 4
-                f32x4_t gram = {0.0f, 0.0f, 0.0f, 0.0f};
+                    // exact bf16 terms of the fp32 values (3 terms cover 24 bits)
+                    f32x4_t d0 = {}, d1 = {};
 #pragma unroll
-                for (int s = 0; s < kSub; ++s) gram = mfma16<kFp16>(buf[st][s], buf[st][s], gram);
-                const int r = j & 3;
-                const float dj = r == 0 ? gram[0] : r == 1 ? gram[1] : r == 2 ? gram[2] : gram[3];
-                part += q == (j >> 2) ? static_cast<double>(dj) : 0.0;
-            }
-        }
-        double var = wave_sum(part) / C;
-        if constexpr (NORM == kLayer) {
-            const double d1 = wave_sum(part1) / C;  // E[x - mu0]
-            var -= d1 * d1;
-            const double mean = static_cast<double>(mu) + d1;
-            mu = static_cast<float>(mean);
-            mu_lo = static_cast<float>(mean - static_cast<double>(mu));
-        }
-        const float inv = static_cast<float>(1.0 / sqrt(var + static_cast<double>(a.eps)));
-        // Keep only the packed row live across the statistics: an empty asm
-        // that claims to change the registers stops the compiler from holding
-        // the widened fp32 copies (twice the registers) until the second use.
+                    for (int term = 0; term < 3; ++term) {
+                        u32x4_t bt;
 #pragma unroll
-        for (int st = 0; st < NT; ++st)
+                        for (int i = 0; i < 4; ++i) bt[i] = bf16_pair_hi(f[2 * i], f[2 * i + 1]);
+                        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bt);
+                        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, b, d0, 0, 0, 0);
+                        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b, d1, 0, 0, 0);
+                        if (term < 2) {
 #pragma unroll
-            for (int s = 0; s < kSub; ++s) asm volatile("" : "+v"(buf[st][s]));
-
-        // ---- normalize, smooth, rotate, encode
-        // Row layout: the row's codes and scales.  Fragment-tiled layout
-        // (records of 16 rows x 4 groups): the row's record row; group g of
-        // row r is slot 16 (g % 4) + r % 16 of record g / 4.
-        const uint32_t nrec = gpr / 4;
-        const auto crsrc = TILED ? row_rsrc(a.codes + (r >> 4) * nrec * 1024, nrec * 1024)
-                                 : row_rsrc(a.codes + r * a.gpr * 16, gpr * 16);
-        const auto srsrc = TILED ? row_rsrc(a.scales + (r >> 4) * nrec * 64, nrec * 64)
-                                 : row_rsrc(a.scales + r * a.gpr, gpr);
-        const uint32_t r16 = static_cast<uint32_t>(r & 15);
+                            for (int t = 0; t < 8; ++t) f[t] = bf16_residual(f[t]);
+                        }
+                    }
+                    float v[8];
 #pragma unroll
-        for (int st = 0; st < NT; ++st) {
-            uint32_t word[kSub];
-            uint32_t sc[kSub];
-#pragma unroll
-            for (int s = 0; s < kSub; ++s) {
-                const int ss = st * kSub + s;
-                const f32x4_t m0 = fm[(ss * 2 + 0) * kWave + lane];
-                const f32x4_t m1 = fm[(ss * 2 + 1) * kWave + lane];
-                const f32x4_t b0 = fb[(ss * 2 + 0) * kWave + lane];
-                const f32x4_t b1 = fb[(ss * 2 + 1) * kWave + lane];
-                float f[8];
-                widen8<kFp16>(buf[st][s], f);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const float d0 = NORM == kLayer ? ((f[t] - mu) - mu_lo) * inv : f[t] * inv;
-                    const float d1 = NORM == kLayer ? ((f[4 + t] - mu) - mu_lo) * inv : f[4 + t] * inv;
-                    f[t] = __builtin_fmaf(d0, m0[t], b0[t]);
-                    f[4 + t] = __builtin_fmaf(d1, m1[t], b1[t]);
-                }
-                // exact bf16 terms of the fp32 values (3 terms cover 24 bits)
-                f32x4_t d0 = {}, d1 = {};
-#pragma unroll
-                for (int term = 0; term < 3; ++term) {
-                    u32x4_t bt;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) bt[i] = bf16_pair_hi(f[2 * i], f[2 * i + 1]);
-                    const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bt);
-                    d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, b, d0, 0, 0, 0);
-                    d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b, d1, 0, 0, 0);
-                    if (term < 2) {
-#pragma unroll
-                        for (int t = 0; t < 8; ++t) f[t] = bf16_residual(f[t]);
+                    for (int t = 0; t < 4; ++t) {
+                        v[t] = d0[t];
+                        v[4 + t] = d1[t];
+                    }
+                    const uint32_t scale_bits = e8m0_scale_bits(group_amax8(v));
+                    sc[s] = scale_bits >> 23;
+                    word[s] = encode8(v, as_f32(scale_bits));
+                    if constexpr (YOUT) {
+                        const auto yrsrc = row_rsrc(a.y + r * a.gpr * kGroup, gpr * kGroup * 4);
+                        const uint32_t off = (static_cast<uint32_t>(kTileGroups * st + 16 * s + j) * kGroup + 8 * q) * 4;
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            u32x4_t{as_u32(v[0]), as_u32(v[1]), as_u32(v[2]), as_u32(v[3])}, yrsrc, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            u32x4_t{as_u32(v[4]), as_u32(v[5]), as_u32(v[6]), as_u32(v[7])}, yrsrc, off + 16, 0, 0);
                     }
                 }
-                float v[8];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    v[t] = d0[t];
-                    v[4 + t] = d1[t];
-                }
-                const uint32_t scale_bits = e8m0_scale_bits(group_amax8(v));
-                sc[s] = scale_bits >> 23;
-                word[s] = encode8(v, as_f32(scale_bits));
-                if constexpr (YOUT) {
-                    const auto yrsrc = row_rsrc(a.y + r * a.gpr * kGroup, gpr * kGroup * 4);
-                    const uint32_t off = (static_cast<uint32_t>(kTileGroups * st + 16 * s + j) * kGroup + 8 * q) * 4;
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        u32x4_t{as_u32(v[0]), as_u32(v[1]), as_u32(v[2]), as_u32(v[3])}, yrsrc, off, 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        u32x4_t{as_u32(v[4]), as_u32(v[5]), as_u32(v[6]), as_u32(v[7])}, yrsrc, off + 16, 0, 0);
+                transpose_words(word);
+                const uint32_t S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
+                const uint32_t g = static_cast<uint32_t>(kTileGroups * st + lane);
+                if constexpr (kStaged) {
+                    stg[sb][wave][g] = u32x4_t{word[0], word[1], word[2], word[3]};
+                    sstg[sb][g * BW + wave] = static_cast<uint8_t>(S);
+                } else {
+                    const uint32_t slot = TILED ? (g >> 2) * 64 + (g & 3) * 16 + r16 : g;
+                    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{word[0], word[1], word[2], word[3]}, crsrc, slot * 16,
+                                                           0, TILED ? 0 : kAuxNT);
+                    __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, slot, 0, 0);
                 }
             }
-            transpose_words(word);
-            const uint32_t S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
-            const uint32_t g = static_cast<uint32_t>(kTileGroups * st + lane);
-            if constexpr (kStaged) {
-                stg[sb][wave][g] = u32x4_t{word[0], word[1], word[2], word[3]};
-                sstg[sb][g * BW + wave] = static_cast<uint8_t>(S);
+            if constexpr (kDouble) {
+#pragma unroll
+                for (int st = 0; st < NT; ++st)
+#pragma unroll
+                    for (int s = 0; s < kSub; ++s) bufA[st][s] = bufB[st][s];
             } else {
-                const uint32_t slot = TILED ? (g >> 2) * 64 + (g & 3) * 16 + r16 : g;
-                __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{word[0], word[1], word[2], word[3]}, crsrc, slot * 16,
-                                                       0, TILED ? 0 : kAuxNT);
-                __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, slot, 0, 0);
+                if (r + a.waves < a.tokens) load_row(bufA, r + a.waves);
             }
-        }
-        if constexpr (kDouble) {
-#pragma unroll
-            for (int st = 0; st < NT; ++st)
-#pragma unroll
-                for (int s = 0; s < kSub; ++s) bufA[st][s] = bufB[st][s];
-        } else {
-            if (r + a.waves < a.tokens) load_row(bufA, r + a.waves);
-        }
         }  // row of this wave
         if constexpr (kStaged) {
             // Every wave's LDS writes complete, then the block meets.  A bare
