@@ -52,7 +52,9 @@
  *   - Limits: channels % 32 == 0, tokens below 2^31, channels at most 2^28,
  *     and tokens * ceil(channels / 2048) below 2^31 (MXQ_ERR_SHAPE).
  *   - NaN or infinite inputs are outside the contract (no error is raised,
- *     the output for such a group is unspecified).
+ *     the output for such a group is unspecified), and so are finite inputs
+ *     whose smoothed or rotated fp32 values overflow (magnitude 2^128 or
+ *     more; e.g. 32 values near the bf16 maximum under a spreading block).
  *   - The library holds no per-call state; calls are thread-safe.  Calls that
  *     write the same output buffers concurrently race, as with any kernel.
  */
