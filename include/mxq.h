@@ -264,7 +264,9 @@ mxq_status mxq_gemm_mxfp4_tiled(const uint8_t *a_tcodes, const uint8_t *a_tscale
  *   positions); channels must be a multiple of 128 (MXQ_ERR_SHAPE).  Each
  *   row is stored on its own, which suits decode-sized batches; at prefill
  *   sizes the row layout plus mxq_tile_mxfp4 moves fewer bytes.  The
- *   padding rows of the last record row are not written.  Other rules as
+ *   padding rows of the last record row are left unspecified (long batches,
+ *   whose rows are staged a record row at a time, write zeros there; short
+ *   ones do not write them).  Other rules as
  *   mxq_norm_rotate_quant. */
 mxq_status mxq_norm_rotate_quant_tiled(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
                                        int64_t x_row_stride, int32_t norm_kind, const float *gamma,
