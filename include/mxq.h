@@ -261,13 +261,12 @@ mxq_status mxq_gemm_mxfp4_tiled(const uint8_t *a_tcodes, const uint8_t *a_tscale
 
 /* mxq_norm_rotate_quant_tiled: mxq_norm_rotate_quant with its codes and
  *   scales written in the tiled layout (bit-identical bytes, other
- *   positions); channels must be a multiple of 128 (MXQ_ERR_SHAPE).  Each
- *   row is stored on its own, which suits decode-sized batches; at prefill
- *   sizes the row layout plus mxq_tile_mxfp4 moves fewer bytes.  The
- *   padding rows of the last record row are left unspecified (long batches,
- *   whose rows are staged a record row at a time, write zeros there; short
- *   ones do not write them).  Other rules as
- *   mxq_norm_rotate_quant. */
+ *   positions); channels must be a multiple of 128 (MXQ_ERR_SHAPE).  Short
+ *   (decode-sized) batches store each row on its own; long batches stage a
+ *   record row, or half of one, in LDS and store whole records.  The
+ *   padding rows of the last record row are left unspecified (the staged
+ *   path writes zeros there, the per-row path does not write them).  Other
+ *   rules as mxq_norm_rotate_quant. */
 mxq_status mxq_norm_rotate_quant_tiled(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
                                        int64_t x_row_stride, int32_t norm_kind, const float *gamma,
                                        const float *beta, float eps, const float *lambda, const uint16_t *r_hat,
