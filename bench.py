@@ -80,6 +80,18 @@ def read_counters(cfg: int, rel: str | None = None, sources=KERNEL_SOURCES):
         return None
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, min_seconds: float):
     import oracle
     orc = oracle.default()
@@ -94,7 +106,7 @@ def cpu_baseline(wl, min_seconds: float):
             break
     med = statistics.median(times)
     return {"value": round(elems / med / 1e9, 4), "unit": "Gelem/s", "cores": orc.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": host_cpu_model(),
             "sample": f"the full {wl.tokens}x{wl.channels} batch, {len(times)} repetitions "
                       f"({sum(times):.1f} s of CPU wall time), median {med * 1e3:.0f} ms each"}
 
@@ -149,7 +161,8 @@ def bench_calibration(args):
         CAL.greedy_givens(xw_host, 128)
         dt = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": round(dt * 1e3, 1), "unit": "ms per search", "cores": 1,
-                                  "kind": "oracle", "sample": "the same block, one search (NumPy fp64)"}
+                                  "kind": "oracle", "cpu": host_cpu_model(),
+                                  "sample": "the same block, one search (NumPy fp64)"}
     print(json.dumps(result), flush=True)
 
 
@@ -274,7 +287,7 @@ def bench_gemm(args):
                      if args.decode else round(2.0 * rows * N * K / med / 1e12, 5))
         result["cpu_baseline"] = {
             "value": cpu_value, "unit": "GB/s" if args.decode else "TFLOP/s",
-            "cores": max(blas, orc.num_threads()), "kind": "oracle",
+            "cores": max(blas, orc.num_threads()), "kind": "oracle", "cpu": host_cpu_model(),
             "sample": f"the first {rows} activation rows against all {N} weight rows (exact dequantization, "
                       f"fp64 matmul), {len(times)} repetitions, median {med:.2f} s each"}
     print(json.dumps(result), flush=True)
@@ -358,7 +371,7 @@ def bench_norm(args):
                 break
         med = statistics.median(times)
         result["cpu_baseline"] = {"value": round(rows * C / med / 1e9, 4), "unit": "Gelem/s",
-                                  "cores": orc.num_threads(), "kind": "oracle",
+                                  "cores": orc.num_threads(), "kind": "oracle", "cpu": host_cpu_model(),
                                   "sample": f"the first {rows} rows of the batch, {len(times)} repetitions, "
                                             f"median {med * 1e3:.0f} ms each"}
     print(json.dumps(result), flush=True)
