@@ -229,3 +229,81 @@ def test_tiled_outputs_from_strided_rows(dev):
         ua = O.untile_mxfp4(a[0].cpu().numpy(), a[1].cpu().numpy(), T, C)
         ub = O.untile_mxfp4(b[0].cpu().numpy(), b[1].cpu().numpy(), T, C)
         assert np.array_equal(ua[0], ub[0]) and np.array_equal(ua[1], ub[1])
+
+
+def _random_shapes(seed, n, t_max, c_max):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, t_max + 1)), 128 * int(rng.integers(1, c_max // 128 + 1))) for _ in range(n)]
+
+
+def _large_shapes(seed, n):
+    # long batches over wide rows: units of 16 rows x super-tile columns reach the
+    # grid's resident waves, so the tiled quantizer takes its 16-row-unit path
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(8192, 16001)), 128 * int(rng.integers(49, 113))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("T,C", _random_shapes(9700, 6, 6000, 8192) + _large_shapes(9703, 4))
+def test_random_shapes_quantizer_tiled_same_bytes(dev, T, C):
+    """Seeded random shapes on both sides of the 16-row-unit switch, with
+    partial super-tile columns: the tiled output equals the repacked row
+    output byte for byte (bf16 without Λ, fp16 with Λ)."""
+    rng = np.random.default_rng(T * 7 + C)
+    for dtype, with_lam in ((torch.bfloat16, False), (torch.float16, True)):
+        x = W.random_activations(rng, T, C, dtype, scale=2.0).to(dev)
+        lam = torch.from_numpy(np.exp(0.5 * rng.standard_normal(C)).astype(np.float32)).to(dev) if with_lam else None
+        r = W.bf16_matrix(W.qr_orthogonal(rng)).to(dev)
+        print(f"  quantizer tiled T={T} C={C} {dtype} lam={with_lam}", flush=True)
+        ref = mxq.tile_mxfp4(*mxq.rotate_quant(x, r, lam))
+        nc, ns = mxq.tiled_sizes(T, C)
+        tc = torch.zeros(nc, dtype=torch.uint8, device=dev)
+        ts = torch.zeros(ns, dtype=torch.uint8, device=dev)
+        mxq.rotate_quant_tiled(x, r, lam, tcodes=tc, tscales=ts)
+        torch.cuda.synchronize()
+        assert torch.equal(tc, ref[0]) and torch.equal(ts, ref[1])
+
+
+@pytest.mark.parametrize("T,C", _random_shapes(9701, 10, 6000, 8192))
+def test_random_shapes_norm_tiled_same_bytes(dev, T, C):
+    """Seeded random shapes on both sides of the staged-store switch (record
+    rows staged in LDS for long batches): the tiled norm output equals the
+    repacked row output byte for byte (RMSNorm bf16, LayerNorm fp16 with β)."""
+    rng = np.random.default_rng(T * 5 + C)
+    for norm, dtype, with_beta in (("rms", torch.bfloat16, False), ("layer", torch.float16, True)):
+        x = W.random_activations(rng, T, C, dtype, scale=2.0).to(dev)
+        gamma = torch.from_numpy(rng.uniform(0.5, 1.5, C).astype(np.float32)).to(dev)
+        beta = torch.from_numpy(rng.normal(0, 0.1, C).astype(np.float32)).to(dev) if with_beta else None
+        lam = torch.from_numpy(np.exp(0.5 * rng.standard_normal(C)).astype(np.float32)).to(dev)
+        r = W.bf16_matrix(W.qr_orthogonal(rng)).to(dev)
+        print(f"  norm tiled T={T} C={C} {norm} {dtype}", flush=True)
+        ref = mxq.tile_mxfp4(*mxq.norm_rotate_quant(x, r, gamma, beta, lam, norm=norm))
+        nc, ns = mxq.tiled_sizes(T, C)
+        tc = torch.zeros(nc, dtype=torch.uint8, device=dev)
+        ts = torch.zeros(ns, dtype=torch.uint8, device=dev)
+        mxq.norm_rotate_quant_tiled(x, r, gamma, beta, lam, norm=norm, tcodes=tc, tscales=ts)
+        torch.cuda.synchronize()
+        assert torch.equal(tc, ref[0]) and torch.equal(ts, ref[1])
+
+
+def _random_products(seed, n):
+    # every other M at most 64 (the split-K decode kernel), the rest above it
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 65) if i % 2 else rng.integers(65, 3000)), int(rng.integers(1, 3000)),
+             128 * int(rng.integers(1, 33))) for i in range(n)]
+
+
+@pytest.mark.parametrize("M,N,K", _random_products(9702, 12))
+def test_random_shapes_product_same_bits(dev, M, N, K):
+    """Seeded random products (decode and large kernels, ragged tiles, odd
+    stage counts): the tiled product equals the row-layout product bit for
+    bit, fp32 and bf16 out."""
+    rng = np.random.default_rng(M * 3 + N * 11 + K)
+    a = [_u8(t, dev) for t in W.random_mxfp4(rng, M, K)]
+    b = [_u8(t, dev) for t in W.random_mxfp4(rng, N, K)]
+    ta, tb = mxq.tile_mxfp4(*a), mxq.tile_mxfp4(*b)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        print(f"  random product M={M} N={N} K={K} {out_dtype}", flush=True)
+        y_row = mxq.gemm_mxfp4(*a, *b, out_dtype)
+        y_t = mxq.gemm_mxfp4_tiled(*ta, *tb, M, N, K, out_dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(y_t, y_row)
