@@ -39,6 +39,7 @@ KERNEL_SOURCES = ("mxfp4_activation_rotation_amd/csrc/mxq.hip",
 COUNTERS = {3: "profiles/rotate_quant_bf16_8192x14336_hbm_counters.txt"}
 GEMM_SOURCES = ("mxfp4_activation_rotation_amd/csrc/mxq_gemm.hip",)
 GEMM_COUNTERS = "profiles/gemm_mxfp4_tiled_8192x4096x14336_hbm_counters.txt"
+DECODE_COUNTERS = {16: "profiles/gemm_mxfp4_tiled_decode_16x4096x14336_hbm_counters.txt"}
 FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 (E2M1) matrix-core peak
 WORKLOAD_NAMES = {
     2: "QKV-input shape: bf16 2048x4096, 0.5% outlier channels x20, lognormal lambda, seeded orthogonal R",
@@ -171,8 +172,9 @@ def bench_gemm(args):
     (8192 x 14336, from mxq_rotate_quant on the headline activations) with
     absorbed, quantized synthetic weights (4096 x 14336), bf16 output.  The
     operands (88 MB) are built once on the GPU before the timed region.
-    With --decode, the activations are 16 tokens of the same batch: the
-    product is bound by reading the weights, so its roofline is HBM.  Both
+    With --decode, the activations are the first --rows tokens (1..64,
+    default 16) of the same batch: the product is bound by reading the
+    weights, so its roofline is HBM.  Both
     operands are in the fragment-tiled layout (the activations written so by
     the quantizer, the weights repacked once offline); --row-layout times the
     row-layout operands instead."""
@@ -193,7 +195,7 @@ def bench_gemm(args):
     weight_bytes = N * (K // 2 + K // 32)
     tiled = not args.row_layout
     if args.decode:
-        M = 16
+        M = args.rows
         ac, asc = ac[:M].contiguous(), asc[:M].contiguous()
     if tiled:
         ta, tsa = mxq.rotate_quant_tiled(wl.x[:M].contiguous().to(dev), r, lam)
@@ -228,7 +230,12 @@ def bench_gemm(args):
     wall = time.perf_counter() - t0
     mean_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
     achieved = flop / mean_launch_s / 1e12
-    hbm = None if (args.decode or not tiled) else read_counters(0, GEMM_COUNTERS, GEMM_SOURCES)
+    if not tiled:
+        hbm = None
+    elif args.decode:
+        hbm = read_counters(0, DECODE_COUNTERS.get(M, ""), GEMM_SOURCES)
+    else:
+        hbm = read_counters(0, GEMM_COUNTERS, GEMM_SOURCES)
     result = {
         "metric": "W4A4 MXFP4 GEMM throughput (consumer of the quantized activations): TFLOP/s",
         "value": round(flop * args.steps / wall / 1e12, 1),
@@ -257,11 +264,13 @@ def bench_gemm(args):
         result["metric"] = "decode-shaped W4A4 MXFP4 GEMM: GB/s of weights streamed"
         result["value"] = round(algo * args.steps / wall / 1e9, 1)
         result["unit"] = "GB/s"
-        result["config"]["workload"] = ("decode product: 16 tokens of the headline batch, rotated and MXFP4-"
-                                        "quantized, times absorbed MXFP4 weights 4096x14336, bf16 output")
+        result["config"]["workload"] = (f"decode product: {M} token{'s' if M > 1 else ''} of the headline batch, "
+                                        "rotated and MXFP4-quantized, times absorbed MXFP4 weights 4096x14336, "
+                                        "bf16 output")
         result["config"]["weight_sets"] = n_w
         result["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                              "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}
+                              "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                              "traffic": None if hbm is None else round(hbm)}
     if not args.no_cpu_baseline:
         import oracle
         orc = oracle.default()
@@ -395,7 +404,9 @@ def main():
                     help="time the consumer instead: the W4A4 MXFP4 product of the headline batch's codes "
                          "with absorbed, quantized weights (8192x14336 by 4096x14336)")
     ap.add_argument("--decode", action="store_true",
-                    help="with --gemm: 16 activation rows (decode), timed against HBM bandwidth")
+                    help="with --gemm: a few activation rows (decode), timed against HBM bandwidth")
+    ap.add_argument("--rows", type=int, default=16,
+                    help="with --gemm --decode: activation rows, 1..64 (default 16)")
     ap.add_argument("--row-layout", action="store_true",
                     help="with --gemm: row-layout operands instead of fragment-tiled ones")
     ap.add_argument("--norm", action="store_true",
@@ -415,9 +426,12 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: this path needs no cross-GPU exchange (each GPU quantizes its own "
-              f"token shard), and runs on more than one GPU are not part of this build "
-              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+              f"token shard), so the whole-job rate is the one-GPU rate times the GPU count, and the bench "
+              f"does not launch on several GPUs (asked for --gpus {args.gpus}, WORLD_SIZE={world}).",
+              file=sys.stderr)
         sys.exit(2)
+    if not 1 <= args.rows <= 64:
+        ap.error("--rows must be in 1..64 (the decode-shaped product kernel's range)")
 
     import numpy as np
     import torch
