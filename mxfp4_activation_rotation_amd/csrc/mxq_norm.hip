@@ -174,19 +174,23 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
     const char* xb = static_cast<const char*>(a.x);
     // (row indices are uniform; readfirstlane tells the compiler so, or it
     // wraps every buffer access in a loop over distinct descriptors)
-    auto load_row = [&](u32x4_t (&buf)[NT][kSub], int64_t r_any) {
+    auto load_tile = [&](u32x4_t (&tile)[kSub], int64_t r_any, int st) {
         const int64_t r = __builtin_amdgcn_readfirstlane(static_cast<int>(r_any));
         const auto rsrc = row_rsrc(xb + r * a.stride * 2, row_bytes);
 #pragma unroll
-        for (int st = 0; st < NT; ++st)
+        for (int s = 0; s < kSub; ++s) {
+            const uint32_t off = (static_cast<uint32_t>(kTileGroups * st + 16 * s + j) * kGroup + 8 * q) * 2;
+            tile[s] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kAuxNT);
+        }
+    };
+    auto load_row = [&](u32x4_t (&buf)[NT][kSub], int64_t r_any) {
 #pragma unroll
-            for (int s = 0; s < kSub; ++s) {
-                const uint32_t off = (static_cast<uint32_t>(kTileGroups * st + 16 * s + j) * kGroup + 8 * q) * 2;
-                buf[st][s] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, kAuxNT);
-            }
+        for (int st = 0; st < NT; ++st) load_tile(buf[st], r_any, st);
     };
     // Two row buffers alternate when they fit in registers (up to 4096
     // channels): the next row is in flight while the current one computes.
+    // Longer rows keep one buffer, and each super-tile of the next row loads
+    // into its registers as soon as the current row's super-tile is encoded.
     constexpr bool kDouble = NT <= 2;
     u32x4_t bufA[NT][kSub], bufB[NT][kSub];
     if (w < a.tokens) load_row(bufA, w);
@@ -357,14 +361,15 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
                                                            0, TILED ? 0 : kAuxNT);
                     __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, slot, 0, 0);
                 }
+                if constexpr (!kDouble) {
+                    if (r + a.waves < a.tokens) load_tile(bufA[st], r + a.waves, st);
+                }
             }
             if constexpr (kDouble) {
 #pragma unroll
                 for (int st = 0; st < NT; ++st)
 #pragma unroll
                     for (int s = 0; s < kSub; ++s) bufA[st][s] = bufB[st][s];
-            } else {
-                if (r + a.waves < a.tokens) load_row(bufA, r + a.waves);
             }
         }  // row of this wave
         if constexpr (kStaged) {
