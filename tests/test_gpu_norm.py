@@ -70,6 +70,18 @@ def test_norm_against_oracle(dev, orc, norm, T, C, dtype):
     full_check(wl.x, wl.r_hat, wl.gamma, wl.beta, wl.lam, norm, wl.eps, dev, orc)
 
 
+@pytest.mark.parametrize("norm,T,C,dtype", [("rms", 3000, 8192, torch.bfloat16), ("layer", 3000, 8192, torch.float16),
+                                            ("rms", 2600, 16384, torch.bfloat16),
+                                            ("layer", 2600, 16384, torch.float16)])
+def test_norm_long_rows_several_per_wave(dev, orc, norm, T, C, dtype):
+    """Rows longer than 4096 channels keep one row buffer, and the next row
+    loads super-tile by super-tile while the current one is encoded.  With
+    more rows than the grid's waves (about 2048 at these widths), waves take
+    two rows, so prefetched super-tiles are checked against the oracle too."""
+    wl = W.norm_workload(T, C, seed=4700 + C + T, dtype=dtype, with_beta=(norm == "layer"))
+    full_check(wl.x, wl.r_hat, wl.gamma, wl.beta, wl.lam, norm, wl.eps, dev, orc)
+
+
 def test_norm_without_lambda_identity_block(dev, orc):
     wl = W.norm_workload(128, 512, seed=4201)
     full_check(wl.x, W.identity_r(), wl.gamma, None, None, "rms", wl.eps, dev, orc)
