@@ -121,6 +121,48 @@ def test_gemm_strided_output_and_tails(dev, orc):
     assert np.all(full[:, N:] == 7.25)  # columns past N untouched
 
 
+def _sparse_operand(rng, rows, K, positions, per_row):
+    """MXFP4 operand that is zero except per_row codes in each row, drawn from
+    positions (nonzero magnitudes), with scales in 2^-2..2^2 so that every sum
+    of a few products is exact in fp32."""
+    codes = np.zeros((rows, K // 2), dtype=np.uint8)
+    scales = rng.integers(125, 130, size=(rows, K // 32), dtype=np.uint8)
+    for i in range(rows):
+        for p in rng.choice(positions, size=per_row, replace=False):
+            c = int(rng.integers(1, 8)) | (8 if rng.integers(0, 2) else 0)
+            codes[i, p // 2] |= np.uint8(c << (4 * (p % 2)))
+    return codes, scales
+
+
+@pytest.mark.parametrize("M", [3, 80])
+def test_gemm_max_k_sparse_exact(dev, orc, M):
+    """K = 2^24, the largest the header allows: record and byte offsets of
+    every operand reach their maximum.  Nonzero codes sit at positions spread
+    over all of K (first and last included); the expected values are the
+    oracle's product over just the groups that hold them (zero codes add
+    nothing), and every output is exact in fp32, so both layouts must match
+    it exactly, on the decode-shaped kernel (M = 3) and the tiled one."""
+    K, N = 1 << 24, 24
+    rng = np.random.default_rng(4242 + M)
+    pos = np.unique(np.concatenate([[0, K - 1, K // 2, K - 32, 31],
+                                    rng.choice(K, size=40, replace=False)]))
+    ac, asc = _sparse_operand(rng, M, K, pos, 4)
+    bc, bsc = _sparse_operand(rng, N, K, pos, 8)
+    groups = np.unique(pos // 32)
+    cols = (groups[:, None] * 16 + np.arange(16)[None, :]).ravel()
+    ref, _ = O.gemm_mxfp4(ac[:, cols], asc[:, groups], bc[:, cols], bsc[:, groups], orc)
+    assert np.count_nonzero(ref) > 0
+    print(f"  K=2^24 M={M} N={N}: {len(groups)} groups hold nonzeros, "
+          f"{np.count_nonzero(ref)} nonzero outputs", flush=True)
+    a = [_dev_u8(t, dev) for t in (ac, asc)]
+    b = [_dev_u8(t, dev) for t in (bc, bsc)]
+    y = mxq.gemm_mxfp4(*a, *b, torch.float32)
+    yt = mxq.gemm_mxfp4_tiled(*mxq.tile_mxfp4(*a), *mxq.tile_mxfp4(*b), M, N, K, torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), ref)
+    assert np.array_equal(yt.cpu().numpy().astype(np.float64), ref)
+
+
 def test_gemm_empty_and_zero_k(dev):
     z = torch.empty((0, 128), dtype=torch.uint8, device=dev)
     zs = torch.empty((0, 8), dtype=torch.uint8, device=dev)
