@@ -229,6 +229,35 @@ def test_ragged_and_strided(dev, orc, T, C, extra):
     assert np.array_equal(cq.cpu().numpy(), c_ref) and np.array_equal(sq.cpu().numpy(), s_ref)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_very_long_rows(dev, orc, dtype):
+    """Rows of 2^21 + 384 channels (1025 super-tile columns, the last one 12
+    of 64 groups): the fused path with and without Λ against the oracle, the
+    tiled output against the repacked row output, and plain quantization of
+    the fp32 rows bit-exact."""
+    T, C = 3, (1 << 21) + 384
+    rng = np.random.default_rng(2 ** 21 + (dtype == torch.float16))
+    x = W.random_activations(rng, T, C, dtype, scale=2.0)
+    x[1, C - 1] = 700.0
+    r = W.bf16_matrix(W.qr_orthogonal(rng))
+    lam = np.exp(0.3 * rng.standard_normal(C)).astype(np.float32)
+    print(f"  long rows {T}x{C} {dtype}", flush=True)
+    full_fused_check(x, None, r, dev, orc)
+    full_fused_check(x, lam, r, dev, orc)
+    xd, lam_d, rd = _to_dev(x, lam, r, dev)
+    ref = mxq.tile_mxfp4(*mxq.rotate_quant(xd, rd, lam_d))
+    nc, ns = mxq.tiled_sizes(T, C)
+    tc = torch.zeros(nc, dtype=torch.uint8, device=dev)  # padding rows stay zero, as in the repack
+    ts = torch.zeros(ns, dtype=torch.uint8, device=dev)
+    mxq.rotate_quant_tiled(xd, rd, lam_d, tcodes=tc, tscales=ts)
+    torch.cuda.synchronize()
+    assert torch.equal(tc, ref[0]) and torch.equal(ts, ref[1])
+    x32 = x.to(torch.float32)
+    cq, sq = mxq.quant(x32.to(dev))
+    c_ref, s_ref = orc.quant(x32)
+    assert np.array_equal(cq.cpu().numpy(), c_ref) and np.array_equal(sq.cpu().numpy(), s_ref)
+
+
 def test_empty_inputs(dev):
     x = torch.empty((0, 256), dtype=torch.bfloat16, device=dev)
     codes, scales = mxq.rotate_quant(x, W.identity_r().to(dev))
