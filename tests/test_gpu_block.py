@@ -79,6 +79,19 @@ def test_block_against_oracle(dev, orc, B, dtype, with_lam):
     full_check(x, lam, r, dev, orc)
 
 
+@pytest.mark.parametrize("B", [16, 32, 64, 128])
+def test_block_very_long_rows(dev, orc, B):
+    """Rows of 2^20 + 640 channels (513 super-tile columns, the last one a
+    partial 20 of 64 groups), fp16 with Λ, against the oracle."""
+    rng = np.random.default_rng(7100 + B)
+    T, C = 2, (1 << 20) + 640
+    x = W.random_activations(rng, T, C, torch.float16, scale=2.0)
+    x[1, C - 2] = 500.0
+    lam = np.exp(0.5 * rng.standard_normal(C)).astype(np.float32)
+    r = W.bf16_matrix(W.qr_orthogonal(rng, B))
+    full_check(x, lam, r, dev, orc)
+
+
 @pytest.mark.parametrize("dtype,with_lam", [(torch.bfloat16, False), (torch.bfloat16, True), (torch.float16, True)])
 def test_block32_same_bits_as_main_kernel(dev, dtype, with_lam):
     rng = np.random.default_rng(7101)
