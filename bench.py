@@ -36,7 +36,10 @@ HBM_PEAK_GBPS = 8000.0
 BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0  # bf16/fp16 in, FP4 codes + E8M0 scales out
 KERNEL_SOURCES = ("mxfp4_activation_rotation_amd/csrc/mxq.hip",
                   "mxfp4_activation_rotation_amd/csrc/mxq_device.h")
-COUNTERS = {3: "profiles/rotate_quant_bf16_8192x14336_hbm_counters.txt"}
+COUNTERS = {3: "profiles/rotate_quant_bf16_8192x14336_hbm_counters.txt",
+            2: "profiles/rotate_quant_bf16_lambda_2048x4096_hbm_counters.txt",
+            4: "profiles/rotate_quant_bf16_lambda_decode_16x8192_hbm_counters.txt",
+            5: "profiles/rotate_quant_fp16_lambda_32768x8192_hbm_counters.txt"}
 GEMM_SOURCES = ("mxfp4_activation_rotation_amd/csrc/mxq_gemm.hip",)
 GEMM_COUNTERS = "profiles/gemm_mxfp4_tiled_8192x4096x14336_hbm_counters.txt"
 DECODE_COUNTERS = {16: "profiles/gemm_mxfp4_tiled_decode_16x4096x14336_hbm_counters.txt"}
@@ -420,6 +423,10 @@ def main():
                     help="rotate: mxq_rotate_quant (the headline); quant: mxq_quant (no smoothing, no "
                          "rotation); dequant: mxq_dequant of the batch's codes to bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="default run only: skip the extra lines of workloads 2, 4 and 5")
+    ap.add_argument("--extra-steps", type=int, default=0,
+                    help="timed calls of each extra workload (0 = 2000, 1024 and 400 for workloads 2, 4, 5)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
 
@@ -452,18 +459,51 @@ def main():
     if args.norm:
         bench_norm(args)
         return
+    result = time_quant(args, args.workload, args.steps, args.warmup, graph=args.graph)
+    default_run = (args.workload == 3 and not (args.block or args.tiled or args.graph) and args.op == "rotate"
+                   and not args.no_extra_workloads)
+    if default_run:
+        # the other seeded workloads of the same path, timed in the same process
+        # (fewer steps; each its own buffer rotation and warm-up)
+        extra = {}
+        for wid, steps in ((2, 2000), (4, 1024), (5, 400)):
+            steps = args.extra_steps or steps
+            warm = min(args.warmup, 300)
+            r = time_quant(args, wid, steps, warm, graph=False, core_only=True)
+            if wid == 4:
+                g = time_quant(args, wid, steps, warm, graph=True, core_only=True)
+                r["graph_launch_us_mean"] = g["launch_us_mean"]
+                r["graph_gelem_s"] = g["gelem_s"]
+            extra[str(wid)] = r
+        result["workloads"] = extra
+    if not args.no_cpu_baseline and not args.block and args.op == "rotate":
+        import workloads
+        result["cpu_baseline"] = cpu_baseline(workloads.make_config(args.workload), args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def time_quant(args, wid, steps, warmup, graph=False, core_only=False):
+    """Time `steps` calls of the quantize path on workload `wid` (buffer sets
+    rotated so each call reads cold data; one event pair around the timed
+    calls on the launch stream).  core_only: the per-workload fields only."""
+    import numpy as np
+    import torch
+
+    import mxfp4_activation_rotation_amd as mxq
+    import workloads
+
     dev = torch.device("cuda:0")
-    wl = workloads.make_config(args.workload)
-    call_tokens = workloads.SHAPES[4][0] if args.workload == 4 else wl.tokens
+    wl = workloads.make_config(wid)
+    call_tokens = workloads.SHAPES[4][0] if wid == 4 else wl.tokens
     C = wl.channels
     elems = call_tokens * C
     step_bytes = elems * BYTES_PER_ELEM
 
     n_buf = args.buffers or max(2, int(np.ceil(768e6 / step_bytes)) + 1)
-    if args.workload == 4:
+    if wid == 4:
         n_buf = wl.tokens // call_tokens  # the 256 distinct decode inputs
     x_all = wl.x.to(dev)
-    xs = [x_all[i * call_tokens:(i + 1) * call_tokens] for i in range(n_buf)] if args.workload == 4 \
+    xs = [x_all[i * call_tokens:(i + 1) * call_tokens] for i in range(n_buf)] if wid == 4 \
         else [x_all] + [x_all.clone() for _ in range(n_buf - 1)]
     lam = torch.from_numpy(wl.lam).to(dev) if wl.lam is not None else None
     r = wl.r_hat.to(dev)
@@ -498,22 +538,22 @@ def main():
         else:
             mxq.rotate_quant(xs[i % n_buf], r, lam, codes=c, scales=s)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
-    graph = None
-    if args.graph:
+    hip_graph = None
+    if graph:
         # Capture exactly the K timed launches (same buffers, same order).
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
+        hip_graph = torch.cuda.CUDAGraph()
         capture_stream = torch.cuda.Stream()
         capture_stream.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(capture_stream):
-            graph.capture_begin()
-            for i in range(args.steps):
-                step(args.warmup + i)
-            graph.capture_end()
+            hip_graph.capture_begin()
+            for i in range(steps):
+                step(warmup + i)
+            hip_graph.capture_end()
         torch.cuda.current_stream().wait_stream(capture_stream)
-        graph.replay()  # one untimed replay after capture
+        hip_graph.replay()  # one untimed replay after capture
     # One event pair brackets the timed region on the launch stream (the
     # binding launches on torch's current stream); events between launches
     # would add several microseconds of queue work to every step.
@@ -522,48 +562,29 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
-    if graph is not None:
-        graph.replay()
+    if hip_graph is not None:
+        hip_graph.replay()
     else:
-        for i in range(args.steps):
-            step(args.warmup + i)
+        for i in range(steps):
+            step(warmup + i)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    mean_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
+    mean_launch_s = ev0.elapsed_time(ev1) / 1e3 / steps
 
     achieved = step_bytes / mean_launch_s / 1e9
-    value = elems * args.steps / wall / 1e9
-    hbm = None if (args.block or args.tiled or args.op != "rotate") else read_counters(args.workload)
-    result = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "Gelem/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if wl.x.dtype == torch.bfloat16 else "fp16",
-        "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[args.workload], "tokens": call_tokens, "channels": C,
-                   "x_dtype": str(wl.x.dtype).replace("torch.", ""), "lambda": wl.lam is not None,
-                   "r_hat": (f"seeded random Hadamard {args.block}x{args.block} (block-size variant kernel)"
-                             if args.block else "bf16 32x32"),
-                   "buffer_sets": n_buf, "parallelism": "single GPU",
-                   "output_layout": "fragment-tiled records" if args.tiled else "row layout",
-                   "launch": "hip graph of the K launches" if args.graph else "eager launches"},
-        "hbm_gbps": round(value * BYTES_PER_ELEM, 1),
-        "pct_hbm_peak": round(100 * value * BYTES_PER_ELEM / HBM_PEAK_GBPS, 2),
+    value = elems * steps / wall / 1e9
+    hbm = None if (args.block or args.tiled or args.op != "rotate") else read_counters(wid)
+    core = {
+        "workload": WORKLOAD_NAMES[wid], "tokens": call_tokens, "channels": C,
+        "x_dtype": str(wl.x.dtype).replace("torch.", ""), "lambda": wl.lam is not None,
+        "steps": steps, "gelem_s": round(value, 2), "hbm_gbps": round(value * BYTES_PER_ELEM, 1),
         "launch_us_mean": round(mean_launch_s * 1e6, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None if hbm is None else round(hbm)},
-        "kernel_source_hash": kernel_source_hash(),
     }
-    if args.workload == 4:
+    if wid == 4 and not graph:
         # decode-shaped calls: per-call latency, each call bracketed by its own
         # event pair (outside the timed region above)
         lat = []
@@ -575,8 +596,40 @@ def main():
             e1.record()
             e1.synchronize()
             lat.append(e0.elapsed_time(e1) * 1e3)
-        result["call_latency_us"] = {"p50": round(float(np.percentile(lat, 50)), 2),
-                                     "p99": round(float(np.percentile(lat, 99)), 2), "calls": len(lat)}
+        core["call_latency_us"] = {"p50": round(float(np.percentile(lat, 50)), 2),
+                                   "p99": round(float(np.percentile(lat, 99)), 2), "calls": len(lat)}
+        core["aggregate_gbps"] = core["hbm_gbps"]
+    if core_only:
+        return core
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall / steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.x.dtype == torch.bfloat16 else "fp16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[wid], "tokens": call_tokens, "channels": C,
+                   "x_dtype": str(wl.x.dtype).replace("torch.", ""), "lambda": wl.lam is not None,
+                   "r_hat": (f"seeded random Hadamard {args.block}x{args.block} (block-size variant kernel)"
+                             if args.block else "bf16 32x32"),
+                   "buffer_sets": n_buf, "parallelism": "single GPU",
+                   "output_layout": "fragment-tiled records" if args.tiled else "row layout",
+                   "launch": "hip graph of the K launches" if graph else "eager launches"},
+        "hbm_gbps": core["hbm_gbps"],
+        "pct_hbm_peak": round(100 * value * BYTES_PER_ELEM / HBM_PEAK_GBPS, 2),
+        "launch_us_mean": core["launch_us_mean"],
+        "roofline": core["roofline"],
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    for k in ("call_latency_us",):
+        if k in core:
+            result[k] = core[k]
     if args.block:
         result["kernel_source_hash"] = kernel_source_hash(("mxfp4_activation_rotation_amd/csrc/mxq_block.hip",
                                                            "mxfp4_activation_rotation_amd/csrc/mxq_device.h"))
@@ -585,9 +638,7 @@ def main():
                             else "MXFP4 dequantization to bf16 (mxq_dequant) throughput: Gelem/s")
         result["config"]["op"] = args.op
         result["kernel_source_hash"] = kernel_source_hash()
-    if not args.no_cpu_baseline and not args.block and args.op == "rotate":
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    return result
 
 
 if __name__ == "__main__":

@@ -93,7 +93,18 @@ typedef enum { MXQ_NORM_RMS = 0, MXQ_NORM_LAYER = 1 } mxq_norm_kind;
  * accumulation.  The activations are split into bf16 terms whose sum is
  * exactly the fp32 value of x' (bf16 x: 1 term; fp16 x: 2 terms; with lambda:
  * 3 terms of x' = x * rcp(lambda), rcp the hardware reciprocal, within 1 ulp),
- * so the products are exact and only the fp32 accumulation rounds.
+ * so the products are exact and only the fp32 accumulation rounds.  That
+ * holds at every magnitude: a group whose rotated maximum is below 2^-64
+ * (whose bf16 terms or products would fall below bf16's or fp32's normal
+ * range) is recomputed from x' * 2^k, k <= 64 a power-of-two shift chosen
+ * from the group's largest |x'| (x * (factor * 2^k) formed exactly in fp64
+ * and rounded to fp32 once), and encoded with its scale reduced by k.  So
+ * every rotated value of a group g is within the fp32 accumulation error of
+ * its 32 terms plus about 2^-23 ||x'_g||_2 (the rounding of x' to fp32) of
+ * the exact x'_g R, for groups of any size; the y_rot output
+ * (mxq_rotate_quant_ex) of a group below fp32's normal range is that value
+ * rounded to fp32.  Rows holding such groups cost a second pass; ordinary
+ * data has none.
  * lambda entries must be finite normal fp32 values with |lambda| in
  * [2^-126, 2^126]; others give unspecified codes for their groups. */
 mxq_status mxq_rotate_quant(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
@@ -149,9 +160,13 @@ mxq_status mxq_rotate_quant_block(const void *x, int32_t x_dtype, int64_t tokens
  * then the rotation and encoding of mxq_rotate_quant.
  *   x        BF16 or FP16, [tokens][x_row_stride], channels <= 16384
  *   gamma    fp32 [channels], required; beta fp32 [channels] or NULL (zero);
- *   lambda   fp32 [channels] or NULL (ones); eps >= 0 (MXQ_ERR_SHAPE if
- *            negative or NaN).  A row of zeros with eps = 0 is outside the
- *            contract (0 / 0).
+ *   lambda   fp32 [channels] or NULL (ones); eps finite and >= 0
+ *            (MXQ_ERR_SHAPE if negative, infinite or NaN).  A row whose
+ *            variance is zero (a row of zeros for RMSNorm, a constant row
+ *            for LayerNorm) with eps = 0 is outside the contract (0 / 0).
+ *            The per-channel factors gamma_c / lambda_c and beta_c / lambda_c,
+ *            rounded to fp32, must each be 0 or of magnitude in
+ *            [2^-64, 2^64); others give unspecified codes for their groups.
  *   y_rot    NULL, or fp32 [tokens][channels] receiving the rotated values
  * Arithmetic: row sums in fp32 per 128 values (exact products of the 16-bit
  * inputs on the matrix cores; LayerNorm's centred sums per 8 values on the
@@ -161,7 +176,15 @@ mxq_status mxq_rotate_quant_block(const void *x, int32_t x_dtype, int64_t tokens
  * rounded to fp32; x'_c = fma(n_c, gamma_c/lambda_c,
  * beta_c/lambda_c) in fp32 (the two factors formed once per block with IEEE
  * division); the product with the block as in mxq_rotate_quant (3 exact
- * bf16 terms).  Same layout, alignment (gamma, beta, lambda: 4 bytes) and
+ * bf16 terms).  Every finite 16-bit row is in range: a bf16 row whose fp32
+ * sum of squares leaves [2^-80, 2^1000] (squares beyond fp32's range, or lost
+ * below it) is scaled by a power of two 2^kr taken from its largest |h| and
+ * its statistics retaken, with eps scaled by 2^(2 kr), which leaves the
+ * normalized row unchanged; a group whose rotated maximum is below 2^-64 is
+ * recomputed from x' * 2^k as in mxq_rotate_quant, with x' * 2^k formed as
+ * fma(d * 2^k, gamma/lambda, (beta/lambda) * 2^k) from 1/sqrt in fp64 times
+ * 2^k.  Such rows cost a second pass over the rows of their wave; ordinary
+ * data has none.  Same layout, alignment (gamma, beta, lambda: 4 bytes) and
  * error rules as mxq_rotate_quant; norm_kind other than the two values gives
  * MXQ_ERR_DTYPE. */
 mxq_status mxq_norm_rotate_quant(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
@@ -261,12 +284,12 @@ mxq_status mxq_gemm_mxfp4_tiled(const uint8_t *a_tcodes, const uint8_t *a_tscale
 
 /* mxq_norm_rotate_quant_tiled: mxq_norm_rotate_quant with its codes and
  *   scales written in the tiled layout (bit-identical bytes, other
- *   positions); channels must be a multiple of 128 (MXQ_ERR_SHAPE).  Short
- *   (decode-sized) batches store each row on its own; long batches stage a
- *   record row, or half of one, in LDS and store whole records.  The
- *   padding rows of the last record row are left unspecified (the staged
- *   path writes zeros there, the per-row path does not write them).  Other
- *   rules as mxq_norm_rotate_quant. */
+ *   positions); channels must be a multiple of 128 (MXQ_ERR_SHAPE) and
+ *   tiled_scales 16-byte aligned (MXQ_ERR_ALIGN).  Short (decode-sized)
+ *   batches store each row on its own; long batches stage a record row, or
+ *   half of one, in LDS and store whole records.  The padding rows of the
+ *   last record row are unspecified: they may be written as zeros or left
+ *   untouched.  Other rules as mxq_norm_rotate_quant. */
 mxq_status mxq_norm_rotate_quant_tiled(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
                                        int64_t x_row_stride, int32_t norm_kind, const float *gamma,
                                        const float *beta, float eps, const float *lambda, const uint16_t *r_hat,

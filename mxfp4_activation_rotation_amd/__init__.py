@@ -105,6 +105,13 @@ def _ptr(t):
     return t.data_ptr() if t is not None else None
 
 
+def _on(name: str, t: torch.Tensor, device: torch.device):
+    """Every tensor handed to the library must live on the GPU the call runs
+    on: a host pointer would reach a kernel, which the C layer cannot detect."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a tensor on {device}")
+
+
 def _check_x(x: torch.Tensor, allowed):
     if not isinstance(x, torch.Tensor) or not x.is_cuda:
         raise ValueError("x must be a device tensor")
@@ -150,6 +157,7 @@ def rotate_quant(x: torch.Tensor, r_hat: torch.Tensor, lam: torch.Tensor | None 
     if y_rot is not None:
         if y_rot.dtype != torch.float32 or y_rot.shape != (T, C) or not y_rot.is_contiguous():
             raise ValueError("y_rot must be a contiguous fp32 [tokens, channels] tensor")
+        _on("y_rot", y_rot, x.device)
         st = lib.mxq_rotate_quant_ex(_ptr(x), _DT[x.dtype], T, C, stride, _ptr(lam), _ptr(r_hat),
                                      _ptr(codes), _ptr(scales), _ptr(y_rot), _stream(x, stream))
         fn = "mxq_rotate_quant_ex"
@@ -178,6 +186,9 @@ def dequant(codes: torch.Tensor, scales: torch.Tensor, out_dtype=torch.float32, 
     lib = load()
     if codes.dtype != torch.uint8 or scales.dtype != torch.uint8 or codes.dim() != 2:
         raise ValueError("codes and scales must be uint8 2-D tensors")
+    if not codes.is_cuda:
+        raise ValueError("codes must be a device tensor")
+    _on("scales", scales, codes.device)
     T, C = codes.shape[0], codes.shape[1] * 2
     if tuple(scales.shape) != (T, C // 32) or not codes.is_contiguous() or not scales.is_contiguous():
         raise ValueError("scales must be contiguous [tokens, channels/32]; codes contiguous")
@@ -185,6 +196,7 @@ def dequant(codes: torch.Tensor, scales: torch.Tensor, out_dtype=torch.float32, 
         out = torch.empty((T, C), dtype=out_dtype, device=codes.device)
     if out.dtype not in (torch.bfloat16, torch.float32) or tuple(out.shape) != (T, C) or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16/fp32 [tokens, channels] tensor")
+    _on("out", out, codes.device)
     st = lib.mxq_dequant(_ptr(codes), _ptr(scales), T, C, _ptr(out), _DT[out.dtype], _stream(codes, stream))
     if st != 0:
         raise MXQError("mxq_dequant", st)
@@ -227,6 +239,7 @@ def gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Ten
     for t in (a_codes, a_scales, b_codes, b_scales):
         if t.dtype != torch.uint8 or t.dim() != 2 or not t.is_contiguous() or not t.is_cuda:
             raise ValueError("codes and scales must be contiguous uint8 2-D device tensors")
+        _on("operand", t, a_codes.device)
     M, K = a_codes.shape[0], a_codes.shape[1] * 2
     N = b_codes.shape[0]
     if b_codes.shape[1] * 2 != K or tuple(a_scales.shape) != (M, K // 32) or tuple(b_scales.shape) != (N, K // 32):
@@ -236,6 +249,7 @@ def gemm_mxfp4(a_codes: torch.Tensor, a_scales: torch.Tensor, b_codes: torch.Ten
     if out.dtype not in (torch.bfloat16, torch.float32) or tuple(out.shape) != (M, N) or \
             (M > 0 and N > 0 and out.stride(1) != 1):
         raise ValueError("out must be a bf16/fp32 [M, N] tensor with unit column stride")
+    _on("out", out, a_codes.device)
     ldy = out.stride(0) if M > 1 else N
     st = lib.mxq_gemm_mxfp4(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales), M, N, K,
                             _ptr(out), _DT[out.dtype], ldy, _stream(a_codes, stream))
@@ -260,6 +274,8 @@ def rotate_quant_block(x: torch.Tensor, r_block: torch.Tensor, lam: torch.Tensor
     codes, scales = _outputs(x, T, C, codes, scales)
     if y_rot is not None and (y_rot.dtype != torch.float32 or y_rot.shape != (T, C) or not y_rot.is_contiguous()):
         raise ValueError("y_rot must be a contiguous fp32 [tokens, channels] tensor")
+    if y_rot is not None:
+        _on("y_rot", y_rot, x.device)
     st = lib.mxq_rotate_quant_block(_ptr(x), _DT[x.dtype], T, C, stride, _ptr(lam), _ptr(r_block), B,
                                     _ptr(codes), _ptr(scales), _ptr(y_rot), _stream(x, stream))
     if st != 0:
@@ -299,6 +315,8 @@ def norm_rotate_quant(x: torch.Tensor, r_hat: torch.Tensor, gamma: torch.Tensor,
     codes, scales = _outputs(x, T, C, codes, scales)
     if y_rot is not None and (y_rot.dtype != torch.float32 or y_rot.shape != (T, C) or not y_rot.is_contiguous()):
         raise ValueError("y_rot must be a contiguous fp32 [tokens, channels] tensor")
+    if y_rot is not None:
+        _on("y_rot", y_rot, x.device)
     st = lib.mxq_norm_rotate_quant(_ptr(x), _DT[x.dtype], T, C, stride, NORM_KINDS[norm], _ptr(gamma), _ptr(beta),
                                    ctypes.c_float(eps), _ptr(lam), _ptr(r_hat), _ptr(codes), _ptr(scales),
                                    _ptr(y_rot), _stream(x, stream))
@@ -339,6 +357,8 @@ def calib_worst_group(x: torch.Tensor, lam: torch.Tensor | None = None, *, strea
     T, C, stride = _check_x(x, (torch.bfloat16, torch.float16, torch.float32))
     if lam is not None and (lam.dtype != torch.float32 or lam.shape != (C,) or not lam.is_contiguous()):
         raise ValueError("lam must be a contiguous fp32 [channels] tensor")
+    if lam is not None:
+        _on("lam", lam, x.device)
     xw = torch.empty((T, 32), dtype=torch.float64, device=x.device)
     group = torch.empty((), dtype=torch.int64, device=x.device)
     linf = torch.empty((), dtype=torch.float64, device=x.device)
@@ -404,6 +424,7 @@ def tile_mxfp4(codes: torch.Tensor, scales: torch.Tensor, *, tcodes=None, tscale
     R, K = codes.shape[0], codes.shape[1] * 2
     if scales.dtype != torch.uint8 or tuple(scales.shape) != (R, K // 32) or not scales.is_contiguous():
         raise ValueError("scales must be a contiguous uint8 [rows, K/32] tensor")
+    _on("scales", scales, codes.device)
     tcodes, tscales = _tiled_outputs(codes.device, R, K, tcodes, tscales)
     st = lib.mxq_tile_mxfp4(_ptr(codes), _ptr(scales), R, K, _ptr(tcodes), _ptr(tscales), _stream(codes, stream))
     if st != 0:
@@ -443,11 +464,13 @@ def gemm_mxfp4_tiled(a_tcodes: torch.Tensor, a_tscales: torch.Tensor, b_tcodes: 
             if t.dtype != torch.uint8 or t.numel() != n or not t.is_contiguous() or not t.is_cuda:
                 raise ValueError(f"{name} operand: tiled buffers must be contiguous uint8 device tensors "
                                  f"of {nc} and {ns} bytes")
+            _on(f"{name} operand", t, a_tcodes.device)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a_tcodes.device)
     if out.dtype not in (torch.bfloat16, torch.float32) or tuple(out.shape) != (M, N) or \
             (M > 0 and N > 0 and out.stride(1) != 1):
         raise ValueError("out must be a bf16/fp32 [M, N] tensor with unit column stride")
+    _on("out", out, a_tcodes.device)
     ldy = out.stride(0) if M > 1 else N
     st = lib.mxq_gemm_mxfp4_tiled(_ptr(a_tcodes), _ptr(a_tscales), _ptr(b_tcodes), _ptr(b_tscales), M, N, K,
                                   _ptr(out), _DT[out.dtype], ldy, _stream(a_tcodes, stream))

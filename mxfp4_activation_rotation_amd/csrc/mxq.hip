@@ -129,8 +129,84 @@ struct Args {
     int32_t unit;     // rows a wave takes back to back (1, or 16 for tiled output)
 };
 
+// Does a rotate instance need the tiny-group path?  fp16 activations without
+// smoothing never do: a nonzero fp16 value is at least 2^-24, and the group's
+// rotated maximum is then far above 2^-64.
+template <int XT, int LAM>
+constexpr bool kGuardTiny = !(XT == kFP16 && LAM == kLamNone);
+
+// x' of a lane's 8 channels in fp32: x * (1/lambda), x * lambda, or x.
+template <int XT, int LAM>
+__device__ __forceinline__ void smoothed8(u32x4_t xq, const float* il, float* f) {
+    widen8<XT == kFP16>(xq, f);
+    if constexpr (LAM != kLamNone) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) f[t] *= il[t];
+    }
+}
+
+// The rotated values y = x' R of a lane's 8 channels of one sub-tile: lane l
+// ends with y[8 q .. 8 q + 7] of group j (the layout described at the top).
+// xq holds the channels as loaded and il their smoothing factors.  The
+// activations enter the matrix cores as exact bf16 terms of the fp32 x': 1
+// for bf16 x, 2 for fp16 x, 3 for x * (1/lambda) or x * lambda.
+// SHIFT: x' is formed 2^k times larger (k in [0, 64], per lane), rounded to
+// fp32 once from the exact product x * factor * 2^k (exact in fp64), for the
+// tiny-group path.
+template <int XT, int LAM, bool SHIFT>
+__device__ __forceinline__ void rotate8(u32x4_t xq, const float* il, bf16x8_t A0, bf16x8_t A1, int k, float* v) {
+    f32x4_t d0 = {}, d1 = {};
+    if constexpr (XT == kBF16 && LAM == kLamNone && !SHIFT) {
+        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, xq);
+        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, b, d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b, d1, 0, 0, 0);
+    } else {
+        float f[8];
+        if constexpr (SHIFT && LAM != kLamNone) {
+            widen8<XT == kFP16>(xq, f);
+            const double p = __builtin_bit_cast(double, static_cast<uint64_t>(1023 + k) << 52);
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                f[t] = static_cast<float>(static_cast<double>(f[t]) * (static_cast<double>(il[t]) * p));
+        } else if constexpr (SHIFT) {
+            // bf16 x: x * 2^k is exact (the group's |x| * 2^k stays below 2^64)
+            widen8<XT == kFP16>(xq, f);
+            const float p = as_f32(static_cast<uint32_t>(127 + k) << 23);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) f[t] *= p;
+        } else {
+            smoothed8<XT, LAM>(xq, il, f);
+        }
+        constexpr int kTerms = LAM != kLamNone ? 3 : (XT == kFP16 ? 2 : 1);
+#pragma unroll
+        for (int term = 0; term < kTerms; ++term) {
+            u32x4_t bt;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bt[i] = bf16_pair_hi(f[2 * i], f[2 * i + 1]);
+            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bt);
+            d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, b, d0, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b, d1, 0, 0, 0);
+            if (term + 1 < kTerms) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) f[t] = bf16_residual(f[t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        v[t] = d0[t];
+        v[4 + t] = d1[t];
+    }
+}
+
+// The occupancy the plan aims at is stated to the compiler, so that the
+// rarely taken tiny-group pass after the main loop does not raise the
+// register count above it (that pass may spill instead; the main loop does
+// not).  The test-only y output instances, and the tiled ones (whose LDS
+// stage allows one 8-wave block per CU), aim at 2 waves per SIMD.
 template <int XT, int MODE, int LAM, bool YOUT, bool TILED = false>
-__global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
+__global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
+                          amdgpu_waves_per_eu((YOUT || TILED) ? 2 : kWavesPerCuOf<XT, MODE, LAM> / 4))) void quant_kernel(Args a) {
     constexpr int kN = (XT == kFP32) ? 2 : 1;  // 16-byte loads per lane per sub-tile
     constexpr uint32_t esz = (XT == kFP32) ? 4 : 2;
     constexpr int kBatch = kBatchOf<XT, MODE, LAM>;
@@ -213,72 +289,46 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
         }
     }
 
-    // Codes and scale of row rr (held in buf[u]): after the transpose lane l
+    // y output of a sub-tile (test use): v holds y * 2^ksh.
+    auto store_y = [&](int64_t rr, int s, const float (&v)[8], int ksh) {
+        const float down = pow2_neg(ksh);
+        const auto yrsrc = row_rsrc(a.y + rr * a.gpr * kGroup, gpr * kGroup * 4);
+        const uint32_t off = (static_cast<uint32_t>(p0 + 16 * s + j) * kGroup + 8 * q) * 4;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4_t{as_u32(v[0] * down), as_u32(v[1] * down), as_u32(v[2] * down), as_u32(v[3] * down)}, yrsrc, off,
+            0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4_t{as_u32(v[4] * down), as_u32(v[5] * down), as_u32(v[6] * down), as_u32(v[7] * down)}, yrsrc,
+            off + 16, 0, 0);
+    };
+    // Codes and scales of row rr (held in buf[u]): after the transpose lane l
     // holds the 16 code bytes of group p0 + l, and S is that group's scale.
+    // A group whose rotated maximum is below 2^-64 (S < 61) only sets
+    // tiny_seen here; such rows are redone after the main loop (below), so
+    // the common path carries one compare per row and no extra registers.
+    bool tiny_seen = false;
     auto encode_row = [&](const Rows& buf, int u, int64_t rr, uint32_t (&word)[kSub], uint32_t& S) {
             uint32_t sc[kSub];
 #pragma unroll
             for (int s = 0; s < kSub; ++s) {
                 float v[8];
                 if constexpr (MODE == kRotate) {
-                    f32x4_t d0 = {}, d1 = {};
-                    if constexpr (XT == kBF16 && LAM == kLamNone) {
-                        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, buf[u][s][0]);
-                        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, b, d0, 0, 0, 0);
-                        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b, d1, 0, 0, 0);
-                    } else {
-                        // x' in fp32, then exact bf16 terms: 2 for fp16 x
-                        // (11-bit significand), 3 for x * (1/lambda) or
-                        // x * lambda (24 bits).
-                        float f[8];
-                        widen8<XT == kFP16>(buf[u][s][0], f);
-                        if constexpr (LAM != kLamNone) {
-#pragma unroll
-                            for (int t = 0; t < 8; ++t) f[t] *= il[s][t];
-                        }
-                        constexpr int kTerms = LAM != kLamNone ? 3 : 2;
-#pragma unroll
-                        for (int term = 0; term < kTerms; ++term) {
-                            u32x4_t bt;
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) bt[i] = bf16_pair_hi(f[2 * i], f[2 * i + 1]);
-                            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bt);
-                            d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, b, d0, 0, 0, 0);
-                            d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b, d1, 0, 0, 0);
-                            if (term + 1 < kTerms) {
-#pragma unroll
-                                for (int t = 0; t < 8; ++t) f[t] = bf16_residual(f[t]);
-                            }
-                        }
-                    }
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        v[t] = d0[t];
-                        v[4 + t] = d1[t];
-                    }
+                    rotate8<XT, LAM, false>(buf[u][s][0], il[s], A0, A1, 0, v);
+                } else if constexpr (XT == kFP32) {
+                    widen4_f32(buf[u][s][0], v);
+                    widen4_f32(buf[u][s][1], v + 4);
                 } else {
-                    if constexpr (XT == kFP32) {
-                        widen4_f32(buf[u][s][0], v);
-                        widen4_f32(buf[u][s][1], v + 4);
-                    } else {
-                        widen8<XT == kFP16>(buf[u][s][0], v);
-                    }
+                    widen8<XT == kFP16>(buf[u][s][0], v);
                 }
                 const uint32_t scale_bits = e8m0_scale_bits(group_amax8(v));
                 sc[s] = scale_bits >> 23;
                 word[s] = encode8(v, as_f32(scale_bits));
-                if constexpr (YOUT) {
-                    const auto yrsrc = row_rsrc(a.y + rr * a.gpr * kGroup, gpr * kGroup * 4);
-                    const uint32_t off = (static_cast<uint32_t>(p0 + 16 * s + j) * kGroup + 8 * q) * 4;
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        u32x4_t{as_u32(v[0]), as_u32(v[1]), as_u32(v[2]), as_u32(v[3])}, yrsrc, off, 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        u32x4_t{as_u32(v[4]), as_u32(v[5]), as_u32(v[6]), as_u32(v[7])}, yrsrc, off + 16, 0, 0);
-                }
+                if constexpr (YOUT) store_y(rr, s, v, 0);
             }
             transpose_words(word);
             // the scale of group 16 q + j is the one computed in sub-tile q
             S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
+            if constexpr (MODE == kRotate && kGuardTiny<XT, LAM>) tiny_seen |= S < (kTinyScaleBits >> 23);
     };
     auto store_row = [&](int64_t rr, const uint32_t (&word)[kSub], uint32_t S) {
             if constexpr (TILED) {
@@ -391,6 +441,71 @@ __global__ __launch_bounds__(kBlockThreads) void quant_kernel(Args a) {
             if (r + step >= T) break;
             if (r + 2 * step < T) load_rows(bufA, r + 2 * step);
             process_rows(bufB, r + step);
+        }
+    }
+
+    // ---- rows holding a tiny group (rare): redone from x' * 2^k ----------
+    // Every row of this wave is reloaded and re-encoded; in a row with a
+    // group whose rotated maximum is below 2^-64, the sub-tiles holding such
+    // groups are recomputed with x' shifted by 2^k (k per group, from its
+    // largest |x'|), and the row's codes and scales are written again (the
+    // other groups' bytes are rewritten unchanged).  The release fence makes
+    // the first stores of these rows complete before the second ones.
+    if constexpr (MODE == kRotate && kGuardTiny<XT, LAM>) {
+        if (any_lane(tiny_seen)) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            auto fix_row = [&](int64_t rr) {
+                const auto rsrc = row_rsrc(xb + rr * a.stride * esz, row_bytes);
+                uint32_t word[kSub], sc[kSub];
+                bool redo = false;
+                // one sub-tile at a time (scheduling barriers between them):
+                // this path must not need more registers than the main loop
+#pragma unroll
+                for (int s = 0; s < kSub; ++s) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    u32x4_t xr_s = __builtin_amdgcn_raw_buffer_load_b128(rsrc, xoff[s], 0, 0);
+                    // an opaque copy of the factors: their fp64 forms are not
+                    // hoisted out of this loop into registers of the main one
+                    float ilc[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        ilc[t] = il[s][t];
+                        if constexpr (LAM != kLamNone) asm volatile("" : "+v"(ilc[t]));
+                    }
+                    float v[8];
+                    rotate8<XT, LAM, false>(xr_s, ilc, A0, A1, 0, v);
+                    uint32_t sb = e8m0_scale_bits(group_amax8(v)), cb = sb;
+                    const bool tiny = sb < kTinyScaleBits;
+                    if (any_lane(tiny)) {
+                        redo = true;
+                        float xp[8];
+                        smoothed8<XT, LAM>(xr_s, ilc, xp);
+                        const int k = tiny ? tiny_shift(group_amax8(xp)) : 0;
+                        float w[8];
+                        rotate8<XT, LAM, true>(xr_s, ilc, A0, A1, k, w);
+                        uint32_t sb2, cb2;
+                        shifted_scale_bits(group_amax8(w), k, sb2, cb2);
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) v[t] = tiny ? w[t] : v[t];
+                        sb = tiny ? sb2 : sb;
+                        cb = tiny ? cb2 : cb;
+                        if constexpr (YOUT) store_y(rr, s, v, tiny ? k : 0);
+                    }
+                    sc[s] = sb >> 23;
+                    word[s] = encode8(v, as_f32(cb));
+                }
+                if (redo) {
+                    transpose_words(word);
+                    const uint32_t S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
+                    store_row(rr, word, S);
+                }
+            };
+            if (TILED && a.unit == 16) {
+                for (int64_t unit = r0; unit < T; unit += 16 * rs)
+                    for (int64_t rr = unit; rr < unit + 16 && rr < T; ++rr) fix_row(rr);
+            } else {
+                for (int64_t rr = r0; rr < T; rr += rs) fix_row(rr);
+            }
         }
     }
 }

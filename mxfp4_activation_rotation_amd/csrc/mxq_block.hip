@@ -21,6 +21,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "mxq.h"
 #include "mxq_device.h"
@@ -49,8 +50,20 @@ struct BlockArgs {
     int32_t row_step;  // waves per super-tile column
 };
 
+// Waves per SIMD each instance reaches without the tiny-block pass; stated
+// to the compiler so that the pass (rare) spills rather than lowering the
+// occupancy of the main loop.
+template <bool LAM, int KB>
+constexpr int kWavesPerSimd = LAM ? (KB == 1 ? 4 : KB == 2 ? 3 : 1) : (KB == 1 ? 7 : KB == 2 ? 4 : 2);
+
+// fp16 activations without smoothing never need the tiny-block pass (a
+// nonzero fp16 value is at least 2^-24).
+template <int XT, bool LAM>
+constexpr bool kGuardTiny = !(XT == MXQ_FP16 && !LAM);
+
 template <int XT, bool LAM, int KB, bool HALF>
-__global__ __launch_bounds__(kBlockThreads) void block_quant_kernel(BlockArgs a) {
+__global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
+                          amdgpu_waves_per_eu(kWavesPerSimd<LAM, KB>))) void block_quant_kernel(BlockArgs a) {
     constexpr bool kFp16 = XT == MXQ_FP16;
     constexpr int kSubs = 4 / KB;  // sub-tiles per super-tile
     constexpr int kB = HALF ? 16 : 32 * KB;
@@ -109,8 +122,97 @@ __global__ __launch_bounds__(kBlockThreads) void block_quant_kernel(BlockArgs a)
 
     const uint32_t row_bytes = gpr * kGroup * 2;
     const char* xb = static_cast<const char*>(a.x);
-    for (int r_loop = r0; r_loop < a.tokens; r_loop += a.row_step) {
-        const int64_t r = __builtin_amdgcn_readfirstlane(r_loop);
+
+    // x' of the lane's 8 channels of k-step k of sub-tile s, in fp32.
+    auto smoothed = [&](const u32x4_t& xq, int s, int k, float* f) {
+        widen8<kFp16>(xq, f);
+        if constexpr (LAM) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) f[t] *= il[s][k][t];
+        }
+    };
+    // The rotated values of sub-tile s: d0[g], d1[g] hold output group g's
+    // two halves.  SHIFT: x' is formed 2^ksh times larger (rounded to fp32
+    // once from the exact product in fp64), for the tiny-block pass.
+    auto product = [&](const u32x4_t (&xin)[kSubs][KB], int s, int ksh, f32x4_t (&d0)[KB], f32x4_t (&d1)[KB],
+                       auto shift_tag) {
+        constexpr bool SHIFT = decltype(shift_tag)::value;
+#pragma unroll
+        for (int g = 0; g < KB; ++g) d0[g] = d1[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (kTerms == 1 && !SHIFT) {
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+                const bf16x8_t b = __builtin_bit_cast(bf16x8_t, xin[s][k]);
+#pragma unroll
+                for (int g = 0; g < KB; ++g) {
+                    d0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0][k], b, d0[g], 0, 0, 0);
+                    d1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1][k], b, d1[g], 0, 0, 0);
+                }
+            }
+        } else {
+            float f[KB][8];
+#pragma unroll
+            for (int k = 0; k < KB; ++k) {
+                if constexpr (SHIFT) {
+                    widen8<kFp16>(xin[s][k], f[k]);
+                    if constexpr (LAM) {
+                        const double p = __builtin_bit_cast(double, static_cast<uint64_t>(1023 + ksh) << 52);
+#pragma unroll
+                        for (int t = 0; t < 8; ++t)
+                            f[k][t] = static_cast<float>(static_cast<double>(f[k][t]) *
+                                                         (static_cast<double>(il[s][k][t]) * p));
+                    } else {
+                        // 16-bit x times 2^ksh is exact (the block's |x| 2^ksh < 2^64)
+                        const float p = as_f32(static_cast<uint32_t>(127 + ksh) << 23);
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) f[k][t] *= p;
+                    }
+                } else {
+                    smoothed(xin[s][k], s, k, f[k]);
+                }
+            }
+            constexpr int kT = SHIFT && kTerms == 1 ? 1 : kTerms;
+#pragma unroll
+            for (int term = 0; term < kT; ++term) {
+#pragma unroll
+                for (int k = 0; k < KB; ++k) {
+                    u32x4_t bt;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) bt[i] = bf16_pair_hi(f[k][2 * i], f[k][2 * i + 1]);
+                    const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bt);
+#pragma unroll
+                    for (int g = 0; g < KB; ++g) {
+                        d0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0][k], b, d0[g], 0, 0, 0);
+                        d1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1][k], b, d1[g], 0, 0, 0);
+                    }
+                    if (term + 1 < kT) {
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) f[k][t] = bf16_residual(f[k][t]);
+                    }
+                }
+            }
+        }
+    };
+    auto store_y = [&](int64_t r, int s, int g, const float (&v)[8], int ksh) {
+        const float down = pow2_neg(ksh);
+        const auto yrsrc = row_rsrc(a.y + r * a.gpr * kGroup, gpr * kGroup * 4);
+        const uint32_t grp = static_cast<uint32_t>(p0 + KB * (16 * s + j) + g);
+        const uint32_t off = (grp * kGroup + 8 * q) * 4;
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4_t{as_u32(v[0] * down), as_u32(v[1] * down), as_u32(v[2] * down), as_u32(v[3] * down)}, yrsrc, off,
+            0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4_t{as_u32(v[4] * down), as_u32(v[5] * down), as_u32(v[6] * down), as_u32(v[7] * down)}, yrsrc,
+            off + 16, 0, 0);
+    };
+
+    // One row.  FIX (the pass for rows with tiny groups, below): a block
+    // column whose output groups all have a rotated maximum below 2^-64 is
+    // recomputed from x' * 2^k, k from the block's largest |x'|; a block with
+    // a larger output group keeps its values, whose errors scale with the
+    // block's norm.  Returns whether some group of the row had S < 61.
+    auto row_body = [&](int64_t r, auto fix_tag) -> bool {
+        constexpr bool FIX = decltype(fix_tag)::value;
         const auto rsrc = row_rsrc(xb + r * a.stride * 2, row_bytes);
         u32x4_t xin[kSubs][KB];
 #pragma unroll
@@ -118,51 +220,60 @@ __global__ __launch_bounds__(kBlockThreads) void block_quant_kernel(BlockArgs a)
 #pragma unroll
             for (int k = 0; k < KB; ++k) {
                 const uint32_t grp = static_cast<uint32_t>(p0 + KB * (16 * s + j) + k);
-                xin[s][k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (grp * kGroup + 8 * q) * 2, 0, kAuxNT);
+                xin[s][k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (grp * kGroup + 8 * q) * 2, 0,
+                                                                  FIX ? 0 : kAuxNT);
             }
         uint32_t word[4], sc[4];
+        bool redo = false;
 #pragma unroll
         for (int s = 0; s < kSubs; ++s) {
             f32x4_t d0[KB], d1[KB];
+            product(xin, s, 0, d0, d1, std::false_type{});
+            uint32_t sb[KB], cb[KB];
+            int ksh = 0;
+            uint32_t colmax = 0;
 #pragma unroll
-            for (int g = 0; g < KB; ++g) d0[g] = d1[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if constexpr (kTerms == 1) {
+            for (int g = 0; g < KB; ++g) {
+                float v[8];
 #pragma unroll
-                for (int k = 0; k < KB; ++k) {
-                    const bf16x8_t b = __builtin_bit_cast(bf16x8_t, xin[s][k]);
-#pragma unroll
-                    for (int g = 0; g < KB; ++g) {
-                        d0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0][k], b, d0[g], 0, 0, 0);
-                        d1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1][k], b, d1[g], 0, 0, 0);
-                    }
+                for (int t = 0; t < 4; ++t) {
+                    v[t] = d0[g][t];
+                    v[4 + t] = d1[g][t];
                 }
-            } else {
-                float f[KB][8];
-#pragma unroll
-                for (int k = 0; k < KB; ++k) {
-                    widen8<kFp16>(xin[s][k], f[k]);
-                    if constexpr (LAM) {
-#pragma unroll
-                        for (int t = 0; t < 8; ++t) f[k][t] *= il[s][k][t];
-                    }
-                }
-#pragma unroll
-                for (int term = 0; term < kTerms; ++term) {
+                sb[g] = cb[g] = e8m0_scale_bits(group_amax8(v));
+                colmax = sb[g] > colmax ? sb[g] : colmax;
+            }
+            if constexpr (FIX) {
+                const bool tiny = colmax < kTinyScaleBits;
+                if (any_lane(tiny)) {
+                    redo = true;
+                    float ax = 0.0f;
 #pragma unroll
                     for (int k = 0; k < KB; ++k) {
-                        u32x4_t bt;
+                        float f[8];
+                        smoothed(xin[s][k], s, k, f);
+                        ax = fmaxf(ax, group_amax8(f));
+                    }
+                    ksh = tiny ? tiny_shift(ax) : 0;
+                    f32x4_t e0[KB], e1[KB];
+                    product(xin, s, ksh, e0, e1, std::true_type{});
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) bt[i] = bf16_pair_hi(f[k][2 * i], f[k][2 * i + 1]);
-                        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bt);
+                    for (int g = 0; g < KB; ++g) {
+                        float w[8];
 #pragma unroll
-                        for (int g = 0; g < KB; ++g) {
-                            d0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0][k], b, d0[g], 0, 0, 0);
-                            d1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1][k], b, d1[g], 0, 0, 0);
+                        for (int t = 0; t < 4; ++t) {
+                            w[t] = e0[g][t];
+                            w[4 + t] = e1[g][t];
                         }
-                        if (term + 1 < kTerms) {
+                        uint32_t s2, c2;
+                        shifted_scale_bits(group_amax8(w), ksh, s2, c2);
 #pragma unroll
-                            for (int t = 0; t < 8; ++t) f[k][t] = bf16_residual(f[k][t]);
+                        for (int t = 0; t < 4; ++t) {
+                            d0[g][t] = tiny ? e0[g][t] : d0[g][t];
+                            d1[g][t] = tiny ? e1[g][t] : d1[g][t];
                         }
+                        sb[g] = tiny ? s2 : sb[g];
+                        cb[g] = tiny ? c2 : cb[g];
                     }
                 }
             }
@@ -174,28 +285,37 @@ __global__ __launch_bounds__(kBlockThreads) void block_quant_kernel(BlockArgs a)
                     v[t] = d0[g][t];
                     v[4 + t] = d1[g][t];
                 }
-                const uint32_t scale_bits = e8m0_scale_bits(group_amax8(v));
-                sc[s * KB + g] = scale_bits >> 23;
-                word[s * KB + g] = encode8(v, as_f32(scale_bits));
-                if (a.y) {
-                    const auto yrsrc = row_rsrc(a.y + r * a.gpr * kGroup, gpr * kGroup * 4);
-                    const uint32_t grp = static_cast<uint32_t>(p0 + KB * (16 * s + j) + g);
-                    const uint32_t off = (grp * kGroup + 8 * q) * 4;
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        u32x4_t{as_u32(v[0]), as_u32(v[1]), as_u32(v[2]), as_u32(v[3])}, yrsrc, off, 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        u32x4_t{as_u32(v[4]), as_u32(v[5]), as_u32(v[6]), as_u32(v[7])}, yrsrc, off + 16, 0, 0);
-                }
+                sc[s * KB + g] = sb[g] >> 23;
+                word[s * KB + g] = encode8(v, as_f32(cb[g]));
+                if (a.y) store_y(r, s, g, v, ksh);
             }
         }
         transpose_words(word);
         const uint32_t S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
-        const uint32_t grp = static_cast<uint32_t>(p0 + KB * (16 * (q / KB) + j) + q % KB);
-        const auto crsrc = row_rsrc(a.codes + r * a.gpr * 16, gpr * 16);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{word[0], word[1], word[2], word[3]}, crsrc, grp * 16, 0,
-                                               kAuxNT);
-        const auto srsrc = row_rsrc(a.scales + r * a.gpr, gpr);
-        __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, grp, 0, 0);
+        if (!FIX || redo) {
+            const uint32_t grp = static_cast<uint32_t>(p0 + KB * (16 * (q / KB) + j) + q % KB);
+            const auto crsrc = row_rsrc(a.codes + r * a.gpr * 16, gpr * 16);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{word[0], word[1], word[2], word[3]}, crsrc, grp * 16, 0,
+                                                   kAuxNT);
+            const auto srsrc = row_rsrc(a.scales + r * a.gpr, gpr);
+            __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, grp, 0, 0);
+        }
+        return S < (kTinyScaleBits >> 23);
+    };
+
+    bool tiny_seen = false;
+    for (int r_loop = r0; r_loop < a.tokens; r_loop += a.row_step) {
+        const int64_t r = __builtin_amdgcn_readfirstlane(r_loop);
+        tiny_seen |= row_body(r, std::false_type{});
+    }
+    // Rows holding a group with S < 61 (rare) are redone; the release fence
+    // makes their first stores complete before the second ones.
+    if (kGuardTiny<XT, LAM> && any_lane(tiny_seen)) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        for (int r_loop = r0; r_loop < a.tokens; r_loop += a.row_step) {
+            const int64_t r = __builtin_amdgcn_readfirstlane(r_loop);
+            row_body(r, std::true_type{});
+        }
     }
 }
 

@@ -84,6 +84,41 @@ __device__ __forceinline__ float bf16_residual(float a) {
     return a - as_f32(as_u32(a) & 0xffff0000u);
 }
 
+// ---- groups of tiny magnitude ----------------------------------------------
+// The exact bf16 terms of x' stop being exact below bf16's smallest subnormal
+// (2^-133), and products on the matrix cores below fp32's normal range lose
+// bits, so a group whose rotated values are all tiny would carry errors that
+// are large against its own norm.  A group whose rotated maximum is below
+// 2^-64 (scale byte below 61) is therefore recomputed from x' * 2^k: the
+// scale follows from the shifted maximum minus k (clamped at -127 like any
+// other), and the converter divides the shifted values by 2^(e + k), which
+// gives the codes of the unshifted group.  Above 2^-64 every lost bit is
+// below 2^-57 of the group's norm.
+constexpr uint32_t kTinyScaleBits = 61u << 23;  // S << 23 of a group maximum 2^-64
+
+// Shift k in [0, 64] for a group whose largest |x'| is ax: x' * 2^k stays
+// below 2^64, so the shifted products cannot overflow whatever the block is
+// (for an orthogonal block a tiny group has ax < 2^-60, so k = 64).
+__device__ __forceinline__ int tiny_shift(float ax) {
+    const int k = 64 - __builtin_amdgcn_frexp_expf(ax);  // ax < 2^frexp_exp; 0 for ax = 0
+    return k < 0 ? 0 : (k > 64 ? 64 : k);
+}
+
+// Scale bits (S << 23) and converter scale bits of a group computed 2^k
+// times its size, from the shifted group maximum.
+__device__ __forceinline__ void shifted_scale_bits(float amax_shifted, int k, uint32_t& s_bits,
+                                                   uint32_t& conv_bits) {
+    s_bits = __builtin_elementwise_sub_sat(as_u32(amax_shifted) & 0x7f800000u, static_cast<uint32_t>(2 + k) << 23);
+    conv_bits = s_bits + (static_cast<uint32_t>(k) << 23);
+}
+
+// 2^-k as fp32, k in [0, 64].
+__device__ __forceinline__ float pow2_neg(int k) { return as_f32(static_cast<uint32_t>(127 - k) << 23); }
+
+// Does the condition hold in any lane of the wave?  (A scalar branch on the
+// result keeps the rare path out of the common one.)
+__device__ __forceinline__ bool any_lane(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
+
 // Widen 8 packed 16-bit elements (one 16-byte load) to fp32, element order kept.
 template <bool IS_FP16>
 __device__ __forceinline__ void widen8(u32x4_t q, float* f) {

@@ -99,8 +99,19 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
+// Waves per SIMD each instance reaches without the pass that redoes rare
+// rows (after the main loop); stated to the compiler so that the pass spills
+// rather than lowering the main loop's occupancy (16-wave blocks need 4).
+template <int NORM, int NT, bool YOUT, int BW>
+constexpr int kWavesPerSimd = BW == 16 ? 4
+                              : NT == 1  ? (YOUT ? 4 : 5)
+                              : NT == 2  ? ((YOUT || NORM == kLayer) ? 3 : 4)
+                              : NT == 4  ? 2
+                                         : 1;
+
 template <int XT, int NORM, int NT, bool YOUT, bool TILED, int BW>
-__global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
+__global__ __attribute__((amdgpu_flat_work_group_size(1, kWave * BW),
+                          amdgpu_waves_per_eu(kWavesPerSimd<NORM, NT, YOUT, BW>))) void norm_quant_kernel(NormArgs a) {
     constexpr int kBlockWaves = BW;
     constexpr int kBlockThreads = kWave * BW;
     constexpr bool kFp16 = XT == MXQ_FP16;
@@ -187,6 +198,87 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
 #pragma unroll
         for (int st = 0; st < NT; ++st) load_tile(buf[st], r_any, st);
     };
+    // Row statistics of a row held in registers (groups past the row end
+    // loaded zeros).  LayerNorm: the first sweep gives a shift mu0 (an fp32
+    // value near the mean); the second accumulates x - mu0 and its square, so
+    // that mean = mu0 + E[x - mu0] and var = E[(x - mu0)^2] - E[x - mu0]^2
+    // carry errors relative to the spread of the row, not to its mean.  The
+    // mean is then applied as an fp32 pair mu + mu_lo.  s2 is the row's sum
+    // of squares (of x - mu0 for LayerNorm).
+    auto row_stats = [&](u32x4_t (&buf)[NT][kSub], double& s2, double& var, double& mean, float& mu,
+                         float& mu_lo) {
+        mu = 0.0f;
+        mu_lo = 0.0f;
+        mean = 0.0;
+        if constexpr (NORM == kLayer) {
+            // all-ones A operand (packed 1.0 pairs): row 0 of the product
+            // (register 0 of lanes 0..15) holds the sums of groups j = lane
+            constexpr uint32_t kOne2 = kFp16 ? 0x3c003c00u : 0x3f803f80u;
+            const u32x4_t ones = {kOne2, kOne2, kOne2, kOne2};
+            double part = 0.0;
+#pragma unroll
+            for (int st = 0; st < NT; ++st) {
+                f32x4_t sums = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int s = 0; s < kSub; ++s) sums = mfma16<kFp16>(ones, buf[st][s], sums);
+                part += q == 0 ? static_cast<double>(sums[0]) : 0.0;
+            }
+            mu = static_cast<float>(wave_sum(part) / C);
+#pragma unroll
+            for (int st = 0; st < NT; ++st)
+#pragma unroll
+                for (int s = 0; s < kSub; ++s) asm volatile("" : "+v"(buf[st][s]));
+        }
+        double part = 0.0, part1 = 0.0;
+#pragma unroll
+        for (int st = 0; st < NT; ++st) {
+            if constexpr (NORM == kLayer) {
+#pragma unroll
+                for (int s = 0; s < kSub; ++s) {
+                    // lanes of groups past the row end loaded zeros, which
+                    // are not zero once centred
+                    const bool valid = kTileGroups * st + 16 * s + j < a.gpr;
+                    float f[8];
+                    widen8<kFp16>(buf[st][s], f);
+                    float c8 = 0.0f, s8 = 0.0f;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const float d = f[t] - mu;
+                        s8 += d;
+                        c8 += d * d;
+                    }
+                    part += valid ? static_cast<double>(c8) : 0.0;
+                    part1 += valid ? static_cast<double>(s8) : 0.0;
+                }
+            } else {
+                // diagonal entry (j, j) of the super-tile's Gram matrices:
+                // lane 16 (j / 4) + j, register j % 4
+                f32x4_t gram = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int s = 0; s < kSub; ++s) gram = mfma16<kFp16>(buf[st][s], buf[st][s], gram);
+                const int r = j & 3;
+                const float dj = r == 0 ? gram[0] : r == 1 ? gram[1] : r == 2 ? gram[2] : gram[3];
+                part += q == (j >> 2) ? static_cast<double>(dj) : 0.0;
+            }
+        }
+        s2 = wave_sum(part);
+        var = s2 / C;
+        if constexpr (NORM == kLayer) {
+            const double d1 = wave_sum(part1) / C;  // E[x - mu0]
+            var -= d1 * d1;
+            mean = static_cast<double>(mu) + d1;
+            mu = static_cast<float>(mean);
+            mu_lo = static_cast<float>(mean - static_cast<double>(mu));
+        }
+        // Keep only the packed row live across the statistics: an empty asm
+        // that claims to change the registers stops the compiler from holding
+        // the widened fp32 copies (twice the registers) until the second use.
+#pragma unroll
+        for (int st = 0; st < NT; ++st)
+#pragma unroll
+            for (int s = 0; s < kSub; ++s) asm volatile("" : "+v"(buf[st][s]));
+    };
+
     // Two row buffers alternate when they fit in registers (up to 4096
     // channels): the next row is in flight while the current one computes.
     // Longer rows keep one buffer, and each super-tile of the next row loads
@@ -194,6 +286,10 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
     constexpr bool kDouble = NT <= 2;
     u32x4_t bufA[NT][kSub], bufB[NT][kSub];
     if (w < a.tokens) load_row(bufA, w);
+    // Rows the main loop cannot do exactly enough (rare) only set fix_seen
+    // there and are redone after it: bf16 rows whose squares leave fp32's
+    // range, and rows holding a group whose rotated maximum is below 2^-64.
+    bool fix_seen = false;
     // Staged: the loop runs over the block's row groups, the same for every
     // wave of the block (it meets a barrier each time); a wave whose row is
     // past the end stages zeros, which become the padding rows.
@@ -212,79 +308,13 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
                 if (r + a.waves < a.tokens) load_row(bufB, r + a.waves);
             }
             // ---- row statistics (groups past the row end loaded zeros)
-            // LayerNorm: the first sweep gives a shift mu0 (an fp32 value near
-            // the mean); the second accumulates x - mu0 and its square, so that
-            // mean = mu0 + E[x - mu0] and var = E[(x - mu0)^2] - E[x - mu0]^2
-            // carry errors relative to the spread of the row, not to its mean.
-            // The mean is then applied as an fp32 pair mu + mu_lo.
-            float mu = 0.0f, mu_lo = 0.0f;
-            if constexpr (NORM == kLayer) {
-                // all-ones A operand (packed 1.0 pairs): row 0 of the product
-                // (register 0 of lanes 0..15) holds the sums of groups j = lane
-                constexpr uint32_t kOne2 = kFp16 ? 0x3c003c00u : 0x3f803f80u;
-                const u32x4_t ones = {kOne2, kOne2, kOne2, kOne2};
-                double part = 0.0;
-#pragma unroll
-                for (int st = 0; st < NT; ++st) {
-                    f32x4_t sums = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int s = 0; s < kSub; ++s) sums = mfma16<kFp16>(ones, buf[st][s], sums);
-                    part += q == 0 ? static_cast<double>(sums[0]) : 0.0;
-                }
-                mu = static_cast<float>(wave_sum(part) / C);
-#pragma unroll
-                for (int st = 0; st < NT; ++st)
-#pragma unroll
-                    for (int s = 0; s < kSub; ++s) asm volatile("" : "+v"(buf[st][s]));
-            }
-            double part = 0.0, part1 = 0.0;
-#pragma unroll
-            for (int st = 0; st < NT; ++st) {
-                if constexpr (NORM == kLayer) {
-#pragma unroll
-                    for (int s = 0; s < kSub; ++s) {
-                        // lanes of groups past the row end loaded zeros, which
-                        // are not zero once centred
-                        const bool valid = kTileGroups * st + 16 * s + j < a.gpr;
-                        float f[8];
-                        widen8<kFp16>(buf[st][s], f);
-                        float c8 = 0.0f, s8 = 0.0f;
-#pragma unroll
-                        for (int t = 0; t < 8; ++t) {
-                            const float d = f[t] - mu;
-                            s8 += d;
-                            c8 += d * d;
-                        }
-                        part += valid ? static_cast<double>(c8) : 0.0;
-                        part1 += valid ? static_cast<double>(s8) : 0.0;
-                    }
-                } else {
-                    // diagonal entry (j, j) of the super-tile's Gram matrices:
-                    // lane 16 (j / 4) + j, register j % 4
-                    f32x4_t gram = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int s = 0; s < kSub; ++s) gram = mfma16<kFp16>(buf[st][s], buf[st][s], gram);
-                    const int r = j & 3;
-                    const float dj = r == 0 ? gram[0] : r == 1 ? gram[1] : r == 2 ? gram[2] : gram[3];
-                    part += q == (j >> 2) ? static_cast<double>(dj) : 0.0;
-                }
-            }
-            double var = wave_sum(part) / C;
-            if constexpr (NORM == kLayer) {
-                const double d1 = wave_sum(part1) / C;  // E[x - mu0]
-                var -= d1 * d1;
-                const double mean = static_cast<double>(mu) + d1;
-                mu = static_cast<float>(mean);
-                mu_lo = static_cast<float>(mean - static_cast<double>(mu));
-            }
+            double s2, var, mean;
+            float mu, mu_lo;
+            row_stats(buf, s2, var, mean, mu, mu_lo);
+            // bf16 rows whose sum of squares left fp32's safe range (squares
+            // over 2^128 or below 2^-149) are redone after the main loop
+            if constexpr (!kFp16) fix_seen |= !(s2 >= 0x1p-80 && s2 <= 0x1p+1000);
             const float inv = static_cast<float>(1.0 / sqrt(var + static_cast<double>(a.eps)));
-            // Keep only the packed row live across the statistics: an empty asm
-            // that claims to change the registers stops the compiler from holding
-            // the widened fp32 copies (twice the registers) until the second use.
-#pragma unroll
-            for (int st = 0; st < NT; ++st)
-#pragma unroll
-                for (int s = 0; s < kSub; ++s) asm volatile("" : "+v"(buf[st][s]));
 
             // ---- normalize, smooth, rotate, encode
             // Row layout: the row's codes and scales.  Fragment-tiled layout
@@ -351,6 +381,7 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
                 }
                 transpose_words(word);
                 const uint32_t S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
+                fix_seen |= S < (kTinyScaleBits >> 23);
                 const uint32_t g = static_cast<uint32_t>(kTileGroups * st + lane);
                 if constexpr (kStaged) {
                     stg[sb][wave][g] = u32x4_t{word[0], word[1], word[2], word[3]};
@@ -407,6 +438,173 @@ __global__ __launch_bounds__(kWave * BW) void norm_quant_kernel(NormArgs a) {
                                                           (g >> 2) * 64 + (g & 3) * 16 + 8 * hb, 0, kAuxNT);
             }
             sb ^= 1;
+        }
+    }
+
+    // ---- rows redone (rare) -------------------------------------------------
+    // When any of this wave's rows set fix_seen, the wave recomputes all of
+    // its rows and stores them again, row by row (the bytes of rows that
+    // needed nothing come out the same).  Per row:
+    //  - bf16 rows whose sum of squares left [2^-80, 2^1000] are scaled by
+    //    2^kr (kr from the row's largest |h|, exact for the 16-bit values
+    //    that matter) and the statistics retaken, with eps scaled by 2^(2 kr):
+    //    the normalized row is unchanged;
+    //  - a group whose rotated maximum is below 2^-64 is recomputed from
+    //    x' * 2^k (k from its largest |x'|, at most 64), formed as
+    //    fma(d 2^k, gamma / lambda, (beta / lambda) 2^k), with d 2^k taken
+    //    from 1/sqrt in fp64 times 2^k, so no fp32 subnormal enters.
+    // Staged blocks first let every wave's record stores complete (fence,
+    // barrier); the fence before the pass does the same for the wave's own.
+    if constexpr (kStaged) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __builtin_amdgcn_s_barrier();
+    }
+    if (any_lane(fix_seen)) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        // x' of a sub-tile's 8 values -> the rotated values (3 exact bf16 terms)
+        auto rotate3 = [&](const float (&xp)[8], float (&v)[8]) {
+            float f[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) f[t] = xp[t];
+            f32x4_t d0 = {}, d1 = {};
+#pragma unroll
+            for (int term = 0; term < 3; ++term) {
+                u32x4_t bt;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) bt[i] = bf16_pair_hi(f[2 * i], f[2 * i + 1]);
+                const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bt);
+                d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, b, d0, 0, 0, 0);
+                d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, b, d1, 0, 0, 0);
+                if (term < 2) {
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) f[t] = bf16_residual(f[t]);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                v[t] = d0[t];
+                v[4 + t] = d1[t];
+            }
+        };
+        for (int64_t r_any = w; r_any < a.tokens; r_any += a.waves) {
+            const int64_t r = __builtin_amdgcn_readfirstlane(static_cast<int>(r_any));
+            u32x4_t rb[NT][kSub];
+            load_row(rb, r);
+            double s2, var, mean;
+            float mu, mu_lo;
+            row_stats(rb, s2, var, mean, mu, mu_lo);
+            double eps_d = static_cast<double>(a.eps);
+            if constexpr (!kFp16) {
+                if (!(s2 >= 0x1p-80 && s2 <= 0x1p+1000)) {
+                    uint32_t m = 0;  // largest |h| of the row, as bf16 bits
+#pragma unroll
+                    for (int st = 0; st < NT; ++st)
+#pragma unroll
+                        for (int s = 0; s < kSub; ++s)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const uint32_t d = rb[st][s][i];
+                                const uint32_t lo = d & 0x7fffu, hi = (d >> 16) & 0x7fffu;
+                                m = m > lo ? m : lo;
+                                m = m > hi ? m : hi;
+                            }
+#pragma unroll
+                    for (int o = 32; o >= 1; o >>= 1) {
+                        const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), o, kWave));
+                        m = m > other ? m : other;
+                    }
+                    if (m != 0) {
+                        // |h| 2^kr < 1 at the row's maximum
+                        const int kr = -__builtin_amdgcn_frexp_expf(as_f32(m << 16));
+#pragma unroll
+                        for (int st = 0; st < NT; ++st)
+#pragma unroll
+                            for (int s = 0; s < kSub; ++s)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    const uint32_t d = rb[st][s][i];
+                                    rb[st][s][i] = bf16_pair_hi(ldexpf(as_f32(d << 16), kr),
+                                                                ldexpf(as_f32(d & 0xffff0000u), kr));
+                                }
+                        eps_d = ldexp(eps_d, 2 * kr);
+                        row_stats(rb, s2, var, mean, mu, mu_lo);
+                    }
+                }
+            }
+            const double inv64 = 1.0 / sqrt(var + eps_d);
+            const float inv = static_cast<float>(inv64);
+            const uint32_t nrec = gpr / 4;
+            const auto crsrc = TILED ? row_rsrc(a.codes + (r >> 4) * nrec * 1024, nrec * 1024)
+                                     : row_rsrc(a.codes + r * a.gpr * 16, gpr * 16);
+            const auto srsrc = TILED ? row_rsrc(a.scales + (r >> 4) * nrec * 64, nrec * 64)
+                                     : row_rsrc(a.scales + r * a.gpr, gpr);
+            const uint32_t r16 = static_cast<uint32_t>(r & 15);
+#pragma unroll
+            for (int st = 0; st < NT; ++st) {
+                uint32_t word[kSub], sc[kSub];
+#pragma unroll
+                for (int s = 0; s < kSub; ++s) {
+                    const int ss = st * kSub + s;
+                    const f32x4_t m0 = fm[(ss * 2 + 0) * kWave + lane];
+                    const f32x4_t m1 = fm[(ss * 2 + 1) * kWave + lane];
+                    const f32x4_t b0 = fb[(ss * 2 + 0) * kWave + lane];
+                    const f32x4_t b1 = fb[(ss * 2 + 1) * kWave + lane];
+                    float f[8], xp[8], v[8];
+                    widen8<kFp16>(rb[st][s], f);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const float d0 = NORM == kLayer ? ((f[t] - mu) - mu_lo) * inv : f[t] * inv;
+                        const float d1 = NORM == kLayer ? ((f[4 + t] - mu) - mu_lo) * inv : f[4 + t] * inv;
+                        xp[t] = __builtin_fmaf(d0, m0[t], b0[t]);
+                        xp[4 + t] = __builtin_fmaf(d1, m1[t], b1[t]);
+                    }
+                    rotate3(xp, v);
+                    uint32_t sbits = e8m0_scale_bits(group_amax8(v)), cbits = sbits;
+                    int ksh = 0;
+                    const bool tiny = sbits < kTinyScaleBits;
+                    if (any_lane(tiny)) {
+                        const int k = tiny ? tiny_shift(group_amax8(xp)) : 0;
+                        const float inv_k = static_cast<float>(ldexp(inv64, k));
+                        const float up = as_f32(static_cast<uint32_t>(127 + k) << 23);
+                        float xs[8], w[8];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) {
+                            const float d0 = NORM == kLayer ? ((f[t] - mu) - mu_lo) * inv_k : f[t] * inv_k;
+                            const float d1 = NORM == kLayer ? ((f[4 + t] - mu) - mu_lo) * inv_k : f[4 + t] * inv_k;
+                            xs[t] = __builtin_fmaf(d0, m0[t], b0[t] * up);
+                            xs[4 + t] = __builtin_fmaf(d1, m1[t], b1[t] * up);
+                        }
+                        rotate3(xs, w);
+                        uint32_t s2b, c2b;
+                        shifted_scale_bits(group_amax8(w), k, s2b, c2b);
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) v[t] = tiny ? w[t] : v[t];
+                        sbits = tiny ? s2b : sbits;
+                        cbits = tiny ? c2b : cbits;
+                        ksh = k;
+                    }
+                    sc[s] = sbits >> 23;
+                    word[s] = encode8(v, as_f32(cbits));
+                    if constexpr (YOUT) {
+                        const float down = pow2_neg(ksh);
+                        const auto yrsrc = row_rsrc(a.y + r * a.gpr * kGroup, gpr * kGroup * 4);
+                        const uint32_t off = (static_cast<uint32_t>(kTileGroups * st + 16 * s + j) * kGroup + 8 * q) * 4;
+                        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{as_u32(v[0] * down), as_u32(v[1] * down),
+                                                                       as_u32(v[2] * down), as_u32(v[3] * down)},
+                                                               yrsrc, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{as_u32(v[4] * down), as_u32(v[5] * down),
+                                                                       as_u32(v[6] * down), as_u32(v[7] * down)},
+                                                               yrsrc, off + 16, 0, 0);
+                    }
+                }
+                transpose_words(word);
+                const uint32_t S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
+                const uint32_t g = static_cast<uint32_t>(kTileGroups * st + lane);
+                const uint32_t slot = TILED ? (g >> 2) * 64 + (g & 3) * 16 + r16 : g;
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{word[0], word[1], word[2], word[3]}, crsrc, slot * 16, 0,
+                                                       0);
+                __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, slot, 0, 0);
+            }
         }
     }
 }
@@ -478,11 +676,12 @@ mxq_status norm_impl(const void* x, int32_t x_dtype, int64_t tokens, int64_t cha
     if (tokens < 0 || channels < 0 || channels % kGroup || channels > kMaxTiles * kTileGroups * kGroup ||
         tokens >= (int64_t(1) << 31) || (tiled && channels % 128))
         return MXQ_ERR_SHAPE;
-    if (!(eps >= 0.0f) || eps > 3.0e38f) return MXQ_ERR_SHAPE;
+    if (!(eps >= 0.0f) || !(eps <= 3.4028234663852886e38f)) return MXQ_ERR_SHAPE;  // NaN, negative, inf
     if (tokens == 0 || channels == 0) return MXQ_OK;
     if (!x || !gamma || !r_hat || !codes || !scales) return MXQ_ERR_NULL;
     if (x_row_stride < channels) return MXQ_ERR_STRIDE;
     if (!aligned_to(x, 16) || (x_row_stride * 2) % 16 || !aligned_to(codes, 16) || !aligned_to(r_hat, 2) ||
+        (tiled && !aligned_to(scales, 16)) ||
         !aligned_to(gamma, 4) || (beta && !aligned_to(beta, 4)) || (lambda && !aligned_to(lambda, 4)) ||
         (y_rot && !aligned_to(y_rot, 16)))
         return MXQ_ERR_ALIGN;

@@ -178,12 +178,6 @@ int oracle_quant(const void *x, int dtype, int64_t tokens, int64_t channels, int
     return 0;
 }
 
-/* Smooth + rotate + quantize (DuQuant++ page sec. 3.3 online side):
- *   x'  = x / lambda (lambda NULL means all ones)        sec. 3.1
- *   y_g = x'_g * R for every 32-channel group g           sec. 3.2 step 4, 3.3
- *   codes, scales = MXFP4(y)                              sec. 2.1
- * r is the shared 32x32 block, row-major, y_n = sum_k x'_k r[k][n]; r_dtype
- * is OR_BF16 (bits) or OR_FP64.  y_out (fp64 [tokens][channels]) may be NULL. */
 /* Smoothing of one element: x' = x / lambda_c (lambda NULL: all ones). */
 static double smooth(double v, const float *lambda, int64_t c) {
     return lambda ? v / (double)lambda[c] : v;
@@ -200,6 +194,12 @@ static void rotate_block(const double *xs, const double R[128][128], int B, doub
     }
 }
 
+/* Smooth + rotate + quantize (DuQuant++ page sec. 3.3 online side):
+ *   x'  = x / lambda (lambda NULL means all ones)        sec. 3.1
+ *   y_g = x'_g * R for every 32-channel group g           sec. 3.2 step 4, 3.3
+ *   codes, scales = MXFP4(y)                              sec. 2.1
+ * r is the shared 32x32 block, row-major, y_n = sum_k x'_k r[k][n]; r_dtype
+ * is OR_BF16 (bits) or OR_FP64.  y_out (fp64 [tokens][channels]) may be NULL. */
 int oracle_rotate_quant(const void *x, int dtype, int64_t tokens, int64_t channels, int64_t stride,
                         const float *lambda, const void *r, int r_dtype,
                         uint8_t *codes, uint8_t *scales, double *y_out) {
@@ -228,7 +228,6 @@ int oracle_rotate_quant(const void *x, int dtype, int64_t tokens, int64_t channe
     return 0;
 }
 
-/* Dequantize: value = (-1)^s * E2M1[m] * 2^(S - 127); S = 255 gives NaN. */
 /* Rotation by a B x B block (B = 16, 32, 64 or 128; r is B x B, row-major,
  * y_n = sum_k x'_k r[k][n] within each block of B channels), then MXFP4 of
  * every 32-element group of the rotated row.  channels must be a multiple
@@ -321,6 +320,7 @@ int oracle_norm_rotate_quant(const void *x, int dtype, int64_t tokens, int64_t c
     return 0;
 }
 
+/* Dequantize: value = (-1)^s * E2M1[m] * 2^(S - 127); S = 255 gives NaN. */
 int oracle_dequant(const uint8_t *codes, const uint8_t *scales, int64_t tokens, int64_t channels,
                    double *out) {
     static const double e2m1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};

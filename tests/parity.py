@@ -4,11 +4,16 @@ Rules (the fused path computes the rotation in fp32 on the matrix cores, the
 oracle in fp64, so an integer decision can differ only where the exact value
 sits on a decision boundary):
 
-* rotated values: |y_gpu - y*| <= 1e-5 * ||x'_g||_2 for every element of
-  group g (x' = x / lambda), an absolute bound per group because a purely
-  relative bound fails on cancellation;
+* rotated values: |y_gpu - y*| <= 1e-5 * ||x'_g||_2 + 2^-149 for every
+  element of group g (x' = x / lambda), an absolute bound per group because a
+  purely relative bound fails on cancellation; 2^-149, fp32's smallest
+  subnormal, is what an fp32 output cannot resolve (groups far below fp32's
+  normal range);
 * same-precision decisions: the oracle's encoder applied to the GPU's own
-  fp32 rotated values reproduces the GPU's codes and scales bit for bit;
+  fp32 rotated values reproduces the GPU's codes and scales bit for bit,
+  except in groups with a scale byte below 61 (a rotated maximum below
+  2^-64) that hold fp32 subnormal outputs: the kernel decides those groups on
+  values 2^k times larger, of which the subnormal outputs are roundings;
 * against the oracle's fp64 decisions: at most 1e-4 of the scales and 1e-4
   of the codes differ; a differing scale is one E8M0 step away and the
   oracle's group maximum lies within 1e-5 * ||x'_g|| of the power of two that
@@ -26,6 +31,8 @@ import oracle as O
 GROUP = 32
 TOL = 1e-5
 MAX_RATE = 1e-4
+FP32_FLOOR = 2.0 ** -149  # smallest fp32 subnormal
+TINY_SCALE = 61           # scale byte of a group maximum 2^-64
 
 # signed E2M1 grid in increasing order, with 0 and -0 as one point
 _SIGNED = np.array([-6, -4, -3, -2, -1.5, -1, -0.5, 0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float64)
@@ -48,7 +55,7 @@ def smoothed_group_norms(x: torch.Tensor, lam) -> np.ndarray:
 def check_rotated_values(y_gpu: np.ndarray, y_ref: np.ndarray, norms: np.ndarray):
     T, C = y_ref.shape
     err = np.abs(y_gpu.astype(np.float64) - y_ref).reshape(T, C // GROUP, GROUP).max(axis=2)
-    bound = TOL * norms
+    bound = TOL * norms + FP32_FLOOR
     bad = err > bound
     worst = float(np.max(err / np.maximum(norms, 1e-300)))
     assert not bad.any(), f"{int(bad.sum())} groups exceed 1e-5*||x'_g||; worst ratio {worst:.3e}"
@@ -58,9 +65,14 @@ def check_rotated_values(y_gpu: np.ndarray, y_ref: np.ndarray, norms: np.ndarray
 def check_same_precision(y_gpu: np.ndarray, codes: np.ndarray, scales: np.ndarray, orc=None):
     orc = orc or O.default()
     T, C = y_gpu.shape
-    c_ref, s_ref = orc.encode_groups(y_gpu.astype(np.float64).reshape(-1, GROUP))
-    assert np.array_equal(s_ref.reshape(scales.shape), scales), "scales differ from oracle(y_gpu)"
-    assert np.array_equal(c_ref.reshape(codes.shape), codes), "codes differ from oracle(y_gpu)"
+    yg = y_gpu.astype(np.float64).reshape(-1, GROUP)
+    c_ref, s_ref = orc.encode_groups(yg)
+    keep = ~((scales.reshape(-1) < TINY_SCALE) & ((yg != 0) & (np.abs(yg) < 2.0 ** -126)).any(axis=1))
+    s_ref, s_got = s_ref.reshape(-1)[keep], scales.reshape(-1)[keep]
+    c_ref, c_got = c_ref.reshape(-1, GROUP // 2)[keep], codes.reshape(-1, GROUP // 2)[keep]
+    assert np.array_equal(s_ref, s_got), "scales differ from oracle(y_gpu)"
+    assert np.array_equal(c_ref, c_got), "codes differ from oracle(y_gpu)"
+    return int((~keep).sum())
 
 
 def check_against_oracle(codes, scales, c_ref, s_ref, y_ref_rows, norms):

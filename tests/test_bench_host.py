@@ -40,7 +40,8 @@ def test_source_hash_is_stable():
 # Every committed HBM counter summary was taken on the current kernel
 # sources: read_counters hands back its per-launch bytes (a kernel edit
 # without new counters makes the bench report traffic null, and fails here).
-SUMMARIES = [(bench.COUNTERS[3], bench.KERNEL_SOURCES), (bench.GEMM_COUNTERS, bench.GEMM_SOURCES),
+SUMMARIES = [(bench.COUNTERS[w], bench.KERNEL_SOURCES) for w in (2, 3, 4, 5)] + [
+             (bench.GEMM_COUNTERS, bench.GEMM_SOURCES),
              (bench.DECODE_COUNTERS[16], bench.GEMM_SOURCES), (bench.NORM_COUNTERS, bench.NORM_SOURCES)]
 
 

@@ -49,7 +49,8 @@ def full_check(x, r, gamma, beta, lam, norm, eps, dev, orc):
     codes, scales, y = run_gpu(x, r, gamma, beta, lam, norm, eps, dev)
     c2, s2, _ = run_gpu(x, r, gamma, beta, lam, norm, eps, dev, want_y=False)
     assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
-    c_ref, s_ref, y_ref = orc.norm_rotate_quant(x, norm, gamma, beta, eps, lam, r, want_y=True)
+    # the kernel receives eps as fp32: the oracle gets that same value
+    c_ref, s_ref, y_ref = orc.norm_rotate_quant(x, norm, gamma, beta, float(np.float32(eps)), lam, r, want_y=True)
     norms = group_norms(y_ref)
     worst = check_rotated_values(y, y_ref, norms)
     check_same_precision(y, codes, scales, orc)
@@ -123,7 +124,8 @@ def test_norm_bench_workload_sampled(dev, orc):
     codes, scales, y = run_gpu(wl.x, wl.r_hat, wl.gamma, None, wl.lam, "rms", wl.eps, dev)
     rows = np.sort(np.random.default_rng(4204).choice(wl.x.shape[0], 256, replace=False))
     xs = wl.x[torch.from_numpy(rows)]
-    c_ref, s_ref, y_ref = orc.norm_rotate_quant(xs, "rms", wl.gamma, None, wl.eps, wl.lam, wl.r_hat, want_y=True)
+    c_ref, s_ref, y_ref = orc.norm_rotate_quant(xs, "rms", wl.gamma, None, float(np.float32(wl.eps)), wl.lam,
+                                                wl.r_hat, want_y=True)
     norms = group_norms(y_ref)
     check_rotated_values(y[rows], y_ref, norms)
     stats = check_against_oracle(codes[rows], scales[rows], c_ref, s_ref, lambda rr: y_ref[rr], norms)
