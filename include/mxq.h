@@ -342,6 +342,22 @@ mxq_status mxq_calib_givens(double *x_worst, int64_t tokens, int32_t max_steps, 
                             double *linf_history, int32_t *steps_done, int32_t *pairs, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/* mxq_calib_worst_group_noalloc: mxq_calib_worst_group for callers that
+ *   cannot allocate device memory -- code under HIP graph capture, tight
+ *   serving loops, harnesses that forbid hipMalloc.  It takes no workspace
+ *   and allocates nothing: the per-group maxima live in a device array of
+ *   the library (64 KiB, one per GPU, held until the process ends), so
+ *   channels is limited to 262144 (MXQ_ERR_SHAPE above that, before any HIP
+ *   call).  Every call on one GPU shares that array; the call clears what it
+ *   uses before reading it, and calls that overlap on one GPU (other
+ *   streams, other threads) race.  The array's address is looked up on the
+ *   first call on each device (MXQ_ERR_HIP if that fails).  Same outputs,
+ *   bit for bit, and the same other rules and errors as
+ *   mxq_calib_worst_group. */
+mxq_status mxq_calib_worst_group_noalloc(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
+                                         int64_t x_row_stride, const float *lambda, double *x_worst,
+                                         int64_t *group, double *linf, void *stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *mxq_status_str(int32_t status);
 

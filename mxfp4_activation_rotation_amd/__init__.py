@@ -26,7 +26,7 @@ EXPORTS = ("mxq_rotate_quant", "mxq_rotate_quant_ex", "mxq_quant", "mxq_dequant"
            "mxq_status_str", "mxq_plan", "mxq_version", "mxq_calib_workspace_bytes",
            "mxq_calib_worst_group", "mxq_calib_givens", "mxq_absorb_quant", "mxq_gemm_mxfp4",
            "mxq_norm_rotate_quant", "mxq_rotate_quant_block", "mxq_tile_mxfp4", "mxq_rotate_quant_tiled",
-           "mxq_gemm_mxfp4_tiled", "mxq_norm_rotate_quant_tiled")
+           "mxq_gemm_mxfp4_tiled", "mxq_norm_rotate_quant_tiled", "mxq_calib_worst_group_noalloc")
 
 _lib = None
 
@@ -64,6 +64,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.mxq_calib_workspace_bytes.restype = sz
     lib.mxq_calib_worst_group.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]
     lib.mxq_calib_givens.argtypes = [vp, i64, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.mxq_calib_worst_group_noalloc.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
     lib.mxq_absorb_quant.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
     lib.mxq_gemm_mxfp4.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp]
     lib.mxq_gemm_mxfp4_tiled.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp]
@@ -77,7 +78,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     for f in ("mxq_rotate_quant", "mxq_rotate_quant_ex", "mxq_quant", "mxq_dequant", "mxq_plan",
               "mxq_version", "mxq_calib_worst_group", "mxq_calib_givens", "mxq_absorb_quant",
               "mxq_gemm_mxfp4", "mxq_norm_rotate_quant", "mxq_rotate_quant_block", "mxq_tile_mxfp4",
-              "mxq_rotate_quant_tiled", "mxq_gemm_mxfp4_tiled", "mxq_norm_rotate_quant_tiled"):
+              "mxq_rotate_quant_tiled", "mxq_gemm_mxfp4_tiled", "mxq_norm_rotate_quant_tiled",
+              "mxq_calib_worst_group_noalloc"):
         getattr(lib, f).restype = ctypes.c_int32
     if path is None:
         _lib = lib
@@ -367,6 +369,33 @@ def calib_worst_group(x: torch.Tensor, lam: torch.Tensor | None = None, *, strea
                                    _ptr(linf), _aligned256(ws), n, _stream(x, stream))
     if st != 0:
         raise MXQError("mxq_calib_worst_group", st)
+    return xw, group, linf
+
+
+def calib_worst_group_noalloc(x: torch.Tensor, lam: torch.Tensor | None = None, *, x_worst=None, group=None,
+                              linf=None, stream=None):
+    """:func:`calib_worst_group` through the entry point that allocates
+    nothing (its scratch is a library-owned device array; channels <= 262144).
+    The outputs may be passed in, so a caller that cannot allocate can make
+    the whole call without allocating."""
+    lib = load()
+    T, C, stride = _check_x(x, (torch.bfloat16, torch.float16, torch.float32))
+    if lam is not None and (lam.dtype != torch.float32 or lam.shape != (C,) or not lam.is_contiguous()):
+        raise ValueError("lam must be a contiguous fp32 [channels] tensor")
+    if lam is not None:
+        _on("lam", lam, x.device)
+    xw = torch.empty((T, 32), dtype=torch.float64, device=x.device) if x_worst is None else x_worst
+    group = torch.empty((), dtype=torch.int64, device=x.device) if group is None else group
+    linf = torch.empty((), dtype=torch.float64, device=x.device) if linf is None else linf
+    for name, t, dt, shape in (("x_worst", xw, torch.float64, (T, 32)), ("group", group, torch.int64, ()),
+                               ("linf", linf, torch.float64, ())):
+        if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor of shape {shape}")
+        _on(name, t, x.device)
+    st = lib.mxq_calib_worst_group_noalloc(_ptr(x), _DT[x.dtype], T, C, stride, _ptr(lam), _ptr(xw), _ptr(group),
+                                           _ptr(linf), _stream(x, stream))
+    if st != 0:
+        raise MXQError("mxq_calib_worst_group_noalloc", st)
     return xw, group, linf
 
 

@@ -28,6 +28,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/mxq.h"
 #include "mxq_device.h"
 #include "mxq_internal.h"
@@ -461,11 +464,79 @@ static mxq_status calib_givens(double* x_worst, int64_t tokens, int32_t max_step
     return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 
+// ---- the worst-group scan without a workspace ---------------------------------
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops, harnesses that forbid hipMalloc): the per-group maxima live
+// in a file-scope device array instead of the caller's workspace.  Each GPU
+// the library runs on holds its own copy (64 KiB, kept until the process
+// ends); its address is looked up once per device, with that device current,
+// and every call on that GPU shares it: the scan's fill kernel clears the
+// entries a call uses before the call reads them, and calls that overlap on
+// one GPU race.
+constexpr int64_t kScratchGroups = 8192;  // channels <= 262144
+static __device__ __align__(256) uint64_t scratch[kScratchGroups];
+constexpr int kMaxDevices = 64;
+
+static mxq_status scratch_ptr(uint64_t** out) {
+    static std::atomic<uint64_t*> ptrs[kMaxDevices];
+    static std::mutex lookup;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MXQ_ERR_HIP;
+    uint64_t* p = ptrs[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> guard(lookup);
+        p = ptrs[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            void* addr = nullptr;
+            if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return MXQ_ERR_HIP;
+            p = static_cast<uint64_t*>(addr);
+            ptrs[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MXQ_OK;
+}
+
+static mxq_status calib_worst_group_noalloc(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels,
+                                            int64_t stride, const float* lambda, double* x_worst, int64_t* group,
+                                            double* linf, void* stream) {
+    if (x_dtype != MXQ_BF16 && x_dtype != MXQ_FP16 && x_dtype != MXQ_FP32) return MXQ_ERR_DTYPE;
+    if (tokens <= 0 || channels <= 0 || channels % calib::kW || channels > kScratchGroups * calib::kW ||
+        tokens > (int64_t(1) << 40) / channels)
+        return MXQ_ERR_SHAPE;
+    if (!x || !x_worst || !group || !linf) return MXQ_ERR_NULL;
+    if (stride < channels) return MXQ_ERR_STRIDE;
+    if ((reinterpret_cast<uintptr_t>(x_worst) & 7) || (reinterpret_cast<uintptr_t>(group) & 7) ||
+        (reinterpret_cast<uintptr_t>(linf) & 7))
+        return MXQ_ERR_ALIGN;
+    uint64_t* gmax = nullptr;
+    const mxq_status s = scratch_ptr(&gmax);
+    if (s != MXQ_OK) return s;
+    const int64_t gpr = channels / calib::kW;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (x_dtype * 2 + (lambda ? 1 : 0)) {
+        case MXQ_BF16 * 2: launch_worst<MXQ_BF16, false>(x, stride, lambda, tokens, gpr, gmax, group, linf, x_worst, st); break;
+        case MXQ_BF16 * 2 + 1: launch_worst<MXQ_BF16, true>(x, stride, lambda, tokens, gpr, gmax, group, linf, x_worst, st); break;
+        case MXQ_FP16 * 2: launch_worst<MXQ_FP16, false>(x, stride, lambda, tokens, gpr, gmax, group, linf, x_worst, st); break;
+        case MXQ_FP16 * 2 + 1: launch_worst<MXQ_FP16, true>(x, stride, lambda, tokens, gpr, gmax, group, linf, x_worst, st); break;
+        case MXQ_FP32 * 2: launch_worst<MXQ_FP32, false>(x, stride, lambda, tokens, gpr, gmax, group, linf, x_worst, st); break;
+        default: launch_worst<MXQ_FP32, true>(x, stride, lambda, tokens, gpr, gmax, group, linf, x_worst, st); break;
+    }
+    return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+}
+
 }  // namespace mxq
 
 extern "C" {
 
 size_t mxq_calib_workspace_bytes(int64_t channels) { return mxq::calib_workspace_bytes(channels); }
+
+mxq_status mxq_calib_worst_group_noalloc(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels,
+                                         int64_t x_row_stride, const float* lambda, double* x_worst,
+                                         int64_t* group, double* linf, void* stream) {
+    return mxq::calib_worst_group_noalloc(x, x_dtype, tokens, channels, x_row_stride, lambda, x_worst, group, linf,
+                                          stream);
+}
 
 mxq_status mxq_calib_worst_group(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels,
                                  int64_t x_row_stride, const float* lambda, double* x_worst, int64_t* group,

@@ -140,6 +140,22 @@ def test_calibration_validation(lib):
     assert g(ctypes.c_void_p(0x10004), 8, 128, P, P, P, None, W16, ws, None) == ALIGN
 
 
+def test_calibration_noalloc_validation(lib):
+    """The allocation-free scan rejects bad arguments, and channels above its
+    scratch limit (262144), on the host before any HIP call."""
+    w = lib.mxq_calib_worst_group_noalloc
+    assert w(P, 5, 8, 64, 64, None, P, P, P, None) == DTYPE
+    assert w(P, 0, 0, 64, 64, None, P, P, P, None) == SHAPE
+    assert w(P, 0, 8, 48, 48, None, P, P, P, None) == SHAPE
+    assert w(P, 0, 1, 262144 + 32, 262144 + 32, None, P, P, P, None) == SHAPE
+    assert w(P, 0, 1, 1 << 20, 1 << 20, None, P, P, P, None) == SHAPE
+    assert w(None, 0, 8, 64, 64, None, P, P, P, None) == NULL
+    assert w(P, 0, 8, 64, 64, None, P, None, P, None) == NULL
+    assert w(P, 0, 8, 64, 32, None, P, P, P, None) == STRIDE
+    assert w(P, 0, 8, 64, 64, None, ctypes.c_void_p(0x10004), P, P, None) == ALIGN
+    assert b"SHAPE" in lib.mxq_status_str(SHAPE)
+
+
 def aq(lib, w=P, dt=0, N=8, K=64, stride=64, lam=None, r=P, codes=P, scales=P):
     return lib.mxq_absorb_quant(w, dt, N, K, stride, lam, r, codes, scales, None)
 
