@@ -90,19 +90,22 @@ typedef enum { MXQ_NORM_RMS = 0, MXQ_NORM_LAYER = 1 } mxq_norm_kind;
  *   r_hat    the shared 32x32 block in bf16
  *   codes, scales  outputs, fully overwritten
  * The rotation runs on the matrix cores with bf16 operands and fp32
- * accumulation.  The activations are split into bf16 terms whose sum is
- * exactly the fp32 value of x' (bf16 x: 1 term; fp16 x: 2 terms; with lambda:
- * 3 terms of x' = x * rcp(lambda), rcp the hardware reciprocal, within 1 ulp),
- * so the products are exact and only the fp32 accumulation rounds.  That
- * holds at every magnitude: a group whose rotated maximum is below 2^-64
- * (whose bf16 terms or products would fall below bf16's or fp32's normal
- * range) is recomputed from x' * 2^k, k <= 64 a power-of-two shift chosen
- * from the group's largest |x'| (x * (factor * 2^k) formed exactly in fp64
- * and rounded to fp32 once), and encoded with its scale reduced by k.  So
- * every rotated value of a group g is within the fp32 accumulation error of
- * its 32 terms plus about 2^-23 ||x'_g||_2 (the rounding of x' to fp32) of
- * the exact x'_g R, for groups of any size; the y_rot output
- * (mxq_rotate_quant_ex) of a group below fp32's normal range is that value
+ * accumulation.  Without lambda the activations enter as bf16 terms whose
+ * sum is exactly x (bf16 x: 1 term; fp16 x: 2 terms), so the products are
+ * exact and only the fp32 accumulation rounds.  With lambda, x' = x *
+ * rcp(lambda) (rcp the hardware reciprocal, within 1 ulp; fp16 x times the
+ * factor in one fused multiply, rounded once) enters as two bf16 terms, each
+ * rounded to nearest: hi = bf16(x'), lo = bf16(x' - hi), |x' - hi - lo| <=
+ * 2^-18 |x'|.  So every rotated value of a group g is within about
+ * 2^-18 ||x'_g||_2 (lambda) or 0 (no lambda), plus the fp32 accumulation
+ * error of its 32 terms, of the exact x'_g R.  That holds at every
+ * magnitude: a group whose rotated maximum is below 2^-64 (whose bf16 terms
+ * or products would fall below bf16's or fp32's normal range) is
+ * recomputed, after the main pass over the rows, from x' * 2^k, k <= 64 a
+ * power-of-two shift chosen from the group's largest |x'| (x * (factor *
+ * 2^k) formed exactly in fp64, rounded to fp32 once, then split into 3 exact
+ * bf16 terms), and encoded with its scale reduced by k; the y_rot output
+ * (mxq_rotate_quant_ex) of a group below fp32's normal range is its value
  * rounded to fp32.  Rows holding such groups cost a second pass; ordinary
  * data has none.
  * lambda entries must be finite normal fp32 values with |lambda| in
@@ -143,7 +146,8 @@ mxq_status mxq_dequant(const uint8_t *codes, const uint8_t *scales, int64_t toke
  * (MXQ_ERR_SHAPE otherwise); y_rot may be NULL or fp32 [tokens][channels].
  * B = 32 gives the same bits as mxq_rotate_quant (same arithmetic, a kernel
  * not tuned for speed); otherwise the same arithmetic, layout and error
- * rules: the product runs on the matrix cores with exact bf16 terms of x'. */
+ * rules: the product runs on the matrix cores with the bf16 terms of x' that
+ * mxq_rotate_quant uses (exact without lambda, two rounded terms with it). */
 mxq_status mxq_rotate_quant_block(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
                                   int64_t x_row_stride, const float *lambda, const uint16_t *r_block,
                                   int32_t block, uint8_t *codes, uint8_t *scales, float *y_rot,
@@ -175,8 +179,8 @@ mxq_status mxq_rotate_quant_block(const void *x, int32_t x_dtype, int64_t tokens
  * error scales with the row's spread, not its mean; 1/sqrt in fp64,
  * rounded to fp32; x'_c = fma(n_c, gamma_c/lambda_c,
  * beta_c/lambda_c) in fp32 (the two factors formed once per block with IEEE
- * division); the product with the block as in mxq_rotate_quant (3 exact
- * bf16 terms).  Every finite 16-bit row is in range: a bf16 row whose fp32
+ * division); the product with the block as in mxq_rotate_quant with lambda
+ * (two bf16 terms rounded to nearest, within 2^-18 |x'|).  Every finite 16-bit row is in range: a bf16 row whose fp32
  * sum of squares leaves [2^-80, 2^1000] (squares beyond fp32's range, or lost
  * below it) is scaled by a power of two 2^kr taken from its largest |h| and
  * its statistics retaken, with eps scaled by 2^(2 kr), which leaves the
@@ -206,8 +210,9 @@ mxq_status mxq_norm_rotate_quant(const void *x, int32_t x_dtype, int64_t tokens,
  *   (same convention as mxq_rotate_quant: y_n = sum_k w'_k r_hat[k][n]) and
  *   MXFP4-encoded along K: codes [rows][cols/2], scales [rows][cols/32], the
  *   B operand of mxq_gemm_mxfp4.  The product w * lambda is rounded once to
- *   fp32 and then split into exact bf16 terms, as in mxq_rotate_quant.  Same
- *   rules, limits and errors as mxq_rotate_quant.
+ *   fp32 and then carried as two bf16 terms rounded to nearest, as x' is in
+ *   mxq_rotate_quant (without lambda, exact terms).  Same rules, limits and
+ *   errors as mxq_rotate_quant.
  *
  * mxq_gemm_mxfp4: y[m][n] = sum_k dq(A)[m][k] * dq(B)[n][k], where
  *   A = (a_codes [M][K/2], a_scales [M][K/32]) are quantized activations as

@@ -58,6 +58,22 @@
 #ifndef MXQ_BATCH_SPLIT
 #define MXQ_BATCH_SPLIT 1
 #endif
+// Smoothed instances (x * 1/lambda, x * lambda: two rounded bf16 terms)
+// keep two rows in flight per wave at 12 waves per CU.
+#ifndef MXQ_WAVES_PER_CU_LAM
+#define MXQ_WAVES_PER_CU_LAM 12
+#endif
+#ifndef MXQ_BATCH_LAM
+#define MXQ_BATCH_LAM 2
+#endif
+// fp16 x times its factor in one v_fma_mix_f32; bf16 terms of a smoothed
+// x' (2: each rounded to nearest, |x' - hi - lo| <= 2^-18 |x'|; 3: exact).
+#ifndef MXQ_FMA_MIX
+#define MXQ_FMA_MIX 1
+#endif
+#ifndef MXQ_LAM_TERMS
+#define MXQ_LAM_TERMS 2
+#endif
 #ifndef MXQ_NT_LOAD
 #define MXQ_NT_LOAD 1
 #endif
@@ -106,9 +122,13 @@ enum : int { kLamNone = 0, kLamDiv = 1, kLamMul = 2 };
 template <int XT, int MODE, int LAM>
 constexpr bool kSplit = MODE == 1 && (XT != MXQ_BF16 || LAM != kLamNone);
 template <int XT, int MODE, int LAM>
-constexpr int kBatchOf = kSplit<XT, MODE, LAM> ? MXQ_BATCH_SPLIT : MXQ_BATCH;  // rows in flight per wave
+constexpr int kBatchOf = (MODE == 1 && LAM != kLamNone) ? MXQ_BATCH_LAM
+                         : kSplit<XT, MODE, LAM>         ? MXQ_BATCH_SPLIT
+                                                         : MXQ_BATCH;  // rows in flight per wave
 template <int XT, int MODE, int LAM>
-constexpr int kWavesPerCuOf = kSplit<XT, MODE, LAM> ? MXQ_WAVES_PER_CU_SPLIT : MXQ_WAVES_PER_CU;
+constexpr int kWavesPerCuOf = (MODE == 1 && LAM != kLamNone) ? MXQ_WAVES_PER_CU_LAM
+                              : kSplit<XT, MODE, LAM>         ? MXQ_WAVES_PER_CU_SPLIT
+                                                              : MXQ_WAVES_PER_CU;
 
 enum : int { kBF16 = MXQ_BF16, kFP16 = MXQ_FP16, kFP32 = MXQ_FP32 };
 enum : int { kQuant = 0, kRotate = 1 };
@@ -138,10 +158,22 @@ constexpr bool kGuardTiny = !(XT == kFP16 && LAM == kLamNone);
 // x' of a lane's 8 channels in fp32: x * (1/lambda), x * lambda, or x.
 template <int XT, int LAM>
 __device__ __forceinline__ void smoothed8(u32x4_t xq, const float* il, float* f) {
-    widen8<XT == kFP16>(xq, f);
-    if constexpr (LAM != kLamNone) {
+    if constexpr (XT == kFP16 && LAM != kLamNone && MXQ_FMA_MIX) {
+        // fp16 x times an fp32 factor in one v_fma_mix_f32 (fp16 source
+        // widened inside the instruction): the exact product rounded once
 #pragma unroll
-        for (int t = 0; t < 8; ++t) f[t] *= il[t];
+        for (int i = 0; i < 4; ++i) {
+            const _Float16 h0 = __builtin_bit_cast(_Float16, static_cast<uint16_t>(xq[i] & 0xffffu));
+            const _Float16 h1 = __builtin_bit_cast(_Float16, static_cast<uint16_t>(xq[i] >> 16));
+            f[2 * i] = __builtin_fmaf(static_cast<float>(h0), il[2 * i], 0.0f);
+            f[2 * i + 1] = __builtin_fmaf(static_cast<float>(h1), il[2 * i + 1], 0.0f);
+        }
+    } else {
+        widen8<XT == kFP16>(xq, f);
+        if constexpr (LAM != kLamNone) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) f[t] *= il[t];
+        }
     }
 }
 
@@ -177,6 +209,24 @@ __device__ __forceinline__ void rotate8(u32x4_t xq, const float* il, bf16x8_t A0
         } else {
             smoothed8<XT, LAM>(xq, il, f);
         }
+        if constexpr (LAM != kLamNone && MXQ_LAM_TERMS == 2 && !SHIFT) {
+            // two bf16 terms, each rounded to nearest: hi = bf16(x'),
+            // lo = bf16(x' - hi); |x' - hi - lo| <= 2^-18 |x'|
+            typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+            typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+            u32x4_t hi, lo;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bf16x2_t h = __builtin_convertvector(f32x2_t{f[2 * i], f[2 * i + 1]}, bf16x2_t);
+                hi[i] = __builtin_bit_cast(uint32_t, h);
+                const f32x2_t r = f32x2_t{f[2 * i], f[2 * i + 1]} - __builtin_convertvector(h, f32x2_t);
+                lo[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+            }
+            d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8_t, hi), d0, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, __builtin_bit_cast(bf16x8_t, hi), d1, 0, 0, 0);
+            d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8_t, lo), d0, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, __builtin_bit_cast(bf16x8_t, lo), d1, 0, 0, 0);
+        } else {
         constexpr int kTerms = LAM != kLamNone ? 3 : (XT == kFP16 ? 2 : 1);
 #pragma unroll
         for (int term = 0; term < kTerms; ++term) {
@@ -190,6 +240,7 @@ __device__ __forceinline__ void rotate8(u32x4_t xq, const float* il, bf16x8_t A0
 #pragma unroll
                 for (int t = 0; t < 8; ++t) f[t] = bf16_residual(f[t]);
             }
+        }
         }
     }
 #pragma unroll
@@ -209,7 +260,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
                           amdgpu_waves_per_eu((YOUT || TILED) ? 2 : kWavesPerCuOf<XT, MODE, LAM> / 4))) void quant_kernel(Args a) {
     constexpr int kN = (XT == kFP32) ? 2 : 1;  // 16-byte loads per lane per sub-tile
     constexpr uint32_t esz = (XT == kFP32) ? 4 : 2;
-    constexpr int kBatch = kBatchOf<XT, MODE, LAM>;
+    constexpr int kBatch = TILED ? 1 : kBatchOf<XT, MODE, LAM>;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int w = static_cast<int>(blockIdx.x) * kWavesPerBlock + wave;

@@ -171,6 +171,32 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
                     smoothed(xin[s][k], s, k, f[k]);
                 }
             }
+            if constexpr (LAM && !SHIFT) {
+                // x' as two bf16 terms rounded to nearest, as in the main
+                // kernel (|x' - hi - lo| <= 2^-18 |x'|), so B = 32 gives its bits
+                typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+                typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+#pragma unroll
+                for (int k = 0; k < KB; ++k) {
+                    u32x4_t hi, lo;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const f32x2_t p2 = f32x2_t{f[k][2 * i], f[k][2 * i + 1]};
+                        const bf16x2_t h = __builtin_convertvector(p2, bf16x2_t);
+                        hi[i] = __builtin_bit_cast(uint32_t, h);
+                        lo[i] = __builtin_bit_cast(uint32_t,
+                                                   __builtin_convertvector(p2 - __builtin_convertvector(h, f32x2_t), bf16x2_t));
+                    }
+#pragma unroll
+                    for (int g = 0; g < KB; ++g) {
+                        d0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0][k], __builtin_bit_cast(bf16x8_t, hi), d0[g], 0, 0, 0);
+                        d1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1][k], __builtin_bit_cast(bf16x8_t, hi), d1[g], 0, 0, 0);
+                        d0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0][k], __builtin_bit_cast(bf16x8_t, lo), d0[g], 0, 0, 0);
+                        d1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1][k], __builtin_bit_cast(bf16x8_t, lo), d1[g], 0, 0, 0);
+                    }
+                }
+                return;
+            }
             constexpr int kT = SHIFT && kTerms == 1 ? 1 : kTerms;
 #pragma unroll
             for (int term = 0; term < kT; ++term) {

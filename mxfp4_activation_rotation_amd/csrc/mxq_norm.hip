@@ -45,6 +45,12 @@
 #include "mxq_device.h"
 #include "mxq_internal.h"
 
+// bf16 terms of x' = fma(n, gamma/lambda, beta/lambda): 2, each rounded to
+// nearest (|x' - hi - lo| <= 2^-18 |x'|), or 3 (exact).
+#ifndef MXQ_NORM_TERMS
+#define MXQ_NORM_TERMS 2
+#endif
+
 namespace mxq {
 namespace norm {
 
@@ -346,8 +352,25 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kWave * BW),
                         f[t] = __builtin_fmaf(d0, m0[t], b0[t]);
                         f[4 + t] = __builtin_fmaf(d1, m1[t], b1[t]);
                     }
-                    // exact bf16 terms of the fp32 values (3 terms cover 24 bits)
                     f32x4_t d0 = {}, d1 = {};
+                    if constexpr (MXQ_NORM_TERMS == 2) {
+                        // two bf16 terms, each rounded to nearest
+                        typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+                        typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+                        u32x4_t hi, lo;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const bf16x2_t h = __builtin_convertvector(f32x2_t{f[2 * i], f[2 * i + 1]}, bf16x2_t);
+                            hi[i] = __builtin_bit_cast(uint32_t, h);
+                            const f32x2_t rr = f32x2_t{f[2 * i], f[2 * i + 1]} - __builtin_convertvector(h, f32x2_t);
+                            lo[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rr, bf16x2_t));
+                        }
+                        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8_t, hi), d0, 0, 0, 0);
+                        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, __builtin_bit_cast(bf16x8_t, hi), d1, 0, 0, 0);
+                        d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, __builtin_bit_cast(bf16x8_t, lo), d0, 0, 0, 0);
+                        d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, __builtin_bit_cast(bf16x8_t, lo), d1, 0, 0, 0);
+                    } else {
+                    // exact bf16 terms of the fp32 values (3 terms cover 24 bits)
 #pragma unroll
                     for (int term = 0; term < 3; ++term) {
                         u32x4_t bt;
@@ -360,6 +383,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kWave * BW),
 #pragma unroll
                             for (int t = 0; t < 8; ++t) f[t] = bf16_residual(f[t]);
                         }
+                    }
                     }
                     float v[8];
 #pragma unroll

@@ -147,7 +147,10 @@ def test_layernorm_large_mean_offset(dev, orc, C, dtype, offset, sigma):
     beta = (0.1 * rng.standard_normal(C)).astype(np.float32)
     lam = np.exp(0.5 * rng.standard_normal(C)).astype(np.float32)
     stats = full_check(x, W.bf16_matrix(W.qr_orthogonal(rng)), gamma, beta, lam, "layer", 1e-5, dev, orc)
-    assert stats["worst_abs_err_over_norm"] < 2e-6
+    # x' enters the matrix cores as two rounded bf16 terms (2^-18 |x'| each),
+    # so the worst value sits near 4e-6 of the group norm; a mean rounded
+    # once to fp32 and subtracted gave 3.5e-5 here
+    assert stats["worst_abs_err_over_norm"] < 8e-6
 
 
 @pytest.mark.parametrize("norm", ["rms", "layer"])
