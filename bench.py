@@ -118,8 +118,10 @@ def cpu_baseline(wl, min_seconds: float):
 def bench_calibration(args):
     """Greedy block search (128 steps max) on a 262144 x 32 fp64 block; each
     timed call starts from a fresh copy of the block (copied outside the
-    events).  The scan kernel reads the block once per step and writes the
-    two rotated columns of the previous step."""
+    events).  With pi/4 the scan kernel reads the block once per step and
+    writes the two rotated columns of the previous step; with an angle grid
+    (--angle-grid M) a step applies the previous rotation in one pass and
+    scans every (candidate, angle) pair in ceil(M / 8) more."""
     import numpy as np
     import torch
 
@@ -137,7 +139,10 @@ def bench_calibration(args):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        _, hist, done, _ = mxq.calib_givens(work, 128)
+        if args.angle_grid:
+            _, hist, done, _, _ = mxq.calib_givens_angles(work, 128, args.angle_grid)
+        else:
+            _, hist, done, _ = mxq.calib_givens(work, 128)
         e1.record()
         e1.synchronize()
         if i >= 3:
@@ -145,15 +150,22 @@ def bench_calibration(args):
     steps = int(done)
     ms = float(np.median(times))
     T = xw_host.shape[0]
-    scans = steps + 2  # init scan, one per step (the last step's pass finds no better candidate), final apply
     bytes_per_scan = T * 32 * 8
+    if args.angle_grid:
+        # init scan; per step executed (steps + 1, the last one refused or the
+        # 128th): an apply pass (none before the first) and ceil(M / 8) angle scans
+        executed = min(steps + 1, 128)
+        scans = 1 + executed * (1 + -(-args.angle_grid // 8))
+    else:
+        scans = steps + 2  # init scan, one per step (the last step's pass finds no better candidate), final apply
     result = {
         "metric": "greedy block calibration time (DuQuant++ page sec. 3.2), GPU fp64",
         "value": round(ms, 3), "unit": "ms per search", "higher_is_better": False, "n_gpus": 1,
         "steps": reps, "data": "synthetic",
         "config": {"workload": "page-scale X_worst: 128 x 2048 tokens x 32 channels fp64, Student-t(3) "
                                "background, +-U(200,800) on 2000 tokens of channel 9",
-                   "tokens": T, "max_steps": 128, "steps_taken": steps},
+                   "tokens": T, "max_steps": 128, "steps_taken": steps,
+                   "angle": f"grid of {args.angle_grid} per candidate" if args.angle_grid else "pi/4"},
         "ms_per_step": round(ms / max(steps, 1), 4),
         "scan_bytes_per_step": bytes_per_scan,
         "achieved_GBps_all_launches": round(bytes_per_scan * scans / (ms * 1e-3) / 1e9, 1),
@@ -161,12 +173,19 @@ def bench_calibration(args):
     }
     if not args.no_cpu_baseline:
         from oracle import calibration as CAL
-        t0 = time.perf_counter()
-        CAL.greedy_givens(xw_host, 128)
-        dt = time.perf_counter() - t0
+        if args.angle_grid:
+            # a whole search would take many minutes: time two steps, scale to the steps taken
+            t0 = time.perf_counter()
+            CAL.greedy_givens_angle(xw_host, 2, args.angle_grid)
+            dt = (time.perf_counter() - t0) / 2 * max(steps, 1)
+            sample = f"the same block, the first 2 steps (NumPy fp64), scaled to {steps} steps"
+        else:
+            t0 = time.perf_counter()
+            CAL.greedy_givens(xw_host, 128)
+            dt = time.perf_counter() - t0
+            sample = "the same block, one search (NumPy fp64)"
         result["cpu_baseline"] = {"value": round(dt * 1e3, 1), "unit": "ms per search", "cores": 1,
-                                  "kind": "oracle", "cpu": host_cpu_model(),
-                                  "sample": "the same block, one search (NumPy fp64)"}
+                                  "kind": "oracle", "cpu": host_cpu_model(), "sample": sample}
     print(json.dumps(result), flush=True)
 
 
@@ -403,6 +422,9 @@ def main():
     ap.add_argument("--calibrate", action="store_true",
                     help="time the greedy block calibration (DuQuant++ page sec. 3.2) on a "
                          "page-scale block instead of the quantization path")
+    ap.add_argument("--angle-grid", type=int, default=0,
+                    help="with --calibrate: choose each candidate's angle from a grid of this many angles "
+                         "(1..1024) instead of pi/4")
     ap.add_argument("--gemm", action="store_true",
                     help="time the consumer instead: the W4A4 MXFP4 product of the headline batch's codes "
                          "with absorbed, quantized weights (8192x14336 by 4096x14336)")

@@ -347,6 +347,24 @@ mxq_status mxq_calib_givens(double *x_worst, int64_t tokens, int32_t max_steps, 
                             double *linf_history, int32_t *steps_done, int32_t *pairs, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/* mxq_calib_givens_angles: the same greedy search, except that every
+ *   candidate j also chooses its angle (the page's step 3d asks for the
+ *   rotation that lowers the largest |value| the most).  The angles form a
+ *   grid of angle_grid = M entries (1 <= M <= 1024, MXQ_ERR_SHAPE otherwise):
+ *   index 0 is pi/4, index k (1 <= k < M) the angle theta with
+ *   tan(theta / 2) = k / M, i.e. c = (M^2 - k^2) / (M^2 + k^2) and
+ *   s = 2 k M / (M^2 + k^2), each a correctly rounded fp64 division.  The
+ *   largest |value| is periodic in theta with period pi/2, so the grid spans
+ *   (0, pi/2) with gaps of at most 2 / M radians.  The pair (j, angle) with
+ *   the smallest largest |value| wins (ties: lowest j, then lowest index).
+ *   M = 1 is mxq_calib_givens bit for bit.  Extra output:
+ *     angles       [max_steps] int32 grid index of each step's angle, or NULL
+ *   Other arguments, outputs, rules and errors as mxq_calib_givens (the
+ *   same workspace size serves both); each step is three kernel launches. */
+mxq_status mxq_calib_givens_angles(double *x_worst, int64_t tokens, int32_t max_steps, int32_t angle_grid,
+                                   double *r_block, double *linf_history, int32_t *steps_done, int32_t *pairs,
+                                   int32_t *angles, void *workspace, size_t workspace_bytes, void *stream);
+
 /* mxq_calib_worst_group_noalloc: mxq_calib_worst_group for callers that
  *   cannot allocate device memory -- code under HIP graph capture, tight
  *   serving loops, harnesses that forbid hipMalloc.  It takes no workspace

@@ -26,7 +26,8 @@ EXPORTS = ("mxq_rotate_quant", "mxq_rotate_quant_ex", "mxq_quant", "mxq_dequant"
            "mxq_status_str", "mxq_plan", "mxq_version", "mxq_calib_workspace_bytes",
            "mxq_calib_worst_group", "mxq_calib_givens", "mxq_absorb_quant", "mxq_gemm_mxfp4",
            "mxq_norm_rotate_quant", "mxq_rotate_quant_block", "mxq_tile_mxfp4", "mxq_rotate_quant_tiled",
-           "mxq_gemm_mxfp4_tiled", "mxq_norm_rotate_quant_tiled", "mxq_calib_worst_group_noalloc")
+           "mxq_gemm_mxfp4_tiled", "mxq_norm_rotate_quant_tiled", "mxq_calib_worst_group_noalloc",
+           "mxq_calib_givens_angles")
 
 _lib = None
 
@@ -64,6 +65,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.mxq_calib_workspace_bytes.restype = sz
     lib.mxq_calib_worst_group.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]
     lib.mxq_calib_givens.argtypes = [vp, i64, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.mxq_calib_givens_angles.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.mxq_calib_worst_group_noalloc.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
     lib.mxq_absorb_quant.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
     lib.mxq_gemm_mxfp4.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i32, i64, vp]
@@ -79,7 +81,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
               "mxq_version", "mxq_calib_worst_group", "mxq_calib_givens", "mxq_absorb_quant",
               "mxq_gemm_mxfp4", "mxq_norm_rotate_quant", "mxq_rotate_quant_block", "mxq_tile_mxfp4",
               "mxq_rotate_quant_tiled", "mxq_gemm_mxfp4_tiled", "mxq_norm_rotate_quant_tiled",
-              "mxq_calib_worst_group_noalloc"):
+              "mxq_calib_worst_group_noalloc", "mxq_calib_givens_angles"):
         getattr(lib, f).restype = ctypes.c_int32
     if path is None:
         _lib = lib
@@ -419,6 +421,30 @@ def calib_givens(x_worst: torch.Tensor, max_steps: int = 128, *, stream=None):
     if st != 0:
         raise MXQError("mxq_calib_givens", st)
     return r, hist, done, pairs
+
+
+def calib_givens_angles(x_worst: torch.Tensor, max_steps: int = 128, angle_grid: int = 64, *, stream=None):
+    """:func:`calib_givens` with a per-candidate angle from a grid of
+    ``angle_grid`` angles (index 0 = pi/4, index k: tan(theta / 2) = k / M).
+    Returns (R, history, steps_done, pairs, angles [max_steps] int32), all on
+    the device; entries past steps_done are unspecified."""
+    lib = load()
+    if x_worst.dtype != torch.float64 or x_worst.dim() != 2 or x_worst.shape[1] != 32 \
+            or not x_worst.is_contiguous() or not x_worst.is_cuda:
+        raise ValueError("x_worst must be a contiguous fp64 [tokens, 32] device tensor")
+    dev = x_worst.device
+    r = torch.empty((32, 32), dtype=torch.float64, device=dev)
+    hist = torch.empty((max_steps + 1,), dtype=torch.float64, device=dev)
+    done = torch.empty((), dtype=torch.int32, device=dev)
+    pairs = torch.empty((max(max_steps, 1), 2), dtype=torch.int32, device=dev)
+    angles = torch.empty((max(max_steps, 1),), dtype=torch.int32, device=dev)
+    ws, n = _workspace(0, dev)
+    st = lib.mxq_calib_givens_angles(_ptr(x_worst), x_worst.shape[0], max_steps, angle_grid, _ptr(r), _ptr(hist),
+                                     _ptr(done), _ptr(pairs), _ptr(angles), _aligned256(ws), n,
+                                     _stream(x_worst, stream))
+    if st != 0:
+        raise MXQError("mxq_calib_givens_angles", st)
+    return r, hist, done, pairs, angles
 
 
 # ---- fragment-tiled operands (records of 16 rows x 128 positions in the

@@ -11,11 +11,18 @@
 // sum below is a separately rounded fp64 operation (no contraction), in a
 // fixed order, so the result is reproducible bit for bit.
 //
-// Readings where the page is silent: the rotation angle is pi/4, so a step
-// maps (x_d, x_j) to (c x_d - s x_j, s x_d + c x_j) with c = s = sqrt(1/2);
-// ties go to the lowest column / candidate / group index; a step is taken
-// while the best candidate does not raise the norm, and the search stops when
-// every candidate would raise it or X_worst is zero.
+// Readings where the page is silent: a Givens rotation by theta maps
+// (x_d, x_j) to (c x_d - s x_j, s x_d + c x_j), c = cos theta, s = sin theta.
+// The angle is pi/4 for every candidate (mxq_calib_givens), or each candidate
+// also picks the best angle of a fixed grid (mxq_calib_givens_angles): pi/4,
+// then the angles with tan(theta / 2) = k / M, k = 1 .. M - 1, whose
+// c = (M^2 - k^2) / (M^2 + k^2) and s = 2 k M / (M^2 + k^2) are correctly
+// rounded divisions of exact integers (the half-angle substitution), so no
+// trigonometric function enters.  The norm has period pi/2 in theta, so the
+// grid spans (0, pi/2).  Ties go to the lowest column / candidate / grid
+// angle / group index; a step is taken while the best candidate does not
+// raise the norm, and the search stops when every candidate would raise it
+// or X_worst is zero.
 //
 // Work layout.  X_worst is [T][32] fp64 (256 bytes per token).  In the scan
 // kernel lane l of a wave holds column l % 32 of token 2 p + l / 32, so one
@@ -24,7 +31,11 @@
 // for the current d accumulate, per candidate j, the maxima of both rotated
 // columns) followed by a one-block decide launch.  Because the maxima of the
 // two rotated columns are exactly the new column maxima of the chosen
-// candidate, one pass over X_worst per step suffices.
+// candidate, one pass over X_worst per step suffices.  With an angle grid a
+// step is three launches: apply the previous step's rotation, scan every
+// (candidate, angle) pair (blockIdx.y picks a chunk of kAngChunk angles; the
+// per-block maxima meet in an array by atomic max, which is order-free), and
+// decide.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,14 +59,18 @@ constexpr int kUnroll = 8;           // token pairs per scan iteration
 constexpr int kSlices = 32;          // decide kernel: threads per candidate
 constexpr double kC = 0x1.6a09e667f3bcdp-1;  // sqrt(1/2), correctly rounded
 constexpr double kS = 0x1.6a09e667f3bcdp-1;
+constexpr int kMaxAngles = 1024;     // largest angle grid
+constexpr int kAngChunk = 8;         // angles per block of the angle scan
+constexpr int kAngUnroll = 4;        // token pairs per angle-scan iteration
 
 struct State {
     int32_t d;           // dimension holding the current maximum
     int32_t pd, pj;      // rotation accepted but not yet applied to X_worst (-1: none)
     int32_t steps_done;
     int32_t stopped;
-    int32_t pad;
+    int32_t pa;          // grid index of the pending rotation's angle
     double linf;
+    double pc, ps;       // cos and sin of the pending rotation
     double colmax[kW];
 };
 
@@ -186,7 +201,10 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(double* xw, int64_t toke
         pd = st->pd;
         pj = st->pj;
         d = st->d;
+        if (MODE == kModeApply && pd < 0) return;
     }
+    const double pc = MODE != kModeInit ? st->pc : 0.0;
+    const double ps = MODE != kModeInit ? st->ps : 0.0;
     const bool eval = MODE == kModeStep && !st->stopped;
     double m1 = 0.0, m2 = 0.0;
     const int64_t pairs = (tokens + 1) / 2;
@@ -207,8 +225,8 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(double* xw, int64_t toke
             if (pd >= 0) {
                 const double xd = shfl_d(v[u], pd + kW * half);
                 const double xj = shfl_d(v[u], pj + kW * half);
-                if (k == pd) v[u] = kC * xd - kS * xj;
-                if (k == pj) v[u] = kS * xd + kC * xj;
+                if (k == pd) v[u] = pc * xd - ps * xj;
+                if (k == pj) v[u] = ps * xd + pc * xj;
                 if (row_ok && (k == pd || k == pj)) xw[t * kW + k] = v[u];
             }
             if (MODE == kModeInit) {
@@ -295,6 +313,9 @@ __global__ __launch_bounds__(kW * kSlices) void decide_kernel(State* st, const d
             st->d = dd;
             st->pd = -1;
             st->pj = -1;
+            st->pa = 0;
+            st->pc = kC;
+            st->ps = kS;
             st->steps_done = 0;
             st->stopped = m == 0.0;
             history[0] = m;
@@ -363,6 +384,227 @@ __global__ __launch_bounds__(kW * kSlices) void decide_kernel(State* st, const d
     }
 }
 
+// ---- greedy search with a per-candidate angle -------------------------------
+
+// (c, s) of the angle grid, index 0 = pi/4, index k = tan(theta / 2) = k / M.
+// Integers below 2^21 and their products are exact in fp64; each quotient is
+// one correctly rounded division.
+__global__ void angle_table_kernel(double* table, int grid) {
+    const int k = static_cast<int>(blockIdx.x * blockDim.x + threadIdx.x);
+    if (k >= grid) return;
+    double c = kC, s = kS;
+    if (k > 0) {
+        const double m = static_cast<double>(grid), kk = static_cast<double>(k);
+        const double den = m * m + kk * kk;
+        c = (m * m - kk * kk) / den;
+        s = (2.0 * kk * m) / den;
+    }
+    table[2 * k] = c;
+    table[2 * k + 1] = s;
+}
+
+// For the current d and the grid angles a0 .. a0 + kAngChunk - 1 (a0 =
+// blockIdx.y * kAngChunk), the maxima over this block's tokens of
+// |c x_d - s x_j| and |s x_d + c x_j| for every j != d, merged into
+// acc[j][a][2] (bit patterns of non-negative doubles, which order like the
+// values) by atomic max.  Lane layout as scan_kernel: lane l holds column
+// l % 32 of token 2 p + l / 32.
+__global__ __launch_bounds__(kThreads) void scan_angles_kernel(const double* xw, int64_t tokens, const State* st,
+                                                              const double* table, int nang, uint64_t* acc) {
+    __shared__ double red[kWavesPerBlock][2][kAngChunk][kW];
+    if (st->stopped) return;  // uniform for the grid
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int k = lane & (kW - 1);
+    const int half = lane >> 5;
+    const int d = st->d;
+    const int a0 = static_cast<int>(blockIdx.y) * kAngChunk;
+    double cc[kAngChunk], ss[kAngChunk], m1[kAngChunk], m2[kAngChunk];
+#pragma unroll
+    for (int a = 0; a < kAngChunk; ++a) {
+        const int idx = a0 + a < nang ? a0 + a : nang - 1;  // past the grid: repeats, not merged
+        cc[a] = table[2 * idx];
+        ss[a] = table[2 * idx + 1];
+        m1[a] = 0.0;
+        m2[a] = 0.0;
+    }
+    const int64_t pairs = (tokens + 1) / 2;
+    const int64_t wstep = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+    for (int64_t p0 = (static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wave) * kAngUnroll; p0 < pairs;
+         p0 += wstep * kAngUnroll) {
+        double v[kAngUnroll];
+#pragma unroll
+        for (int u = 0; u < kAngUnroll; ++u) {
+            const int64_t t = 2 * (p0 + u) + half;
+            v[u] = t < tokens ? xw[t * kW + k] : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < kAngUnroll; ++u) {
+            const int64_t t = 2 * (p0 + u) + half;
+            const double xd = shfl_d(v[u], d + kW * half);
+            if (t < tokens && k != d) {
+#pragma unroll
+                for (int a = 0; a < kAngChunk; ++a) {
+                    const double a1 = fabs(cc[a] * xd - ss[a] * v[u]);
+                    const double a2 = fabs(ss[a] * xd + cc[a] * v[u]);
+                    m1[a] = a1 > m1[a] ? a1 : m1[a];
+                    m2[a] = a2 > m2[a] ? a2 : m2[a];
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int a = 0; a < kAngChunk; ++a) {
+        const double o1 = shfl_d(m1[a], lane ^ 32);
+        const double o2 = shfl_d(m2[a], lane ^ 32);
+        m1[a] = o1 > m1[a] ? o1 : m1[a];
+        m2[a] = o2 > m2[a] ? o2 : m2[a];
+        if (half == 0) {
+            red[wave][0][a][k] = m1[a];
+            red[wave][1][a][k] = m2[a];
+        }
+    }
+    __syncthreads();
+    static_assert(kAngChunk * kW == kThreads, "one thread per (angle, column) of the chunk");
+    const int j = threadIdx.x & (kW - 1);
+    const int a = threadIdx.x / kW;
+    if (j == d || a0 + a >= nang) return;
+    double b1 = red[0][0][a][j], b2 = red[0][1][a][j];
+    for (int w = 1; w < kWavesPerBlock; ++w) {
+        b1 = red[w][0][a][j] > b1 ? red[w][0][a][j] : b1;
+        b2 = red[w][1][a][j] > b2 ? red[w][1][a][j] : b2;
+    }
+    uint64_t* dst = acc + (static_cast<int64_t>(j) * nang + a0 + a) * 2;
+    atomicMax(reinterpret_cast<unsigned long long*>(dst), static_cast<unsigned long long>(__builtin_bit_cast(uint64_t, b1)));
+    atomicMax(reinterpret_cast<unsigned long long*>(dst + 1),
+              static_cast<unsigned long long>(__builtin_bit_cast(uint64_t, b2)));
+}
+
+// One block of 32 x 32 threads.  Thread (slice, j) reads (and clears, for the
+// next step) the merged maxima of candidate j at angles slice, slice + 32, ...
+// and keeps its best (smallest norm, then earliest angle); slice 0 reduces
+// the slices per candidate, thread 0 the candidates (smallest norm, then
+// lowest j), takes or refuses the step, and writes the scalar state; slice 0
+// then updates R.
+__global__ __launch_bounds__(kW * kSlices) void decide_angles_kernel(State* st, uint64_t* acc, const double* table,
+                                                                    int nang, double* r, double* history,
+                                                                    int32_t* pairs_out, int32_t* angles_out,
+                                                                    int32_t* steps_done) {
+    __shared__ double cm[kW];
+    __shared__ double bn[kSlices][kW], b1[kSlices][kW], b2[kSlices][kW];
+    __shared__ int ba[kSlices][kW];
+    __shared__ int acc_d, acc_j;
+    __shared__ double acc_c, acc_s;
+    if (st->stopped) return;  // uniform
+    const int j = threadIdx.x & (kW - 1);
+    const int slice = threadIdx.x / kW;
+    const int d = st->d;
+    if (slice == 0) cm[j] = st->colmax[j];
+    __syncthreads();
+    double rest = 0.0;
+    for (int k2 = 0; k2 < kW; ++k2)
+        if (k2 != d && k2 != j && cm[k2] > rest) rest = cm[k2];
+    double best = 0.0, bm1 = 0.0, bm2 = 0.0;
+    int besta = -1;
+#pragma unroll 1
+    for (int a = slice; a < nang; a += kSlices) {
+        uint64_t* p = acc + (static_cast<int64_t>(j) * nang + a) * 2;
+        const double m1 = __builtin_bit_cast(double, p[0]);
+        const double m2 = __builtin_bit_cast(double, p[1]);
+        p[0] = 0;
+        p[1] = 0;
+        double norm = m1 > m2 ? m1 : m2;
+        norm = rest > norm ? rest : norm;
+        if (besta < 0 || norm < best) {
+            best = norm;
+            besta = a;
+            bm1 = m1;
+            bm2 = m2;
+        }
+    }
+    bn[slice][j] = best;
+    ba[slice][j] = j == d ? -1 : besta;
+    b1[slice][j] = bm1;
+    b2[slice][j] = bm2;
+    __syncthreads();
+    if (slice == 0) {  // best over the slices of candidate j: smallest norm, then earliest angle
+#pragma unroll 1
+        for (int sl = 1; sl < kSlices; ++sl) {
+            const int a = ba[sl][j];
+            if (a < 0) continue;
+            if (ba[0][j] < 0 || bn[sl][j] < bn[0][j] || (bn[sl][j] == bn[0][j] && a < ba[0][j])) {
+                bn[0][j] = bn[sl][j];
+                ba[0][j] = a;
+                b1[0][j] = b1[sl][j];
+                b2[0][j] = b2[sl][j];
+            }
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        acc_j = -1;
+        const double linf = st->linf;
+        double bnorm = 0.0;
+        int bj = -1;
+        if (linf > 0.0) {
+            for (int c = 0; c < kW; ++c) {
+                if (c == d || ba[0][c] < 0) continue;
+                if (bj < 0 || bn[0][c] < bnorm) {
+                    bnorm = bn[0][c];
+                    bj = c;
+                }
+            }
+        }
+        if (bj < 0 || bnorm > linf) {  // zero block, or every candidate raises the norm
+            st->stopped = 1;
+            st->pd = -1;
+            st->pj = -1;
+        } else {
+            const int a = ba[0][bj];
+            cm[d] = b1[0][bj];
+            cm[bj] = b2[0][bj];
+            double m = 0.0;
+            int dd = 0;
+            for (int c = 0; c < kW; ++c)
+                if (cm[c] > m) {
+                    m = cm[c];
+                    dd = c;
+                }
+            const int s = st->steps_done;
+            history[s + 1] = m;
+            if (pairs_out) {
+                pairs_out[2 * s] = d;
+                pairs_out[2 * s + 1] = bj;
+            }
+            if (angles_out) angles_out[s] = a;
+            st->linf = m;
+            st->pd = d;
+            st->pj = bj;
+            st->pa = a;
+            st->pc = table[2 * a];
+            st->ps = table[2 * a + 1];
+            st->d = dd;
+            st->steps_done = s + 1;
+            *steps_done = s + 1;
+            acc_d = d;
+            acc_j = bj;
+            acc_c = table[2 * a];
+            acc_s = table[2 * a + 1];
+        }
+    }
+    __syncthreads();
+    if (slice != 0) return;
+    st->colmax[j] = cm[j];
+    if (acc_j >= 0) {
+        // R <- R G: columns d and j of row `j` (thread j owns row j)
+        const int dd = acc_d, c = acc_j;
+        const double cs = acc_c, sn = acc_s;
+        const double rd = r[j * kW + dd], rc = r[j * kW + c];
+        r[j * kW + dd] = cs * rd - sn * rc;
+        r[j * kW + c] = sn * rd + cs * rc;
+    }
+}
+
 }  // namespace calib
 
 // ---- host entry points ------------------------------------------------------
@@ -383,10 +625,20 @@ static int64_t scan_blocks(int64_t tokens) {
 
 static size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
+// Workspace layout: State | per-block partial maxima | angle table | merged
+// (candidate, angle) maxima | per-group maxima of the worst-group scan.
+static size_t ws_partials() { return align256(sizeof(State)); }
+static size_t ws_table() {
+    return ws_partials() + align256(static_cast<size_t>(kCalibMaxBlocks) * calib::kW * 2 * sizeof(double));
+}
+static size_t ws_acc() { return ws_table() + align256(static_cast<size_t>(calib::kMaxAngles) * 2 * sizeof(double)); }
+static size_t ws_gmax() {
+    return ws_acc() + align256(static_cast<size_t>(calib::kW) * calib::kMaxAngles * 2 * sizeof(uint64_t));
+}
+
 static size_t calib_workspace_bytes(int64_t channels) {
     const int64_t gpr = channels > 0 ? channels / calib::kW : 0;
-    return align256(sizeof(State)) + align256(static_cast<size_t>(kCalibMaxBlocks) * calib::kW * 2 * sizeof(double)) +
-           align256(static_cast<size_t>(gpr) * sizeof(uint64_t));
+    return ws_gmax() + align256(static_cast<size_t>(gpr) * sizeof(uint64_t));
 }
 
 template <int XT, bool LAM>
@@ -421,8 +673,7 @@ static mxq_status calib_worst_group(const void* x, int32_t x_dtype, int64_t toke
         return MXQ_ERR_ALIGN;
     const int64_t gpr = channels / calib::kW;
     char* ws = static_cast<char*>(workspace);
-    uint64_t* gmax = reinterpret_cast<uint64_t*>(
-        ws + align256(sizeof(State)) + align256(static_cast<size_t>(kCalibMaxBlocks) * calib::kW * 2 * sizeof(double)));
+    uint64_t* gmax = reinterpret_cast<uint64_t*>(ws + ws_gmax());
     hipStream_t st = static_cast<hipStream_t>(stream);
     switch (x_dtype * 2 + (lambda ? 1 : 0)) {
         case MXQ_BF16 * 2: launch_worst<MXQ_BF16, false>(x, stride, lambda, tokens, gpr, gmax, group, linf, x_worst, st); break;
@@ -446,7 +697,7 @@ static mxq_status calib_givens(double* x_worst, int64_t tokens, int32_t max_step
         return MXQ_ERR_ALIGN;
     char* ws = static_cast<char*>(workspace);
     State* state = reinterpret_cast<State*>(ws);
-    double* partials = reinterpret_cast<double*>(ws + align256(sizeof(State)));
+    double* partials = reinterpret_cast<double*>(ws + ws_partials());
     const int64_t nb = scan_blocks(tokens);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const dim3 grid(static_cast<unsigned>(nb)), block(calib::kThreads);
@@ -459,6 +710,49 @@ static mxq_status calib_givens(double* x_worst, int64_t tokens, int32_t max_step
                            partials);
         hipLaunchKernelGGL(calib::decide_kernel<calib::kModeStep>, dim3(1), dblock, 0, st, state,
                            partials, static_cast<int>(nb), r, history, pairs, steps_done);
+    }
+    hipLaunchKernelGGL(calib::scan_kernel<calib::kModeApply>, grid, block, 0, st, x_worst, tokens, state, partials);
+    return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+}
+
+static mxq_status calib_givens_angles(double* x_worst, int64_t tokens, int32_t max_steps, int32_t angle_grid,
+                                      double* r, double* history, int32_t* steps_done, int32_t* pairs,
+                                      int32_t* angles, void* workspace, size_t workspace_bytes, void* stream) {
+    if (tokens <= 0 || tokens > (int64_t(1) << 40) || max_steps < 0 || max_steps > 1000000 || angle_grid < 1 ||
+        angle_grid > calib::kMaxAngles)
+        return MXQ_ERR_SHAPE;
+    if (!x_worst || !r || !history || !steps_done || !workspace) return MXQ_ERR_NULL;
+    if (workspace_bytes < calib_workspace_bytes(0) || (reinterpret_cast<uintptr_t>(workspace) & 255) ||
+        (reinterpret_cast<uintptr_t>(x_worst) & 7) || (reinterpret_cast<uintptr_t>(r) & 7) ||
+        (reinterpret_cast<uintptr_t>(history) & 7) || (reinterpret_cast<uintptr_t>(steps_done) & 3) ||
+        (reinterpret_cast<uintptr_t>(pairs) & 3) || (reinterpret_cast<uintptr_t>(angles) & 3))
+        return MXQ_ERR_ALIGN;
+    char* ws = static_cast<char*>(workspace);
+    State* state = reinterpret_cast<State*>(ws);
+    double* partials = reinterpret_cast<double*>(ws + ws_partials());
+    double* table = reinterpret_cast<double*>(ws + ws_table());
+    uint64_t* acc = reinterpret_cast<uint64_t*>(ws + ws_acc());
+    const int64_t nb = scan_blocks(tokens);
+    const int chunks = (angle_grid + calib::kAngChunk - 1) / calib::kAngChunk;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 grid(static_cast<unsigned>(nb)), block(calib::kThreads);
+    const dim3 agrid(static_cast<unsigned>(nb), static_cast<unsigned>(chunks));
+    const dim3 dblock(calib::kW * calib::kSlices);
+    const int64_t nacc = static_cast<int64_t>(calib::kW) * angle_grid * 2;
+    hipLaunchKernelGGL(calib::fill_u64, dim3(static_cast<unsigned>((nacc + 255) / 256)), dim3(256), 0, st, acc, nacc,
+                       uint64_t(0));
+    hipLaunchKernelGGL(calib::angle_table_kernel, dim3(static_cast<unsigned>((angle_grid + 255) / 256)), dim3(256), 0,
+                       st, table, angle_grid);
+    hipLaunchKernelGGL(calib::scan_kernel<calib::kModeInit>, grid, block, 0, st, x_worst, tokens, state, partials);
+    hipLaunchKernelGGL(calib::decide_kernel<calib::kModeInit>, dim3(1), dblock, 0, st, state, partials,
+                       static_cast<int>(nb), r, history, pairs, steps_done);
+    for (int32_t s = 0; s < max_steps; ++s) {
+        hipLaunchKernelGGL(calib::scan_kernel<calib::kModeApply>, grid, block, 0, st, x_worst, tokens, state,
+                           partials);
+        hipLaunchKernelGGL(calib::scan_angles_kernel, agrid, block, 0, st, x_worst, tokens, state, table,
+                           angle_grid, acc);
+        hipLaunchKernelGGL(calib::decide_angles_kernel, dim3(1), dblock, 0, st, state, acc, table, angle_grid, r,
+                           history, pairs, angles, steps_done);
     }
     hipLaunchKernelGGL(calib::scan_kernel<calib::kModeApply>, grid, block, 0, st, x_worst, tokens, state, partials);
     return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
@@ -543,6 +837,13 @@ mxq_status mxq_calib_worst_group(const void* x, int32_t x_dtype, int64_t tokens,
                                  double* linf, void* workspace, size_t workspace_bytes, void* stream) {
     return mxq::calib_worst_group(x, x_dtype, tokens, channels, x_row_stride, lambda, x_worst, group, linf,
                                   workspace, workspace_bytes, stream);
+}
+
+mxq_status mxq_calib_givens_angles(double* x_worst, int64_t tokens, int32_t max_steps, int32_t angle_grid,
+                                   double* r_block, double* linf_history, int32_t* steps_done, int32_t* pairs,
+                                   int32_t* angles, void* workspace, size_t workspace_bytes, void* stream) {
+    return mxq::calib_givens_angles(x_worst, tokens, max_steps, angle_grid, r_block, linf_history, steps_done, pairs,
+                                    angles, workspace, workspace_bytes, stream);
 }
 
 mxq_status mxq_calib_givens(double* x_worst, int64_t tokens, int32_t max_steps, double* r_block,

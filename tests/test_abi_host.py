@@ -138,6 +138,15 @@ def test_calibration_validation(lib):
     assert g(P, 8, 128, P, None, P, None, W16, ws, None) == NULL
     assert g(P, 8, 128, P, P, P, None, W16, 8, None) == ALIGN
     assert g(ctypes.c_void_p(0x10004), 8, 128, P, P, P, None, W16, ws, None) == ALIGN
+    a = lib.mxq_calib_givens_angles
+    assert a(P, 8, 128, 0, P, P, P, None, None, W16, ws, None) == SHAPE
+    assert a(P, 8, 128, 1025, P, P, P, None, None, W16, ws, None) == SHAPE
+    assert a(P, 0, 128, 64, P, P, P, None, None, W16, ws, None) == SHAPE
+    assert a(P, 8, -1, 64, P, P, P, None, None, W16, ws, None) == SHAPE
+    assert a(None, 8, 128, 64, P, P, P, None, None, W16, ws, None) == NULL
+    assert a(P, 8, 128, 64, P, P, None, None, None, W16, ws, None) == NULL
+    assert a(P, 8, 128, 64, P, P, P, None, None, W16, 8, None) == ALIGN
+    assert a(P, 8, 128, 64, P, P, P, None, ctypes.c_void_p(0x10002), W16, ws, None) == ALIGN
 
 
 def test_calibration_noalloc_validation(lib):

@@ -129,11 +129,14 @@ def test_block_embeddings_same_bits(dev):
         assert torch.equal(c1, c2) and torch.equal(s1, s2), B
 
 
-def _greedy_block(wl, B):
+def _greedy_block(wl, B, grid=0):
     from oracle import calibration as CAL
     s, n = wl.meta["calib_start"], wl.meta["calib_len"]
     _, _, xw = CAL.worst_group(wl.x[s:s + n], wl.lam, block=B)
-    R, _, _, pairs = CAL.greedy_givens(xw, 128)
+    if grid:
+        R, _, _, pairs = CAL.greedy_givens_angle(xw, 128, grid)
+    else:
+        R, _, _, pairs = CAL.greedy_givens(xw, 128)
     return W.bf16_matrix(R), len(pairs)
 
 
@@ -154,8 +157,9 @@ def test_error_study_block_sizes(dev, orc, cfg):
     report = {}
     for B in (16, 32, 64, 128):
         greedy, steps = _greedy_block(wl, B)
+        greedy8, steps8 = _greedy_block(wl, B, 8)
         kinds = {"hadamard": W.bf16_matrix(W.random_hadamard(np.random.default_rng(2005 + B), B)),
-                 f"greedy({steps})": greedy}
+                 f"greedy({steps})": greedy, f"greedy_grid8({steps8})": greedy8}
         for name, r in kinds.items():
             y = torch.empty(wl.x.shape, dtype=torch.float32, device=dev)
             codes, scales = mxq.rotate_quant_block(xd, r.to(dev), lam_d, y_rot=y)

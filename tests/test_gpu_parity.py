@@ -325,13 +325,17 @@ def test_dequant_round_trip(dev, orc):
 
 # ---- error study (reported, not asserted) --------------------------------------
 
-def _greedy_block(wl):
+def _greedy_block(wl, grid=0):
     """The page's greedy outlier-aware block (sec. 3.2), from the workload's
-    own calibration slice, computed by the fp64 oracle on the CPU."""
+    own calibration slice, computed by the fp64 oracle on the CPU: angle
+    pi/4 (grid 0) or each candidate's best angle of a grid of that size."""
     from oracle import calibration as CAL
     s, n = wl.meta["calib_start"], wl.meta["calib_len"]
     _, _, xw = CAL.worst_group(wl.x[s:s + n], wl.lam)
-    R, _, hist, pairs = CAL.greedy_givens(xw, 128)
+    if grid:
+        R, _, hist, pairs = CAL.greedy_givens_angle(xw, 128, grid)
+    else:
+        R, _, hist, pairs = CAL.greedy_givens(xw, 128)
     return W.bf16_matrix(R), len(pairs)
 
 
@@ -346,10 +350,14 @@ def test_error_study(dev, orc, cfg):
     wl = W.make_config(cfg)
     xd, lam_d, _ = _to_dev(wl.x, wl.lam, wl.r_hat, dev)
     greedy, steps = _greedy_block(wl)
+    greedy8, steps8 = _greedy_block(wl, 8)
+    greedy64, steps64 = _greedy_block(wl, 64)
     blocks = {"identity": W.identity_r(),
               "random_hadamard": W.bf16_matrix(W.random_hadamard(np.random.default_rng(2005))),
               "householder": wl.r_hat,
-              "greedy_givens": greedy}
+              "greedy_givens": greedy,
+              "greedy_angle_grid8": greedy8,
+              "greedy_angle_grid64": greedy64}
     rows = np.sort(np.random.default_rng(2006).choice(wl.tokens, 256, replace=False))
     xs = wl.x[torch.from_numpy(rows)].contiguous()
     report = {}
@@ -373,7 +381,8 @@ def test_error_study(dev, orc, cfg):
         assert np.isfinite(mean) and 0 < mean < 1
         del y, dq, codes, scales, eps
         torch.cuda.empty_cache()
-    print(f"  error study, config {cfg} (greedy steps {steps}): {report}", flush=True)
+    print(f"  error study, config {cfg} (greedy steps: pi/4 {steps}, grid 8 {steps8}, grid 64 {steps64}): "
+          f"{report}", flush=True)
 
 
 def test_graph_capture_replays(dev):
