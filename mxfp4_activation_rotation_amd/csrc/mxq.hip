@@ -71,6 +71,22 @@
 #ifndef MXQ_FMA_MIX
 #define MXQ_FMA_MIX 1
 #endif
+// Short smoothed batches (each wave would take at most two batches of rows):
+// the waves of a block work on one super-tile column and share its factors,
+// loaded and inverted once per block and kept in LDS, and each wave keeps
+// one row in flight at 16 waves per CU.  In a launch of one round the
+// factor loads and each wave's serial work sit on the critical path; in long
+// launches the factors are paid once per wave and the row-major wave order
+// streams better.
+#ifndef MXQ_SHARE_LAM
+#define MXQ_SHARE_LAM 1
+#endif
+#ifndef MXQ_WAVES_PER_CU_SHARE
+#define MXQ_WAVES_PER_CU_SHARE 16
+#endif
+#ifndef MXQ_BATCH_SHARE
+#define MXQ_BATCH_SHARE 1
+#endif
 #ifndef MXQ_LAM_TERMS
 #define MXQ_LAM_TERMS 2
 #endif
@@ -125,10 +141,19 @@ template <int XT, int MODE, int LAM>
 constexpr int kBatchOf = (MODE == 1 && LAM != kLamNone) ? MXQ_BATCH_LAM
                          : kSplit<XT, MODE, LAM>         ? MXQ_BATCH_SPLIT
                                                          : MXQ_BATCH;  // rows in flight per wave
+// Block-shared factors: smoothed row-layout instances launched for short
+// batches.
+template <int LAM, bool TILED, bool SHARE>
+constexpr bool kShareLamOf = SHARE && MXQ_SHARE_LAM && LAM != kLamNone && !TILED;
+
 template <int XT, int MODE, int LAM>
 constexpr int kWavesPerCuOf = (MODE == 1 && LAM != kLamNone) ? MXQ_WAVES_PER_CU_LAM
                               : kSplit<XT, MODE, LAM>         ? MXQ_WAVES_PER_CU_SPLIT
                                                               : MXQ_WAVES_PER_CU;
+template <int XT, int MODE, int LAM, bool TILED, bool SHARE>
+constexpr int kBatchFor = TILED ? 1 : kShareLamOf<LAM, TILED, SHARE> ? MXQ_BATCH_SHARE : kBatchOf<XT, MODE, LAM>;
+template <int XT, int MODE, int LAM, bool TILED, bool SHARE>
+constexpr int kWavesPerCuFor = kShareLamOf<LAM, TILED, SHARE> ? MXQ_WAVES_PER_CU_SHARE : kWavesPerCuOf<XT, MODE, LAM>;
 
 enum : int { kBF16 = MXQ_BF16, kFP16 = MXQ_FP16, kFP32 = MXQ_FP32 };
 enum : int { kQuant = 0, kRotate = 1 };
@@ -255,18 +280,24 @@ __device__ __forceinline__ void rotate8(u32x4_t xq, const float* il, bf16x8_t A0
 // register count above it (that pass may spill instead; the main loop does
 // not).  The test-only y output instances, and the tiled ones (whose LDS
 // stage allows one 8-wave block per CU), aim at 2 waves per SIMD.
-template <int XT, int MODE, int LAM, bool YOUT, bool TILED = false>
+template <int XT, int MODE, int LAM, bool YOUT, bool TILED = false, bool SHARE = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
-                          amdgpu_waves_per_eu((YOUT || TILED) ? 2 : kWavesPerCuOf<XT, MODE, LAM> / 4))) void quant_kernel(Args a) {
+                          amdgpu_waves_per_eu((YOUT || TILED) ? 2 : kWavesPerCuFor<XT, MODE, LAM, TILED, SHARE> / 4))) void quant_kernel(Args a) {
     constexpr int kN = (XT == kFP32) ? 2 : 1;  // 16-byte loads per lane per sub-tile
     constexpr uint32_t esz = (XT == kFP32) ? 4 : 2;
-    constexpr int kBatch = TILED ? 1 : kBatchOf<XT, MODE, LAM>;
+    constexpr int kBatch = kBatchFor<XT, MODE, LAM, TILED, SHARE>;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    constexpr bool kShareLam = kShareLamOf<LAM, TILED, SHARE>;
+    // Wave -> (super-tile column, first row).  With shared factors a block
+    // holds 4 consecutive row offsets of one column (the plan's row step is a
+    // multiple of 4 and every wave of the grid exists); otherwise consecutive
+    // waves take consecutive columns.
     const int w = static_cast<int>(blockIdx.x) * kWavesPerBlock + wave;
-    if (w >= a.waves) return;
-    const int tc = w % a.tcols;
-    const int64_t r0 = static_cast<int64_t>(w / a.tcols) * (TILED ? a.unit : 1);
+    if (!kShareLam && w >= a.waves) return;
+    const int tc = kShareLam ? static_cast<int>(blockIdx.x) % a.tcols : w % a.tcols;
+    const int64_t r0 = kShareLam ? static_cast<int64_t>(static_cast<int>(blockIdx.x) / a.tcols) * kWavesPerBlock + wave
+                                 : static_cast<int64_t>(w / a.tcols) * (TILED ? a.unit : 1);
     const int64_t rs = a.row_step;
     const int64_t T = a.tokens;
     const int j = lane & 15;
@@ -322,7 +353,39 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
     // channels this lane feeds in each sub-tile.  Lanes of groups past the
     // row end get 0.
     float il[kSub][8];
-    if constexpr (LAM != kLamNone) {
+    if constexpr (kShareLam) {
+        // Each thread of the block inverts kPer consecutive channels of the
+        // column into LDS; each lane then reads its 8 channels per sub-tile.
+        // A group's 8 slots of 16 bytes are padded to 9, so the 16 groups a
+        // read instruction touches start on distinct bank quads.
+        constexpr int kPer = kTileGroups * kGroup / kBlockThreads;
+        static_assert(kPer % 4 == 0 && kPer * kBlockThreads == kTileGroups * kGroup, "whole 16-byte loads");
+        __shared__ u32x4_t lam_s[kTileGroups * 9];
+        const auto lrsrc = row_rsrc(a.lambda, gpr * kGroup * 4);
+#pragma unroll
+        for (int h = 0; h < kPer / 4; ++h) {
+            const uint32_t e = kPer / 4 * threadIdx.x + h;  // 16-byte slot in the column
+            const u32x4_t l = __builtin_amdgcn_raw_buffer_load_b128(lrsrc, (static_cast<uint32_t>(p0) * kGroup + 4 * e) * 4,
+                                                                    0, 0);
+            u32x4_t inv;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                inv[t] = LAM == kLamMul ? l[t] : as_u32(__builtin_amdgcn_rcpf(as_f32(l[t])));
+            lam_s[e + (e >> 3)] = inv;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < kSub; ++s) {
+            const int idx = (16 * s + j) * 9 + 2 * q;
+            const u32x4_t v0 = lam_s[idx], v1 = lam_s[idx + 1];
+            const bool valid = p0 + 16 * s + j < a.gpr;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                il[s][t] = valid ? as_f32(v0[t]) : 0.0f;
+                il[s][4 + t] = valid ? as_f32(v1[t]) : 0.0f;
+            }
+        }
+    } else if constexpr (LAM != kLamNone) {
         const auto lrsrc = row_rsrc(a.lambda, gpr * kGroup * 4);
 #pragma unroll
         for (int s = 0; s < kSub; ++s) {
@@ -700,13 +763,13 @@ static bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintp
 static size_t dtype_size(int32_t dt) { return dt == MXQ_FP32 ? 4 : 2; }
 
 // Resident waves per CU the kernel instance allows (registers), queried once.
-template <int XT, int MODE, int LAM, bool YOUT, bool TILED>
+template <int XT, int MODE, int LAM, bool YOUT, bool TILED, bool SHARE = false>
 static int occupancy_waves_per_cu() {
     static std::atomic<int> cached{0};
     int v = cached.load(std::memory_order_relaxed);
     if (v > 0) return v;
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, quant_kernel<XT, MODE, LAM, YOUT, TILED>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, quant_kernel<XT, MODE, LAM, YOUT, TILED, SHARE>,
                                                      kBlockThreads, 0) != hipSuccess ||
         blocks <= 0)
         blocks = 1;
@@ -732,6 +795,27 @@ static mxq_status launch(Args a, int64_t tokens, int64_t channels, hipStream_t s
     }
     if (!make_plan(a.unit == 16 ? (tokens + 15) / 16 : tokens, channels, cus, per_cu, &pl)) return MXQ_ERR_SHAPE;
     a.tcols = pl.tcols;
+    if constexpr (kShareLamOf<LAM, TILED, true>) {
+        // A short batch (at most two batches of rows per wave under the
+        // row-major plan) takes the block-shared-factor instance, planned
+        // at its own occupancy.  Whole blocks per column: the row step
+        // rounds up to a multiple of the block's waves (waves whose first
+        // row is past the end do nothing but share the block's factor load).
+        if ((tokens + pl.row_step - 1) / pl.row_step <= 2 * kBatchOf<XT, MODE, LAM>) {
+            const int occ_s = occupancy_waves_per_cu<XT, MODE, LAM, YOUT, TILED, true>();
+            constexpr int want_s = kWavesPerCuFor<XT, MODE, LAM, TILED, true>;
+            Plan ps;
+            if (!make_plan(tokens, channels, cus, occ_s < want_s ? occ_s : want_s, &ps)) return MXQ_ERR_SHAPE;
+            const int64_t rs =
+                (static_cast<int64_t>(ps.row_step) + kWavesPerBlock - 1) / kWavesPerBlock * kWavesPerBlock;
+            if (rs * ps.tcols > kMaxI32) return MXQ_ERR_SHAPE;
+            a.row_step = static_cast<int32_t>(rs);
+            a.waves = static_cast<int32_t>(rs * ps.tcols);
+            hipLaunchKernelGGL((quant_kernel<XT, MODE, LAM, YOUT, TILED, true>), dim3(a.waves / kWavesPerBlock),
+                               dim3(kBlockThreads), 0, st, a);
+            return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+        }
+    }
     a.row_step = pl.row_step;
     a.waves = pl.waves;
     hipLaunchKernelGGL((quant_kernel<XT, MODE, LAM, YOUT, TILED>), dim3(pl.blocks), dim3(kBlockThreads), 0, st, a);

@@ -290,6 +290,26 @@ def test_determinism(dev):
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("cfg", [2, 5])
+@pytest.mark.parametrize("want_y", [False, True])
+def test_same_rows_same_bits_at_any_batch(dev, cfg, want_y):
+    """A row's codes, scales and rotated values do not depend on the batch
+    around it.  Short smoothed batches launch the block-shared-factor
+    instance (each block works on one super-tile column), long ones the
+    row-major instance; the first rows of a long batch, quantized alone in
+    short batches of several sizes, give the same bits."""
+    wl = W.make_config(cfg)
+    # long enough for 8 rows per wave (the row-major instance)
+    x = wl.x[:4096].contiguous() if cfg == 5 else torch.cat([wl.x] * 4).contiguous()
+    full = run_fused(x, wl.lam, wl.r_hat, dev, want_y)
+    for n in (1, 16, 300, 512):
+        part = run_fused(x[:n].contiguous(), wl.lam, wl.r_hat, dev, want_y)
+        for got, ref in zip(part, full):
+            if got is None:
+                continue
+            assert np.array_equal(np.asarray(got).view(np.uint8), np.asarray(ref)[:n].view(np.uint8)), (cfg, n)
+
+
 # ---- dequant: bit-exact -------------------------------------------------------------
 
 def test_dequant_every_code_and_scale(dev, orc):
