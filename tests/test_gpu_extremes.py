@@ -105,6 +105,27 @@ def test_identity_block_every_pattern(dev, orc, dtype, shuffle):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_signed_permutation_long_batch(dev, orc, dtype):
+    """Every pattern in bit order (groups of like magnitude) repeated to
+    about 9000 rows (each wave of the row-major smoothed instance takes five
+    batches of rows; the tests above, at 250 rows, run the short-batch
+    instance), lambda = 2^120 (every group far below 2^-64, so every row goes
+    through the pass that redoes rows), a signed permutation block: bit for
+    bit."""
+    x = torch.cat([every_pattern(dtype)] * 36).contiguous()
+    C = x.shape[1]
+    lam = np.full(C, np.ldexp(1.0, 120), np.float32)
+    r = signed_permutation(15)
+    codes, scales, y = run_fused(x, lam, r, dev)
+    c_ref, s_ref, y_ref = orc.rotate_quant(x, lam, r, want_y=True)
+    assert np.array_equal(scales, s_ref), int((scales != s_ref).sum())
+    assert np.array_equal(codes, c_ref), int((codes != c_ref).sum())
+    check_rotated_values(y, y_ref, smoothed_group_norms(x, lam))
+    assert (scales < 61).sum() > 0
+    print(f"  {dtype} long batch: tiny groups {int((scales < 61).sum())}", flush=True)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("lam_exp", [None, 60, 120, 126, -126, "mixed"])
 def test_signed_permutation_every_pattern(dev, orc, dtype, lam_exp):
     """A signed permutation block and power-of-two lambda make every product
@@ -157,12 +178,15 @@ def test_large_lambda_general_block(dev, orc, dtype, lam_exp):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-def test_mixed_magnitudes_in_one_batch(dev, orc, dtype):
+@pytest.mark.parametrize("T", [300, 3000])
+def test_mixed_magnitudes_in_one_batch(dev, orc, dtype, T):
     """Rows of ordinary size, rows scaled into the subnormal range, and rows
     with single tiny groups, so the pass that redoes rows meets rows with
-    both kinds of groups; with lambda of every size in [2^-60, 2^120]."""
-    rng = np.random.default_rng(8100 + (dtype == torch.float16))
-    T, C = 300, 4096 + 1024
+    both kinds of groups; with lambda of every size in [2^-60, 2^120].
+    300 rows launch the short-batch instance (block-shared factors), 3000
+    rows (five batches of rows per wave) the row-major one."""
+    rng = np.random.default_rng(8100 + (dtype == torch.float16) + 2 * (T > 300))
+    C = 4096 + 1024
     x = rng.standard_normal((T, C))
     lam = np.ldexp(1.0, rng.integers(-60, 121, C)).astype(np.float32) * rng.uniform(1, 2, C).astype(np.float32)
     if dtype == torch.bfloat16:
