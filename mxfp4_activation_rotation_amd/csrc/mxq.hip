@@ -71,13 +71,14 @@
 #ifndef MXQ_FMA_MIX
 #define MXQ_FMA_MIX 1
 #endif
-// Short smoothed batches (each wave would take at most two batches of rows):
-// the waves of a block work on one super-tile column and share its factors,
-// loaded and inverted once per block and kept in LDS, and each wave keeps
-// one row in flight at 16 waves per CU.  In a launch of one round the
-// factor loads and each wave's serial work sit on the critical path; in long
-// launches the factors are paid once per wave and the row-major wave order
-// streams better.
+// Short smoothed batches (each wave of the row-major plan would take at most
+// eight batches of rows): the waves of a block work on one super-tile column
+// and share its factors, loaded and inverted once per block and kept in LDS,
+// and each wave keeps one row in flight at 16 waves per CU (the row-major
+// instance fits one 8-wave block per CU).  In a launch of a round or a few
+// the factor loads and each wave's serial work sit on the critical path; in
+// long launches the factors are paid once per wave and the row-major wave
+// order streams better.
 #ifndef MXQ_SHARE_LAM
 #define MXQ_SHARE_LAM 1
 #endif
@@ -796,12 +797,12 @@ static mxq_status launch(Args a, int64_t tokens, int64_t channels, hipStream_t s
     if (!make_plan(a.unit == 16 ? (tokens + 15) / 16 : tokens, channels, cus, per_cu, &pl)) return MXQ_ERR_SHAPE;
     a.tcols = pl.tcols;
     if constexpr (kShareLamOf<LAM, TILED, true>) {
-        // A short batch (at most two batches of rows per wave under the
+        // A short batch (at most eight batches of rows per wave under the
         // row-major plan) takes the block-shared-factor instance, planned
         // at its own occupancy.  Whole blocks per column: the row step
         // rounds up to a multiple of the block's waves (waves whose first
         // row is past the end do nothing but share the block's factor load).
-        if ((tokens + pl.row_step - 1) / pl.row_step <= 2 * kBatchOf<XT, MODE, LAM>) {
+        if ((tokens + pl.row_step - 1) / pl.row_step <= 8 * kBatchOf<XT, MODE, LAM>) {
             const int occ_s = occupancy_waves_per_cu<XT, MODE, LAM, YOUT, TILED, true>();
             constexpr int want_s = kWavesPerCuFor<XT, MODE, LAM, TILED, true>;
             Plan ps;

@@ -107,12 +107,12 @@ def test_identity_block_every_pattern(dev, orc, dtype, shuffle):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
 def test_signed_permutation_long_batch(dev, orc, dtype):
     """Every pattern in bit order (groups of like magnitude) repeated to
-    about 9000 rows (each wave of the row-major smoothed instance takes five
+    about 35000 rows (each wave of the row-major smoothed instance takes 18
     batches of rows; the tests above, at 250 rows, run the short-batch
     instance), lambda = 2^120 (every group far below 2^-64, so every row goes
     through the pass that redoes rows), a signed permutation block: bit for
     bit."""
-    x = torch.cat([every_pattern(dtype)] * 36).contiguous()
+    x = torch.cat([every_pattern(dtype)] * 140).contiguous()
     C = x.shape[1]
     lam = np.full(C, np.ldexp(1.0, 120), np.float32)
     r = signed_permutation(15)
@@ -178,13 +178,13 @@ def test_large_lambda_general_block(dev, orc, dtype, lam_exp):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("T", [300, 3000])
+@pytest.mark.parametrize("T", [300, 12000])
 def test_mixed_magnitudes_in_one_batch(dev, orc, dtype, T):
     """Rows of ordinary size, rows scaled into the subnormal range, and rows
     with single tiny groups, so the pass that redoes rows meets rows with
     both kinds of groups; with lambda of every size in [2^-60, 2^120].
-    300 rows launch the short-batch instance (block-shared factors), 3000
-    rows (five batches of rows per wave) the row-major one."""
+    300 rows launch the short-batch instance (block-shared factors), 12000
+    rows (18 batches of rows per wave) the row-major one."""
     rng = np.random.default_rng(8100 + (dtype == torch.float16) + 2 * (T > 300))
     C = 4096 + 1024
     x = rng.standard_normal((T, C))

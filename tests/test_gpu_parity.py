@@ -299,8 +299,8 @@ def test_same_rows_same_bits_at_any_batch(dev, cfg, want_y):
     row-major instance; the first rows of a long batch, quantized alone in
     short batches of several sizes, give the same bits."""
     wl = W.make_config(cfg)
-    # long enough for 8 rows per wave (the row-major instance)
-    x = wl.x[:4096].contiguous() if cfg == 5 else torch.cat([wl.x] * 4).contiguous()
+    # long enough for 32 rows per wave (the row-major instance)
+    x = wl.x[:16384].contiguous() if cfg == 5 else torch.cat([wl.x] * 16).contiguous()
     full = run_fused(x, wl.lam, wl.r_hat, dev, want_y)
     for n in (1, 16, 300, 512):
         part = run_fused(x[:n].contiguous(), wl.lam, wl.r_hat, dev, want_y)
