@@ -273,3 +273,41 @@ def test_consumer_full_size_sampled(dev, orc):
     worst = check_product(got, ref, s_abs, wl.channels, "full size")
     print(f"  full-size sampled worst |err| / sum|products| = {worst:.3g}", flush=True)
     assert not torch.isnan(y).any().item()
+
+
+@pytest.mark.parametrize("cfg,smooth", [(3, False), (5, True), (5, False)])
+def test_consumer_error_by_block(dev, orc, cfg, smooth):
+    """The layer output the rotation exists for (DuQuant++ page sec. 3.3:
+    X W = (X Lambda^-1 R)(R^T Lambda W)): 2048 rows of the workload through a
+    layer of 1024 outputs, X and the absorbed W both MXFP4 (W4A4), for each
+    block kind of the error studies, with the workload's smoothing or none.
+    Reported, not asserted beyond sanity (the page prints no values): the
+    relative Frobenius error against the exact X W in fp64, of the W4A4
+    product and of the product with only X quantized (the absorbed weights
+    exact, from the oracle)."""
+    from oracle import calibration as CAL
+    wl = W.make_config(cfg)
+    lam = wl.lam if smooth else None
+    rows = np.sort(np.random.default_rng(2100 + cfg).choice(wl.tokens, 2048, replace=False))
+    x = wl.x[torch.from_numpy(rows)].contiguous()
+    w = W.linear_weights(1024, wl.channels, seed=2200 + cfg, dtype=wl.x.dtype)
+    exact = x.to(torch.float64).numpy() @ w.to(torch.float64).numpy().T
+    s, n = wl.meta["calib_start"], wl.meta["calib_len"]
+    _, _, xw = CAL.worst_group(wl.x[s:s + n], lam)
+    blocks = {"identity": W.identity_r(),
+              "random_hadamard": W.bf16_matrix(W.random_hadamard(np.random.default_rng(2005))),
+              "householder": wl.r_hat,
+              "greedy_pi4": W.bf16_matrix(CAL.greedy_givens(xw, 128)[0]),
+              "greedy_grid8": W.bf16_matrix(CAL.greedy_givens_angle(xw, 128, 8)[0])}
+    report = {}
+    for name, r in blocks.items():
+        ac, asc, _, _, y = _pipeline(x, lam, r, w, dev)
+        y = y.cpu().numpy().astype(np.float64)
+        assert np.isfinite(y).all()
+        da = orc.dequant(ac.cpu().numpy(), asc.cpu().numpy())
+        ya = da @ O.absorb_weights(w, lam, r).T
+        e4 = float(np.linalg.norm(y - exact) / np.linalg.norm(exact))
+        ea = float(np.linalg.norm(ya - exact) / np.linalg.norm(exact))
+        report[name] = (round(e4, 4), round(ea, 4))
+        assert e4 < 1.5 and ea < 1.5, name
+    print(f"  layer-output error (W4A4, A4 only), config {cfg}, smoothing {smooth}: {report}", flush=True)
