@@ -405,6 +405,33 @@ def test_error_study(dev, orc, cfg):
           f"{report}", flush=True)
 
 
+def test_concurrent_streams(dev):
+    """The library keeps no per-call state: calls on two streams at once
+    (default priority), each rotating through its own inputs and outputs,
+    give the bytes of the same calls made one after another."""
+    wl2, wl5 = W.make_config(2), W.make_config(5)
+    x2, lam2, r2 = _to_dev(wl2.x, wl2.lam, wl2.r_hat, dev)
+    x5, lam5, r5 = _to_dev(wl5.x[:4096].contiguous(), wl5.lam, wl5.r_hat, dev)
+    ref2 = mxq.rotate_quant(x2, r2, lam2)
+    ref5 = mxq.rotate_quant(x5, r5, lam5)
+    refq = mxq.quant(x2)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for it in range(20):
+        with torch.cuda.stream(streams[0]):
+            outs.append(("2", mxq.rotate_quant(x2, r2, lam2)))
+            outs.append(("q", mxq.quant(x2)))
+        with torch.cuda.stream(streams[1]):
+            outs.append(("5", mxq.rotate_quant(x5, r5, lam5)))
+    torch.cuda.synchronize()
+    for tag, (c, sc) in outs:
+        rc, rs = {"2": ref2, "5": ref5, "q": refq}[tag]
+        assert torch.equal(c, rc) and torch.equal(sc, rs), tag
+
+
 def test_graph_capture_replays(dev):
     """The entry points launch no allocation, memset or synchronization, so a
     HIP graph of several calls replays correctly: every replay (with eager
