@@ -146,25 +146,54 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kWave * BW),
     __shared__ __attribute__((aligned(16))) uint8_t sstg[kStaged ? 2 : 1][kStaged ? kGroups * BW : 1];
     static_assert(!kStaged || BW == 8 || BW == 16, "a staged tile is a record row or half of one");
 
-    // Factor setup: consecutive threads take consecutive channels (coalesced
-    // loads of gamma, beta, lambda) and scatter the two factors to the lane
-    // order above.  Channels past the row end keep factor 0.
     const int C = a.channels;
-    float* fmf = reinterpret_cast<float*>(fm);
-    float* fbf = reinterpret_cast<float*>(fb);
-    for (int c = threadIdx.x; c < NT * kTileGroups * kGroup; c += kBlockThreads) {
-        float mv = 0.0f, bv = 0.0f;
-        if (c < C) {
-            const float lam = a.lambda ? a.lambda[c] : 1.0f;
-            mv = a.gamma[c] / lam;
-            bv = a.beta ? a.beta[c] / lam : 0.0f;
+    // Factor setup: thread t takes the runs of 4 consecutive channels
+    // 4 t, 4 (t + threads), ... with 16-byte loads of gamma, beta and lambda
+    // (coalesced).  The 4 channels of a run fill one factor unit (one group,
+    // one lane, one half), so a run is one 16-byte LDS store.  A batch of
+    // runs issues all its loads before the first division waits on them: one
+    // memory latency per batch, not one per channel.  Runs past the row end
+    // (C is a multiple of 32, so a run is in or out whole) keep factor 0.
+    {
+        constexpr int kRuns = NT * kTileGroups * kGroup / 4;
+        constexpr int kPerThread = (kRuns + kBlockThreads - 1) / kBlockThreads;
+        constexpr int kBatch = kPerThread < 4 ? kPerThread : 4;
+        static_assert(kPerThread % kBatch == 0, "whole batches");
+        const uint32_t nbytes = static_cast<uint32_t>(C) * 4;
+        const auto grs = row_rsrc(a.gamma, nbytes);
+        const auto brs = row_rsrc(a.beta, a.beta ? nbytes : 0);
+        const auto lrs = row_rsrc(a.lambda, a.lambda ? nbytes : 0);
+#pragma unroll 1
+        for (int b0 = 0; b0 < kPerThread; b0 += kBatch) {
+            u32x4_t gv[kBatch], bv[kBatch], lv[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                const uint32_t off = (static_cast<uint32_t>(b0 + i) * kBlockThreads + threadIdx.x) * 16;
+                gv[i] = __builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0);
+                bv[i] = __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, 0);
+                lv[i] = __builtin_amdgcn_raw_buffer_load_b128(lrs, off, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                const int u = (b0 + i) * kBlockThreads + static_cast<int>(threadIdx.x);  // run: channels 4u .. 4u + 3
+                if (kRuns % kBlockThreads != 0 && u >= kRuns) continue;
+                f32x4_t mv = {0.0f, 0.0f, 0.0f, 0.0f}, bq = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (4 * u < C) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const float lam = a.lambda ? as_f32(lv[i][t]) : 1.0f;
+                        mv[t] = as_f32(gv[i][t]) / lam;
+                        bq[t] = a.beta ? as_f32(bv[i][t]) / lam : 0.0f;
+                    }
+                }
+                const int p = u >> 3;  // group: 16 ss + j
+                const int k = 4 * (u & 7);  // first channel of the run in its group: 8 q + 4 h
+                const int lane_c = 16 * (k >> 3) + (p & 15);
+                const int unit = ((p >> 4) * 2 + ((k >> 2) & 1)) * kWave + lane_c;
+                fm[unit] = mv;
+                fb[unit] = bq;
+            }
         }
-        const int p = c / kGroup;         // group: 16 ss + j
-        const int k = c % kGroup;         // channel in group: 8 q + 4 h + t
-        const int lane_c = 16 * (k >> 3) + (p & 15);
-        const int unit = ((p >> 4) * 2 + ((k >> 2) & 1)) * kWave + lane_c;
-        fmf[unit * 4 + (k & 3)] = mv;
-        fbf[unit * 4 + (k & 3)] = bv;
     }
     __syncthreads();
 
