@@ -61,7 +61,33 @@ constexpr int kWavesPerSimd = LAM ? (KB == 1 ? 4 : KB == 2 ? 3 : 1) : (KB == 1 ?
 template <int XT, bool LAM>
 constexpr bool kGuardTiny = !(XT == MXQ_FP16 && !LAM);
 
-template <int XT, bool LAM, int KB, bool HALF>
+// Whole-block loads for B = 64 without smoothing.  With one MFMA column per
+// block, a 16-byte-per-lane load of one k-step reads 64 bytes of each of 16
+// blocks: half of 16 different 128-byte lines.  Instead load i (i = 0, 1)
+// of a sub-tile reads 1 KB of whole blocks: lane (q, j) takes block
+// 8 i + j % 8, k-step j / 8, 8-channel chunk q.  K-step k's operand is then
+// load k with its other half-row (lanes 8..15 for k = 0, lanes 0..7 for
+// k = 1) taken from load 1 - k rotated by 8 lanes (DPP row_ror:8 with a
+// per-bank write mask), which puts block j, k-step k, chunk q in lane
+// (q, j) as the MFMA expects.  The smoothed instances do more VALU work per
+// element and gain nothing from it, and for B = 128 the 4-way merge costs
+// what the loads save, so they keep the per-k-step loads.
+template <int KB, bool LAM>
+constexpr bool kWholeBlockLoads = KB == 2 && !LAM;
+
+__device__ __forceinline__ void merge_half_rows(const u32x4_t& l0, const u32x4_t& l1, u32x4_t& k0, u32x4_t& k1) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int a0 = static_cast<int>(l0[d]), a1 = static_cast<int>(l1[d]);
+        k0[d] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(a0, a1, 0x128, 0xf, 0xc, false));
+        k1[d] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(a1, a0, 0x128, 0xf, 0x3, false));
+    }
+}
+
+// The rotated-value output (YOUT) is a template parameter: a runtime branch
+// around its stores would cut each row's unrolled sub-tiles into separate
+// basic blocks that the scheduler cannot interleave.
+template <int XT, bool LAM, int KB, bool HALF, bool YOUT>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
                           amdgpu_waves_per_eu(kWavesPerSimd<LAM, KB>))) void block_quant_kernel(BlockArgs a) {
     constexpr bool kFp16 = XT == MXQ_FP16;
@@ -237,18 +263,41 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
     // recomputed from x' * 2^k, k from the block's largest |x'|; a block with
     // a larger output group keeps its values, whose errors scale with the
     // block's norm.  Returns whether some group of the row had S < 61.
-    auto row_body = [&](int64_t r, auto fix_tag) -> bool {
-        constexpr bool FIX = decltype(fix_tag)::value;
-        const auto rsrc = row_rsrc(xb + r * a.stride * 2, row_bytes);
-        u32x4_t xin[kSubs][KB];
+    // The operands of row r, in the MFMA's layout.  Rows past the end read
+    // through an empty range (zeros, no traffic), so the prefetch below needs
+    // no branch: a conditional load would make the wait before the current
+    // row's first use count the next row's loads too.
+    auto load_row = [&](u32x4_t (&xin)[kSubs][KB], int64_t r, auto nt_tag) {
+        constexpr int aux = decltype(nt_tag)::value ? kAuxNT : 0;
+        const bool in = r < a.tokens;
+        const auto rsrc = row_rsrc(xb + (in ? r : 0) * a.stride * 2, in ? row_bytes : 0u);
+        if constexpr (kWholeBlockLoads<KB, LAM>) {
 #pragma unroll
-        for (int s = 0; s < kSubs; ++s)
-#pragma unroll
-            for (int k = 0; k < KB; ++k) {
-                const uint32_t grp = static_cast<uint32_t>(p0 + KB * (16 * s + j) + k);
-                xin[s][k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (grp * kGroup + 8 * q) * 2, 0,
-                                                                  FIX ? 0 : kAuxNT);
+            for (int s = 0; s < kSubs; ++s) {
+                const uint32_t base = static_cast<uint32_t>(p0) * kGroup * 2 + s * 2048 +
+                                      static_cast<uint32_t>(j & 7) * 128 + static_cast<uint32_t>(j >> 3) * 64 + 16 * q;
+                const u32x4_t l0 = __builtin_amdgcn_raw_buffer_load_b128(rsrc, base, 0, aux);
+                const u32x4_t l1 = __builtin_amdgcn_raw_buffer_load_b128(rsrc, base + 1024, 0, aux);
+                merge_half_rows(l0, l1, xin[s][0], xin[s][1]);
             }
+        } else {
+#pragma unroll
+            for (int s = 0; s < kSubs; ++s)
+#pragma unroll
+                for (int k = 0; k < KB; ++k) {
+                    const uint32_t grp = static_cast<uint32_t>(p0 + KB * (16 * s + j) + k);
+                    xin[s][k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, (grp * kGroup + 8 * q) * 2, 0, aux);
+                }
+        }
+    };
+
+    // One row.  FIX (the pass for rows with tiny groups, below): a block
+    // column whose output groups all have a rotated maximum below 2^-64 is
+    // recomputed from x' * 2^k, k from the block's largest |x'|; a block with
+    // a larger output group keeps its values, whose errors scale with the
+    // block's norm.  Returns whether some group of the row had S < 61.
+    auto row_body = [&](int64_t r, const u32x4_t (&xin)[kSubs][KB], auto fix_tag) -> bool {
+        constexpr bool FIX = decltype(fix_tag)::value;
         uint32_t word[4], sc[4];
         bool redo = false;
 #pragma unroll
@@ -313,7 +362,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
                 }
                 sc[s * KB + g] = sb[g] >> 23;
                 word[s * KB + g] = encode8(v, as_f32(cb[g]));
-                if (a.y) store_y(r, s, g, v, ksh);
+                if constexpr (YOUT) store_y(r, s, g, v, ksh);
             }
         }
         transpose_words(word);
@@ -330,9 +379,29 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
     };
 
     bool tiny_seen = false;
-    for (int r_loop = r0; r_loop < a.tokens; r_loop += a.row_step) {
-        const int64_t r = __builtin_amdgcn_readfirstlane(r_loop);
-        tiny_seen |= row_body(r, std::false_type{});
+    if constexpr (KB == 2) {
+        // Two row buffers alternate: the next row is in flight while the
+        // current one computes.  Measured side by side it helps B = 64 only:
+        // B <= 32 runs more waves per SIMD (up to 7), which hide the latency
+        // already, and at B = 128 the A operands take half the registers.
+        u32x4_t bufA[kSubs][KB], bufB[kSubs][KB];
+        const int64_t rs = a.row_step;
+        load_row(bufA, __builtin_amdgcn_readfirstlane(r0), std::true_type{});
+        for (int r_loop = r0; r_loop < a.tokens; r_loop += 2 * a.row_step) {
+            const int64_t r = __builtin_amdgcn_readfirstlane(r_loop);
+            load_row(bufB, r + rs, std::true_type{});
+            tiny_seen |= row_body(r, bufA, std::false_type{});
+            if (r + rs >= a.tokens) break;
+            load_row(bufA, r + 2 * rs, std::true_type{});
+            tiny_seen |= row_body(r + rs, bufB, std::false_type{});
+        }
+    } else {
+        for (int r_loop = r0; r_loop < a.tokens; r_loop += a.row_step) {
+            const int64_t r = __builtin_amdgcn_readfirstlane(r_loop);
+            u32x4_t xin[kSubs][KB];
+            load_row(xin, r, std::true_type{});
+            tiny_seen |= row_body(r, xin, std::false_type{});
+        }
     }
     // Rows holding a group with S < 61 (rare) are redone; the release fence
     // makes their first stores complete before the second ones.
@@ -340,20 +409,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         for (int r_loop = r0; r_loop < a.tokens; r_loop += a.row_step) {
             const int64_t r = __builtin_amdgcn_readfirstlane(r_loop);
-            row_body(r, std::true_type{});
+            u32x4_t xin[kSubs][KB];
+            load_row(xin, r, std::false_type{});
+            row_body(r, xin, std::true_type{});
         }
     }
 }
 
 bool aligned_to(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
-template <int XT, bool LAM, int KB, bool HALF>
+template <int XT, bool LAM, int KB, bool HALF, bool YOUT>
 int waves_per_cu() {
     static std::atomic<int> cached{0};
     int v = cached.load(std::memory_order_relaxed);
     if (v > 0) return v;
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, block_quant_kernel<XT, LAM, KB, HALF>, kBlockThreads,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, block_quant_kernel<XT, LAM, KB, HALF, YOUT>, kBlockThreads,
                                                      0) != hipSuccess ||
         blocks <= 0)
         blocks = 1;
@@ -362,18 +433,23 @@ int waves_per_cu() {
     return v;
 }
 
-template <int XT, bool LAM, int KB, bool HALF>
-mxq_status launch(BlockArgs a, hipStream_t st) {
+template <int XT, bool LAM, int KB, bool HALF, bool YOUT>
+mxq_status launch_y(BlockArgs a, hipStream_t st) {
     a.tcols = (a.gpr + kTileGroups - 1) / kTileGroups;
-    const int64_t slots = static_cast<int64_t>(device_cu_count()) * waves_per_cu<XT, LAM, KB, HALF>();
+    const int64_t slots = static_cast<int64_t>(device_cu_count()) * waves_per_cu<XT, LAM, KB, HALF, YOUT>();
     int64_t rs = slots / a.tcols;
     if (rs < 1) rs = 1;
     if (rs > a.tokens) rs = a.tokens;
     a.row_step = static_cast<int32_t>(rs);
     const int64_t waves = static_cast<int64_t>(a.tcols) * rs;
     const int blocks = static_cast<int>((waves + kBlockWaves - 1) / kBlockWaves);
-    hipLaunchKernelGGL((block_quant_kernel<XT, LAM, KB, HALF>), dim3(blocks), dim3(kBlockThreads), 0, st, a);
+    hipLaunchKernelGGL((block_quant_kernel<XT, LAM, KB, HALF, YOUT>), dim3(blocks), dim3(kBlockThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+}
+
+template <int XT, bool LAM, int KB, bool HALF>
+mxq_status launch(const BlockArgs& a, hipStream_t st) {
+    return a.y ? launch_y<XT, LAM, KB, HALF, true>(a, st) : launch_y<XT, LAM, KB, HALF, false>(a, st);
 }
 
 template <int XT, bool LAM>
