@@ -443,7 +443,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
             transpose_words(word);
             // the scale of group 16 q + j is the one computed in sub-tile q
             S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
-            if constexpr (MODE == kRotate && kGuardTiny<XT, LAM>) tiny_seen |= S < (kTinyScaleBits >> 23);
+            // (groups past the row end, zeros whose stores are dropped, do not count)
+            if constexpr (MODE == kRotate && kGuardTiny<XT, LAM>)
+                tiny_seen |= S < (kTinyScaleBits >> 23) && static_cast<uint32_t>(p0 + lane) < gpr;
     };
     auto store_row = [&](int64_t rr, const uint32_t (&word)[kSub], uint32_t S) {
             if constexpr (TILED) {

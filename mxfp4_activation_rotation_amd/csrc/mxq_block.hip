@@ -367,15 +367,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
         }
         transpose_words(word);
         const uint32_t S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
+        const uint32_t grp = static_cast<uint32_t>(p0 + KB * (16 * (q / KB) + j) + q % KB);
         if (!FIX || redo) {
-            const uint32_t grp = static_cast<uint32_t>(p0 + KB * (16 * (q / KB) + j) + q % KB);
             const auto crsrc = row_rsrc(a.codes + r * a.gpr * 16, gpr * 16);
             __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{word[0], word[1], word[2], word[3]}, crsrc, grp * 16, 0,
                                                    kAuxNT);
             const auto srsrc = row_rsrc(a.scales + r * a.gpr, gpr);
             __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, grp, 0, 0);
         }
-        return S < (kTinyScaleBits >> 23);
+        // (groups past the row end, zeros whose stores are dropped, do not count)
+        return S < (kTinyScaleBits >> 23) && grp < gpr;
     };
 
     bool tiny_seen = false;

@@ -434,8 +434,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kWave * BW),
                 }
                 transpose_words(word);
                 const uint32_t S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
-                fix_seen |= S < (kTinyScaleBits >> 23);
                 const uint32_t g = static_cast<uint32_t>(kTileGroups * st + lane);
+                // (groups past the row end, zeros whose stores are dropped, do not count)
+                fix_seen |= S < (kTinyScaleBits >> 23) && g < gpr;
                 if constexpr (kStaged) {
                     stg[sb][wave][g] = u32x4_t{word[0], word[1], word[2], word[3]};
                     sstg[sb][g * BW + wave] = static_cast<uint8_t>(S);
