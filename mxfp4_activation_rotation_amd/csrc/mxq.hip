@@ -422,6 +422,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
     // tiny_seen here; such rows are redone after the main loop (below), so
     // the common path carries one compare per row and no extra registers.
     bool tiny_seen = false;
+    constexpr bool kFlagTiny = MODE == kRotate && kGuardTiny<XT, LAM>;
     auto encode_row = [&](const Rows& buf, int u, int64_t rr, uint32_t (&word)[kSub], uint32_t& S) {
             uint32_t sc[kSub];
 #pragma unroll
@@ -443,9 +444,27 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
             transpose_words(word);
             // the scale of group 16 q + j is the one computed in sub-tile q
             S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
-            // (groups past the row end, zeros whose stores are dropped, do not count)
-            if constexpr (MODE == kRotate && kGuardTiny<XT, LAM>)
-                tiny_seen |= S < (kTinyScaleBits >> 23) && static_cast<uint32_t>(p0 + lane) < gpr;
+            // Groups past the row end (zeros whose stores are dropped) do not
+            // count, nor do groups of zeros: their rotated maximum is 0 like
+            // that of a tiny group, but their codes and scale are exact
+            // already.  Telling zeros from tiny values takes the input, so it
+            // is looked at only in a row where some group fell below the bound.
+            if constexpr (kFlagTiny) {
+                bool t = S < (kTinyScaleBits >> 23) && static_cast<uint32_t>(p0 + lane) < gpr;
+                if (any_lane(t)) {
+                    // bit j of nzm[s]: group 16 s + j holds a nonzero input bit pattern
+                    uint32_t nzm[kSub];
+#pragma unroll
+                    for (int s = 0; s < kSub; ++s) {
+                        const u32x4_t& w = buf[u][s][0];
+                        const uint64_t b = __builtin_amdgcn_ballot_w64((w[0] | w[1] | w[2] | w[3]) != 0u);
+                        const uint64_t f = b | (b >> 32);
+                        nzm[s] = static_cast<uint32_t>(f | (f >> 16)) & 0xffffu;
+                    }
+                    const uint32_t nz = q == 0 ? nzm[0] : q == 1 ? nzm[1] : q == 2 ? nzm[2] : nzm[3];
+                    tiny_seen |= t && ((nz >> j) & 1u);
+                }
+            }
     };
     auto store_row = [&](int64_t rr, const uint32_t (&word)[kSub], uint32_t S) {
             if constexpr (TILED) {

@@ -1,4 +1,4 @@
-"""Ragged channel counts keep the common path.
+"""Ragged channel counts, and rows of zeros, keep the common path.
 
 A row whose group count is not a multiple of a super-tile (64 groups) leaves
 padding groups in the last super-tile: they load zeros, and their stores are
@@ -10,6 +10,12 @@ to 9 times slower than aligned ones of the same size (8192 x 5120: 56 us
 against 22 us for 8192 x 6144).  The outputs are covered by the parity tests;
 these check the time, against an aligned shape with at least as many bytes,
 with margins far above the run-to-run spread (a few per cent).
+
+Groups of zeros have rotated maximum 0 too, but their codes and scale are
+exact already; the quantize kernel tells them from tiny groups by their input
+(only in rows where some group fell below the bound).  Before, a batch with
+every other row zero ran 3.6 times slower (8192 x 14336: 175 us against 48 us)
+and 6.4 times with smoothing at 2048 x 4096.
 """
 import numpy as np
 import pytest
@@ -128,3 +134,24 @@ def test_ragged_rows_still_redo_tiny_groups(dev):
     assert np.array_equal(c1[:, -16:], c2[:, -16:])
     assert np.array_equal(s1[:, -1].astype(np.int64), s2[:, -1].astype(np.int64) - 100)
     assert (s1[:, -1] < 61).all()
+
+
+@pytest.mark.parametrize("smoothed", [False, True])
+def test_rotate_quant_rows_of_zeros(dev, smoothed):
+    r = _orthogonal(32, 9, dev)
+    x, lam, _ = _inputs(2048, 4096, 10, dev)
+    xz = x.clone()
+    xz[1::2] = 0
+    codes, scales = _outputs(2048, 4096, dev)
+    t = _time_us(lambda: mxq.rotate_quant(x, r, lam if smoothed else None, codes=codes, scales=scales))
+    tz = _time_us(lambda: mxq.rotate_quant(xz, r, lam if smoothed else None, codes=codes, scales=scales))
+    print(f"  rotate_quant smoothed={smoothed} 2048x4096: {t:.1f} us, every other row zero {tz:.1f} us")
+    assert tz < 1.5 * t
+    # the zero rows come out as zero codes with the scale byte of a zero maximum,
+    # and the other rows as they do without the zero rows
+    c1, s1 = mxq.rotate_quant(x, r, lam if smoothed else None)
+    c2, s2 = mxq.rotate_quant(xz, r, lam if smoothed else None)
+    torch.cuda.synchronize()
+    c1, s1, c2, s2 = (a.cpu().numpy() for a in (c1, s1, c2, s2))
+    assert np.array_equal(c1[0::2], c2[0::2]) and np.array_equal(s1[0::2], s2[0::2])
+    assert not c2[1::2].any() and not s2[1::2].any()
