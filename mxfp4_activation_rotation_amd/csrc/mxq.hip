@@ -38,6 +38,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "../../include/mxq.h"
 #include "mxq_device.h"
@@ -281,7 +282,9 @@ __device__ __forceinline__ void rotate8(u32x4_t xq, const float* il, bf16x8_t A0
 // register count above it (that pass may spill instead; the main loop does
 // not).  The test-only y output instances, and the tiled ones (whose LDS
 // stage allows one 8-wave block per CU), aim at 2 waves per SIMD.
-template <int XT, int MODE, int LAM, bool YOUT, bool TILED = false, bool SHARE = false>
+// TU: rows per unit of the tiled output (1, 8 or 16; 0 for the row layout),
+// a template parameter so that each unit's loop gets its own registers.
+template <int XT, int MODE, int LAM, bool YOUT, bool TILED = false, bool SHARE = false, int TU = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
                           amdgpu_waves_per_eu((YOUT || TILED) ? 2 : kWavesPerCuFor<XT, MODE, LAM, TILED, SHARE> / 4))) void quant_kernel(Args a) {
     constexpr int kN = (XT == kFP32) ? 2 : 1;  // 16-byte loads per lane per sub-tile
@@ -298,7 +301,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
     if (!kShareLam && w >= a.waves) return;
     const int tc = kShareLam ? static_cast<int>(blockIdx.x) % a.tcols : w % a.tcols;
     const int64_t r0 = kShareLam ? static_cast<int64_t>(static_cast<int>(blockIdx.x) / a.tcols) * kWavesPerBlock + wave
-                                 : static_cast<int64_t>(w / a.tcols) * (TILED ? a.unit : 1);
+                                 : static_cast<int64_t>(w / a.tcols) * (TILED ? TU : 1);
     const int64_t rs = a.row_step;
     const int64_t T = a.tokens;
     const int j = lane & 15;
@@ -507,36 +510,37 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
     // current one is computed.
     if constexpr (TILED) {
         static_assert(kBatch == 1, "one row per step");
-        if (a.unit == 16) {
-            // Units of 16 consecutive rows (one record row), units
-            // r0 / 16 + k * rs.  The unit's codes go to a per-wave LDS tile
-            // ([row][group], padded) and leave it record by record: lane l
-            // carries slot l (row l % 16, group 4 rec + l / 16), so each
-            // store instruction writes one whole 1 KB record.  Scattered
-            // 16-byte stores (one line per lane) cost half the bandwidth,
-            // and records written as two 8-row halves at different times
-            // (every 256-byte group chunk in two pieces) cost 5 %.  The 16
-            // scale bytes of a lane's group are contiguous in its record and
-            // go out as one 16-byte store per unit.  Both stores are
-            // non-temporal (written once, read by the next kernel).  The
-            // tile's row pitch is 65 slots of 16 bytes: the 16 lanes of a
-            // ds_read_b128 pass read 16 rows of one group, which an odd pitch
-            // spreads over all 16 bank quads of the 64 four-byte banks.
-            __shared__ u32x4_t stg[kWavesPerBlock][16][kTileGroups + 1];
-            const uint32_t nrec = gpr / 4;
-            const uint32_t rec0 = static_cast<uint32_t>(p0) / 4;
-            const uint32_t grp = static_cast<uint32_t>(p0 + lane);
-            const uint32_t soff = (grp >> 2) * 64 + (grp & 3) * 16;
-            const int st_row = lane & 15;
-            const int st_grp = lane >> 4;
-            for (int64_t unit = r0; unit < T; unit += 16 * rs) {
+        // Units of U consecutive rows (U = 16: one record row; U = 8: half of
+        // one), units r0 / U + k * rs.  The unit's codes go to a per-wave LDS
+        // tile ([row][group], padded) and leave it record by record.  U = 16:
+        // lane l carries slot l (row l % 16, group 4 rec + l / 16), so each
+        // store instruction writes one whole 1 KB record.  U = 8: lane l
+        // carries row l % 8 of group (l / 8) % 4 of record 2 m + l / 32, so
+        // every 8 lanes write one 128-byte line (rows 8 h .. + 7 of a 256-byte
+        // group chunk).  Scattered 16-byte stores (one line per lane) cost
+        // half the bandwidth; records written as two 8-row halves at
+        // different times cost 5 % when 16-row units fill the grid, but give
+        // twice the units when they do not.  The U scale bytes of a lane's
+        // group are contiguous in its record and go out as one store per
+        // unit.  Both stores are non-temporal (written once, read by the
+        // next kernel).  The tile's row pitch is 65 slots of 16 bytes: the 16
+        // lanes of a ds_read_b128 pass read 16 rows of one group (U = 16),
+        // which an odd pitch spreads over all 16 bank quads.
+        __shared__ u32x4_t stg[kWavesPerBlock][16][kTileGroups + 1];
+        const uint32_t nrec = gpr / 4;
+        const uint32_t rec0 = static_cast<uint32_t>(p0) / 4;
+        const uint32_t grp = static_cast<uint32_t>(p0 + lane);
+        const uint32_t soff = (grp >> 2) * 64 + (grp & 3) * 16;
+        auto run_units = [&](auto u_tag) {
+            constexpr int U = decltype(u_tag)::value;
+            for (int64_t unit = r0; unit < T; unit += U * rs) {
                 uint32_t spk[4] = {0u, 0u, 0u, 0u};
                 const auto crsrc = row_rsrc(a.codes + (unit >> 4) * nrec * 1024, nrec * 1024);
 #pragma unroll
-                for (int k = 0; k < 16; ++k) {
+                for (int k = 0; k < U; ++k) {
                     const int64_t r = unit + k;
                     if (r < T) {
-                        const int64_t rn = k < 15 ? r + 1 : unit + 16 * rs;
+                        const int64_t rn = k < U - 1 ? r + 1 : unit + U * rs;
                         Rows& cur = (k & 1) ? bufB : bufA;
                         Rows& nxt = (k & 1) ? bufA : bufB;
                         if (rn < T) load_rows(nxt, rn);
@@ -547,19 +551,48 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
                         spk[k / 4] |= S << (8 * (k % 4));
                     }
                 }
-                // rows past the end (the last unit's padding) are not written
-                const bool row_ok = unit + st_row < T;
-#pragma unroll
-                for (int rec = 0; rec < 16; ++rec) {
-                    const u32x4_t v = stg[wave][st_row][4 * rec + st_grp];
-                    if (row_ok)
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            v, crsrc, (rec0 + static_cast<uint32_t>(rec)) * 1024 + 16 * static_cast<uint32_t>(lane), 0,
-                            kAuxNT);
-                }
                 const auto srsrc = row_rsrc(a.scales + (unit >> 4) * nrec * 64, nrec * 64);
-                __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{spk[0], spk[1], spk[2], spk[3]}, srsrc, soff, 0, kAuxNT);
+                if constexpr (U == 16) {
+                    // rows past the end (the last unit's padding) are not written
+                    const int st_row = lane & 15;
+                    const int st_grp = lane >> 4;
+                    const bool row_ok = unit + st_row < T;
+#pragma unroll
+                    for (int rec = 0; rec < 16; ++rec) {
+                        const u32x4_t v = stg[wave][st_row][4 * rec + st_grp];
+                        if (row_ok)
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                v, crsrc, (rec0 + static_cast<uint32_t>(rec)) * 1024 + 16 * static_cast<uint32_t>(lane),
+                                0, kAuxNT);
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{spk[0], spk[1], spk[2], spk[3]}, srsrc, soff, 0,
+                                                           kAuxNT);
+                } else {
+                    const uint32_t h = static_cast<uint32_t>(unit >> 3) & 1;  // which half of the record row
+                    const int st_row = lane & 7;
+                    const int st_grp = (lane >> 3) & 3;
+                    const int st_rec = lane >> 5;
+                    const bool row_ok = unit + st_row < T;
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        const int rec = 2 * m + st_rec;
+                        const u32x4_t v = stg[wave][st_row][4 * rec + st_grp];
+                        if (row_ok)
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                v, crsrc,
+                                (rec0 + static_cast<uint32_t>(rec)) * 1024 + static_cast<uint32_t>(st_grp) * 256 +
+                                    (8 * h + static_cast<uint32_t>(st_row)) * 16,
+                                0, kAuxNT);
+                    }
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{spk[0], spk[1]}, srsrc, soff + 8 * h, 0, kAuxNT);
+                }
             }
+        };
+        static_assert(!TILED || TU == 1 || TU == 8 || TU == 16, "tiled units of 1, 8 or 16 rows");
+        if constexpr (TU == 16) {
+            run_units(std::integral_constant<int, 16>{});
+        } else if constexpr (TU == 8) {
+            run_units(std::integral_constant<int, 8>{});
         } else {
             for (int64_t r = r0; r < T; r += 2 * rs) {
                 if (r + rs < T) load_rows(bufB, r + rs);
@@ -585,11 +618,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
     // group whose rotated maximum is below 2^-64, the sub-tiles holding such
     // groups are recomputed with x' shifted by 2^k (k per group, from its
     // largest |x'|), and the row's codes and scales are written again (the
-    // other groups' bytes are rewritten unchanged).  The release fence makes
-    // the first stores of these rows complete before the second ones.
+    // other groups' bytes are rewritten unchanged).  The wave first waits for
+    // its own first stores of these rows, so the second ones land after them
+    // (the rows are the wave's own; an agent-scope release fence would also
+    // write back the L2).
     if constexpr (MODE == kRotate && kGuardTiny<XT, LAM>) {
         if (any_lane(tiny_seen)) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             auto fix_row = [&](int64_t rr) {
                 const auto rsrc = row_rsrc(xb + rr * a.stride * esz, row_bytes);
                 uint32_t word[kSub], sc[kSub];
@@ -636,9 +671,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
                     store_row(rr, word, S);
                 }
             };
-            if (TILED && a.unit == 16) {
-                for (int64_t unit = r0; unit < T; unit += 16 * rs)
-                    for (int64_t rr = unit; rr < unit + 16 && rr < T; ++rr) fix_row(rr);
+            if constexpr (TILED && TU > 1) {
+                for (int64_t unit = r0; unit < T; unit += TU * rs)
+                    for (int64_t rr = unit; rr < unit + TU && rr < T; ++rr) fix_row(rr);
             } else {
                 for (int64_t rr = r0; rr < T; rr += rs) fix_row(rr);
             }
@@ -761,6 +796,33 @@ static bool make_plan(int64_t tokens, int64_t channels, int cu_count, int waves_
     return true;
 }
 
+// Rows per unit of the tiled output (16, 8 or 1), from a cost model fitted
+// to timings of each unit forced on smoothed bf16 batches of 256 to 12000
+// rows x 4096, 8192 and 14336 channels: a wave's rows, ceil(units / (slots
+// / columns)) rounds of U rows, times a per-row cost of 1.5 for single rows
+// (each lane's 16-byte store lands in its own record), 1 for 8-row units and
+// 0.95 for 16-row units.  On those 27 shapes the cheapest unit was the
+// fastest or within 7 % of it.
+static int tiled_unit(int64_t tokens, int64_t channels, int64_t slots) {
+    const int64_t tcols = (channels / kGroup + kTileGroups - 1) / kTileGroups;
+    int64_t per_col = slots / (tcols > 0 ? tcols : 1);
+    if (per_col < 1) per_col = 1;
+    static const int kUnits[3] = {16, 8, 1};
+    static const int kCost20[3] = {19, 20, 30};  // per-row cost x 20
+    int best = 1;
+    int64_t best_cost = -1;
+    for (int i = 0; i < 3; ++i) {
+        const int64_t units = (tokens + kUnits[i] - 1) / kUnits[i];
+        const int64_t rounds = (units + per_col - 1) / per_col;
+        const int64_t cost = rounds * kUnits[i] * kCost20[i];
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = kUnits[i];
+        }
+    }
+    return best;
+}
+
 // Shapes the launch plan accepts (no device query).
 static bool shape_ok(int64_t tokens, int64_t channels) {
     Plan pl;
@@ -791,7 +853,8 @@ static int occupancy_waves_per_cu() {
     int v = cached.load(std::memory_order_relaxed);
     if (v > 0) return v;
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, quant_kernel<XT, MODE, LAM, YOUT, TILED, SHARE>,
+    // (the tiled instances share one LDS size and register target)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, quant_kernel<XT, MODE, LAM, YOUT, TILED, SHARE, TILED ? 16 : 0>,
                                                      kBlockThreads, 0) != hipSuccess ||
         blocks <= 0)
         blocks = 1;
@@ -808,14 +871,8 @@ static mxq_status launch(Args a, int64_t tokens, int64_t channels, hipStream_t s
     const int per_cu = occ < want ? occ : want;
     const int cus = device_cu_count();
     a.unit = 1;
-    if (TILED) {
-        // 16-row units when there are enough of them to fill the grid;
-        // short batches (decode) keep one row per unit, for parallelism.
-        const int64_t units = (tokens + 15) / 16;
-        const int64_t tcols = (channels / kGroup + kTileGroups - 1) / kTileGroups;
-        if (units * tcols >= static_cast<int64_t>(cus) * per_cu) a.unit = 16;
-    }
-    if (!make_plan(a.unit == 16 ? (tokens + 15) / 16 : tokens, channels, cus, per_cu, &pl)) return MXQ_ERR_SHAPE;
+    if (TILED) a.unit = tiled_unit(tokens, channels, static_cast<int64_t>(cus) * per_cu);
+    if (!make_plan((tokens + a.unit - 1) / a.unit, channels, cus, per_cu, &pl)) return MXQ_ERR_SHAPE;
     a.tcols = pl.tcols;
     if constexpr (kShareLamOf<LAM, TILED, true>) {
         // A short batch (at most eight batches of rows per wave under the
@@ -840,7 +897,19 @@ static mxq_status launch(Args a, int64_t tokens, int64_t channels, hipStream_t s
     }
     a.row_step = pl.row_step;
     a.waves = pl.waves;
-    hipLaunchKernelGGL((quant_kernel<XT, MODE, LAM, YOUT, TILED>), dim3(pl.blocks), dim3(kBlockThreads), 0, st, a);
+    if constexpr (TILED) {
+        if (a.unit == 16)
+            hipLaunchKernelGGL((quant_kernel<XT, MODE, LAM, YOUT, TILED, false, 16>), dim3(pl.blocks), dim3(kBlockThreads),
+                               0, st, a);
+        else if (a.unit == 8)
+            hipLaunchKernelGGL((quant_kernel<XT, MODE, LAM, YOUT, TILED, false, 8>), dim3(pl.blocks), dim3(kBlockThreads),
+                               0, st, a);
+        else
+            hipLaunchKernelGGL((quant_kernel<XT, MODE, LAM, YOUT, TILED, false, 1>), dim3(pl.blocks), dim3(kBlockThreads),
+                               0, st, a);
+    } else {
+        hipLaunchKernelGGL((quant_kernel<XT, MODE, LAM, YOUT, TILED>), dim3(pl.blocks), dim3(kBlockThreads), 0, st, a);
+    }
     return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
 }
 

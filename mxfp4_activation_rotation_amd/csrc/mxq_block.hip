@@ -404,10 +404,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
             tiny_seen |= row_body(r, xin, std::false_type{});
         }
     }
-    // Rows holding a group with S < 61 (rare) are redone; the release fence
-    // makes their first stores complete before the second ones.
+    // Rows holding a group with S < 61 (rare) are redone; the wave first waits
+    // for its own first stores of these rows, so the second ones land after.
     if (kGuardTiny<XT, LAM> && any_lane(tiny_seen)) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         for (int r_loop = r0; r_loop < a.tokens; r_loop += a.row_step) {
             const int64_t r = __builtin_amdgcn_readfirstlane(r_loop);
             u32x4_t xin[kSubs][KB];

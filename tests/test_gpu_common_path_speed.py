@@ -1,4 +1,5 @@
-"""Ragged channel counts, and rows of zeros, keep the common path.
+"""Ragged channel counts, rows of zeros and the tiled norm output keep the
+common path.
 
 A row whose group count is not a multiple of a super-tile (64 groups) leaves
 padding groups in the last super-tile: they load zeros, and their stores are
@@ -155,3 +156,21 @@ def test_rotate_quant_rows_of_zeros(dev, smoothed):
     c1, s1, c2, s2 = (a.cpu().numpy() for a in (c1, s1, c2, s2))
     assert np.array_equal(c1[0::2], c2[0::2]) and np.array_equal(s1[0::2], s2[0::2])
     assert not c2[1::2].any() and not s2[1::2].any()
+
+
+@pytest.mark.parametrize("T,C,bound", [(8192, 4096, 1.4), (2048, 5120, 1.6)])
+def test_norm_tiled_output_keeps_pace(dev, T, C, bound):
+    """The tiled output of long batches stages record rows in LDS and meets
+    at one block barrier per step; it should cost about what the row layout
+    does.  An agent-scope release fence before the rare pass (an L2
+    write-back by every wave) once made it 3.4-3.6 times slower."""
+    r = _orthogonal(32, 11, dev)
+    x, lam, gamma = _inputs(T, C, 12, dev)
+    codes, scales = _outputs(T, C, dev)
+    tc, ts = mxq.norm_rotate_quant_tiled(x, r, gamma, None, lam, norm="rms", eps=1e-5)
+    t_row = _time_us(lambda: mxq.norm_rotate_quant(x, r, gamma, None, lam, norm="rms", eps=1e-5,
+                                                   codes=codes, scales=scales))
+    t_tiled = _time_us(lambda: mxq.norm_rotate_quant_tiled(x, r, gamma, None, lam, norm="rms", eps=1e-5,
+                                                           tcodes=tc, tscales=ts))
+    print(f"  norm {T}x{C}: row layout {t_row:.1f} us, tiled {t_tiled:.1f} us")
+    assert t_tiled < bound * t_row
