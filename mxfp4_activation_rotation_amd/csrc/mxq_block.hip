@@ -53,8 +53,22 @@ struct BlockArgs {
 // Waves per SIMD each instance reaches without the tiny-block pass; stated
 // to the compiler so that the pass (rare) spills rather than lowering the
 // occupancy of the main loop.
-template <bool LAM, int KB>
-constexpr int kWavesPerSimd = LAM ? (KB == 1 ? 4 : KB == 2 ? 3 : 1) : (KB == 1 ? 7 : KB == 2 ? 4 : 2);
+// B = 64 and 128: the KB x 2 x KB A operands (32 and 128 VGPRs per lane in
+// registers) live in LDS, 8 or 32 KB shared by the block's waves, each read
+// by one conflict-free ds_read_b128 (64 lanes x 16 bytes in lane order) next
+// to its MFMAs.  At B = 128 this frees half the register file: 3 waves per
+// SIMD instead of 2 (1 with smoothing, which now also keeps the next row in
+// flight).  Side by side, bit-identical: bf16 8192 x 14336 B = 128 60.0 ->
+// 56.7-57.1 us, fp16 32768 x 8192 with lambda 280 -> 160 us; B = 64 54.0 ->
+// 53.0 us and 133.9 -> 130.9 us.
+template <int KB>
+constexpr bool kLdsOperands = KB >= 2;
+
+// (fp16 without smoothing at B = 128 keeps 2: its two exact terms of all
+// four k-steps do not fit the main loop in 168 registers)
+template <int XT, bool LAM, int KB>
+constexpr int kWavesPerSimd = LAM ? (KB == 1 ? 4 : 3)
+                                  : (KB == 1 ? 7 : KB == 2 ? 4 : (XT == MXQ_FP16 ? 2 : 3));
 
 // fp16 activations without smoothing never need the tiny-block pass (a
 // nonzero fp16 value is at least 2^-24).
@@ -89,7 +103,7 @@ __device__ __forceinline__ void merge_half_rows(const u32x4_t& l0, const u32x4_t
 // basic blocks that the scheduler cannot interleave.
 template <int XT, bool LAM, int KB, bool HALF, bool YOUT>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
-                          amdgpu_waves_per_eu(kWavesPerSimd<LAM, KB>))) void block_quant_kernel(BlockArgs a) {
+                          amdgpu_waves_per_eu(kWavesPerSimd<XT, LAM, KB>))) void block_quant_kernel(BlockArgs a) {
     constexpr bool kFp16 = XT == MXQ_FP16;
     constexpr int kSubs = 4 / KB;  // sub-tiles per super-tile
     constexpr int kB = HALF ? 16 : 32 * KB;
@@ -97,6 +111,35 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int w = static_cast<int>(blockIdx.x) * kBlockWaves + wave;
+
+    // A operand (g, h, k) of lane ln: element t is
+    // R[32 k + 8 (ln / 16) + t][32 g + 8 (ln % 16 / 4) + 4 h + ln % 4]
+    auto operand = [&](int g, int h, int k, int ln) {
+        bf16x8_t op;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int row = 32 * k + 8 * (ln >> 4) + t;
+            const int col = 32 * g + 8 * ((ln & 15) >> 2) + 4 * h + (ln & 3);
+            uint16_t bits;
+            if constexpr (HALF)
+                bits = (row >> 4) == (col >> 4) ? a.r[(row & 15) * 16 + (col & 15)] : uint16_t(0);
+            else
+                bits = a.r[row * kB + col];
+            op[t] = __builtin_bit_cast(__bf16, bits);
+        }
+        return op;
+    };
+    constexpr bool kLds = kLdsOperands<KB>;
+    __shared__ __attribute__((aligned(16))) bf16x8_t a_lds[kLds ? KB * 2 * KB * kWave : 1];
+    if constexpr (kLds) {
+        // every wave of the block fills its share and meets the barrier
+        // before any wave without work leaves
+        for (int e = static_cast<int>(threadIdx.x); e < KB * 2 * KB * kWave; e += kBlockThreads) {
+            const int op = e / kWave;
+            a_lds[e] = operand(op / (2 * KB), (op / KB) & 1, op % KB, e % kWave);
+        }
+        __syncthreads();
+    }
     if (w >= a.tcols * a.row_step) return;
     const int tc = w % a.tcols;
     const int r0 = w / a.tcols;
@@ -105,25 +148,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
     const uint32_t gpr = static_cast<uint32_t>(a.gpr);
     const int p0 = tc * kTileGroups;
 
-    // A operands: A[gamma][h][kappa][t] = R[32 kappa + 8 q + t][32 gamma + 8 (j / 4) + 4 h + j % 4]
-    bf16x8_t A[KB][2][KB];
+    // A operands in registers (B <= 32), or read from LDS where they are used
+    bf16x8_t A[kLds ? 1 : KB][2][kLds ? 1 : KB];
+    if constexpr (!kLds) {
 #pragma unroll
-    for (int g = 0; g < KB; ++g)
+        for (int g = 0; g < KB; ++g)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int k = 0; k < KB; ++k)
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const int row = 32 * k + 8 * q + t;
-                    const int col = 32 * g + 8 * (j >> 2) + 4 * h + (j & 3);
-                    uint16_t bits;
-                    if constexpr (HALF)
-                        bits = (row >> 4) == (col >> 4) ? a.r[(row & 15) * 16 + (col & 15)] : uint16_t(0);
-                    else
-                        bits = a.r[row * kB + col];
-                    A[g][h][k][t] = __builtin_bit_cast(__bf16, bits);
-                }
+                for (int k = 0; k < KB; ++k) A[g][h][k] = operand(g, h, k, lane);
+    }
+    auto opA = [&](int g, int h, int k) -> bf16x8_t {
+        if constexpr (kLds)
+            return a_lds[((g * 2 + h) * KB + k) * kWave + lane];
+        else
+            return A[g][h][k];
+    };
 
     // 1 / lambda for the lane's 8 channels of every (sub-tile, k-step)
     float il[kSubs][KB][8];
@@ -171,8 +211,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
                 const bf16x8_t b = __builtin_bit_cast(bf16x8_t, xin[s][k]);
 #pragma unroll
                 for (int g = 0; g < KB; ++g) {
-                    d0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0][k], b, d0[g], 0, 0, 0);
-                    d1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1][k], b, d1[g], 0, 0, 0);
+                    d0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(opA(g, 0, k), b, d0[g], 0, 0, 0);
+                    d1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(opA(g, 1, k), b, d1[g], 0, 0, 0);
                 }
             }
         } else {
@@ -215,10 +255,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
                     }
 #pragma unroll
                     for (int g = 0; g < KB; ++g) {
-                        d0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0][k], __builtin_bit_cast(bf16x8_t, hi), d0[g], 0, 0, 0);
-                        d1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1][k], __builtin_bit_cast(bf16x8_t, hi), d1[g], 0, 0, 0);
-                        d0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0][k], __builtin_bit_cast(bf16x8_t, lo), d0[g], 0, 0, 0);
-                        d1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1][k], __builtin_bit_cast(bf16x8_t, lo), d1[g], 0, 0, 0);
+                        d0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(opA(g, 0, k), __builtin_bit_cast(bf16x8_t, hi), d0[g], 0, 0, 0);
+                        d1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(opA(g, 1, k), __builtin_bit_cast(bf16x8_t, hi), d1[g], 0, 0, 0);
+                        d0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(opA(g, 0, k), __builtin_bit_cast(bf16x8_t, lo), d0[g], 0, 0, 0);
+                        d1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(opA(g, 1, k), __builtin_bit_cast(bf16x8_t, lo), d1[g], 0, 0, 0);
                     }
                 }
                 return;
@@ -234,8 +274,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
                     const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bt);
 #pragma unroll
                     for (int g = 0; g < KB; ++g) {
-                        d0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0][k], b, d0[g], 0, 0, 0);
-                        d1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1][k], b, d1[g], 0, 0, 0);
+                        d0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(opA(g, 0, k), b, d0[g], 0, 0, 0);
+                        d1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(opA(g, 1, k), b, d1[g], 0, 0, 0);
                     }
                     if (term + 1 < kT) {
 #pragma unroll
@@ -298,6 +338,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
     // block's norm.  Returns whether some group of the row had S < 61.
     auto row_body = [&](int64_t r, const u32x4_t (&xin)[kSubs][KB], auto fix_tag) -> bool {
         constexpr bool FIX = decltype(fix_tag)::value;
+        // (LDS operands are re-read for every row, not held in registers
+        // across rows: the clobber keeps the compiler from hoisting them)
+        if constexpr (kLds) asm volatile("" ::: "memory");
         uint32_t word[4], sc[4];
         bool redo = false;
 #pragma unroll
@@ -380,11 +423,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
     };
 
     bool tiny_seen = false;
-    if constexpr (KB == 2) {
+    if constexpr (KB == 2 || (KB == 4 && LAM)) {
         // Two row buffers alternate: the next row is in flight while the
-        // current one computes.  Measured side by side it helps B = 64 only:
-        // B <= 32 runs more waves per SIMD (up to 7), which hide the latency
-        // already, and at B = 128 the A operands take half the registers.
+        // current one computes.  Measured side by side it helps B = 64 and
+        // smoothed B = 128 (170 -> 160 us on fp16 32768 x 8192): B <= 32 runs
+        // more waves per SIMD (up to 7), which hide the latency already, and
+        // unsmoothed B = 128 stays level (56.7 against 57.1 us).
         u32x4_t bufA[kSubs][KB], bufB[kSubs][KB];
         const int64_t rs = a.row_step;
         load_row(bufA, __builtin_amdgcn_readfirstlane(r0), std::true_type{});
