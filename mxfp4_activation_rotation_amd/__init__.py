@@ -89,6 +89,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
 
 
 _DT = {torch.bfloat16: MXQ_BF16, torch.float16: MXQ_FP16, torch.float32: MXQ_FP32}
+_HALF_TYPES = (torch.bfloat16, torch.float16)
 
 
 try:  # raw current-stream handle without building a Stream object
@@ -97,11 +98,11 @@ except AttributeError:  # pragma: no cover
     _raw_stream = None
 
 
-def _stream(t: torch.Tensor, stream):
+def _stream(t: torch.Tensor, stream, dev: int | None = None):
     if stream is not None:
         return stream.cuda_stream
     if _raw_stream is not None:
-        return _raw_stream(t.device.index)
+        return _raw_stream(t.get_device() if dev is None else dev)
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
@@ -122,21 +123,30 @@ def _check_x(x: torch.Tensor, allowed):
     if x.dim() != 2:
         raise ValueError("x must be 2-D [tokens, channels]")
     T, C = x.shape
-    if T > 0 and C > 0 and x.stride(1) != 1:
+    st = x.stride()
+    if T > 0 and C > 0 and st[1] != 1:
         raise ValueError("x must have unit column stride")
     if x.dtype not in allowed:
         raise ValueError(f"unsupported x dtype {x.dtype}")
-    return T, C, (x.stride(0) if T > 1 else C)
+    return T, C, (st[0] if T > 1 else C)
 
 
-def _outputs(x, T, C, codes, scales):
+# Per-call checks compare device indices (get_device(): -1 for host
+# tensors) rather than torch.device objects, which cost several times more
+# to build and compare; a decode-sized call spends most of its host time here.
+def _outputs(x, T, C, codes, scales, dev: int | None = None):
+    if dev is None:
+        dev = x.get_device()
     if codes is None:
         codes = torch.empty((T, C // 2), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((T, C // 32), dtype=torch.uint8, device=x.device)
-    for name, t, shape in (("codes", codes, (T, C // 2)), ("scales", scales, (T, C // 32))):
-        if t.dtype != torch.uint8 or t.shape != shape or not t.is_contiguous() or t.device != x.device:
-            raise ValueError(f"{name} must be a contiguous uint8 tensor of shape {shape} on {x.device}")
+    if codes.dtype != torch.uint8 or codes.shape != (T, C // 2) or not codes.is_contiguous() \
+            or codes.get_device() != dev:
+        raise ValueError(f"codes must be a contiguous uint8 tensor of shape {(T, C // 2)} on {x.device}")
+    if scales.dtype != torch.uint8 or scales.shape != (T, C // 32) or not scales.is_contiguous() \
+            or scales.get_device() != dev:
+        raise ValueError(f"scales must be a contiguous uint8 tensor of shape {(T, C // 32)} on {x.device}")
     return codes, scales
 
 
@@ -149,15 +159,16 @@ def rotate_quant(x: torch.Tensor, r_hat: torch.Tensor, lam: torch.Tensor | None 
     given, is a contiguous fp32 [tokens, channels] tensor that receives the
     rotated values (test and error-study use).
     """
-    lib = load()
-    T, C, stride = _check_x(x, (torch.bfloat16, torch.float16))
+    lib = _lib or load()
+    T, C, stride = _check_x(x, _HALF_TYPES)
+    dev = x.get_device()
     if r_hat.dtype != torch.bfloat16 or r_hat.shape != (32, 32) or not r_hat.is_contiguous() \
-            or r_hat.device != x.device:
+            or r_hat.get_device() != dev:
         raise ValueError("r_hat must be a contiguous bf16 [32, 32] tensor on x's device")
     if lam is not None and (lam.dtype != torch.float32 or lam.shape != (C,) or not lam.is_contiguous()
-                            or lam.device != x.device):
+                            or lam.get_device() != dev):
         raise ValueError("lam must be a contiguous fp32 [channels] tensor on x's device")
-    codes, scales = _outputs(x, T, C, codes, scales)
+    codes, scales = _outputs(x, T, C, codes, scales, dev)
     if y_rot is not None:
         if y_rot.dtype != torch.float32 or y_rot.shape != (T, C) or not y_rot.is_contiguous():
             raise ValueError("y_rot must be a contiguous fp32 [tokens, channels] tensor")
@@ -166,8 +177,8 @@ def rotate_quant(x: torch.Tensor, r_hat: torch.Tensor, lam: torch.Tensor | None 
                                      _ptr(codes), _ptr(scales), _ptr(y_rot), _stream(x, stream))
         fn = "mxq_rotate_quant_ex"
     else:
-        st = lib.mxq_rotate_quant(_ptr(x), _DT[x.dtype], T, C, stride, _ptr(lam), _ptr(r_hat),
-                                  _ptr(codes), _ptr(scales), _stream(x, stream))
+        st = lib.mxq_rotate_quant(x.data_ptr(), _DT[x.dtype], T, C, stride, _ptr(lam), r_hat.data_ptr(),
+                                  codes.data_ptr(), scales.data_ptr(), _stream(x, stream, dev))
         fn = "mxq_rotate_quant"
     if st != 0:
         raise MXQError(fn, st)
