@@ -322,12 +322,21 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
     const char* xb = static_cast<const char*>(a.x);
 
     typedef u32x4_t Rows[kBatch][kSub][kN];
+    // With shared factors, rows past the end load through an empty buffer
+    // range (zeros, no traffic) instead of behind a branch: with a
+    // conditional load the compiler's wait for the factors, issued before
+    // the rows, must assume the row loads may be the later ones and waits for
+    // them as well, which puts the whole first-row latency in front of the
+    // block's factor setup.  (The row-major instances keep the branch: their
+    // setup is per wave, and without the branch the long batches ran 2 %
+    // slower, 49.0 against 48.1 us on bf16 8192 x 14336.)
     auto load_rows = [&](Rows& buf, int64_t r) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int64_t rr = r + u * rs;
-            if (rr < T) {
-                const auto rsrc = row_rsrc(xb + rr * a.stride * esz, row_bytes);
+            const bool in = rr < T;
+            if (kShareLam || in) {
+                const auto rsrc = row_rsrc(xb + (in ? rr : 0) * a.stride * esz, in ? row_bytes : 0u);
 #pragma unroll
                 for (int s = 0; s < kSub; ++s)
 #pragma unroll
@@ -338,19 +347,44 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
         }
     };
 
-    Rows bufA, bufB;
-    load_rows(bufA, r0);
-
     // Block and smoothing factors are set up while the first rows load.
+    // Their loads are issued first: vector-memory loads complete in issue
+    // order for the wait counter, so a wait for a factor issued after the
+    // rows would also wait for the rows, and the setup (with its block
+    // barrier) would not overlap them.  In a launch of one round of waves
+    // that setup is on the critical path.
+    constexpr int kLamSlots = kShareLam ? kTileGroups * kGroup / kBlockThreads / 4 : 1;
+    u32x4_t lam_raw[kLamSlots];
+    if constexpr (kShareLam) {
+        const auto lrsrc = row_rsrc(a.lambda, gpr * kGroup * 4);
+#pragma unroll
+        for (int h = 0; h < kLamSlots; ++h) {
+            const uint32_t e = kLamSlots * threadIdx.x + h;  // 16-byte slot in the column
+            lam_raw[h] = __builtin_amdgcn_raw_buffer_load_b128(lrsrc, (static_cast<uint32_t>(p0) * kGroup + 4 * e) * 4,
+                                                               0, 0);
+        }
+    }
     // Rotation block as the A operands of the two output halves, bf16 bits:
     // A_h[t] = R[8q + t][8 (j / 4) + 4 h + j % 4].
-    bf16x8_t A0, A1;
+    uint16_t r_raw[2][8];
     if constexpr (MODE == kRotate) {
         const int n0 = 8 * (j >> 2) + (j & 3);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            A0[t] = __builtin_bit_cast(__bf16, a.r_hat[(8 * q + t) * kGroup + n0]);
-            A1[t] = __builtin_bit_cast(__bf16, a.r_hat[(8 * q + t) * kGroup + n0 + 4]);
+            r_raw[0][t] = a.r_hat[(8 * q + t) * kGroup + n0];
+            r_raw[1][t] = a.r_hat[(8 * q + t) * kGroup + n0 + 4];
+        }
+    }
+
+    Rows bufA, bufB;
+    load_rows(bufA, r0);
+
+    bf16x8_t A0, A1;
+    if constexpr (MODE == kRotate) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            A0[t] = __builtin_bit_cast(__bf16, r_raw[0][t]);
+            A1[t] = __builtin_bit_cast(__bf16, r_raw[1][t]);
         }
     }
     // 1 / lambda (v_rcp_f32, within 1 ulp), or lambda itself, for the 8
@@ -365,16 +399,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
         constexpr int kPer = kTileGroups * kGroup / kBlockThreads;
         static_assert(kPer % 4 == 0 && kPer * kBlockThreads == kTileGroups * kGroup, "whole 16-byte loads");
         __shared__ u32x4_t lam_s[kTileGroups * 9];
-        const auto lrsrc = row_rsrc(a.lambda, gpr * kGroup * 4);
 #pragma unroll
         for (int h = 0; h < kPer / 4; ++h) {
             const uint32_t e = kPer / 4 * threadIdx.x + h;  // 16-byte slot in the column
-            const u32x4_t l = __builtin_amdgcn_raw_buffer_load_b128(lrsrc, (static_cast<uint32_t>(p0) * kGroup + 4 * e) * 4,
-                                                                    0, 0);
+            const u32x4_t l = lam_raw[h];
+            // (slots of groups past the row end, which loaded zeros, hold 0)
+            const bool valid = p0 + static_cast<int>(e >> 3) < a.gpr;
             u32x4_t inv;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                inv[t] = LAM == kLamMul ? l[t] : as_u32(__builtin_amdgcn_rcpf(as_f32(l[t])));
+                inv[t] = !valid ? 0u : LAM == kLamMul ? l[t] : as_u32(__builtin_amdgcn_rcpf(as_f32(l[t])));
             lam_s[e + (e >> 3)] = inv;
         }
         __syncthreads();
@@ -382,11 +416,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
         for (int s = 0; s < kSub; ++s) {
             const int idx = (16 * s + j) * 9 + 2 * q;
             const u32x4_t v0 = lam_s[idx], v1 = lam_s[idx + 1];
-            const bool valid = p0 + 16 * s + j < a.gpr;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                il[s][t] = valid ? as_f32(v0[t]) : 0.0f;
-                il[s][4 + t] = valid ? as_f32(v1[t]) : 0.0f;
+                il[s][t] = as_f32(v0[t]);
+                il[s][4 + t] = as_f32(v1[t]);
             }
         }
     } else if constexpr (LAM != kLamNone) {
