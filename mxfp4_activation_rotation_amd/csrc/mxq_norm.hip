@@ -147,7 +147,7 @@ __device__ __forceinline__ double wave_sum(double v) {
 // rather than lowering the main loop's occupancy (16-wave blocks need 4).
 template <int NORM, int NT, bool YOUT, int BW>
 constexpr int kWavesPerSimd = BW == 16 ? 4
-                              : NT == 1  ? (YOUT ? 4 : 5)
+                              : NT == 1  ? 4
                               : NT == 2  ? ((YOUT || NORM == kLayer) ? 3 : 4)
                               : NT == 4  ? 2
                                          : 1;
@@ -184,74 +184,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kWave * BW),
     static_assert(!kStaged || BW == 8 || BW == 16, "a staged tile is a record row or half of one");
 
     const int C = a.channels;
-    // Factor setup: thread t takes the runs of 4 consecutive channels
-    // 4 t, 4 (t + threads), ... with 16-byte loads of gamma, beta and lambda
-    // (coalesced).  The 4 channels of a run fill one factor unit (one group,
-    // one lane, one half), so a run is one 16-byte LDS store.  A batch of
-    // runs issues all its loads before the first division waits on them: one
-    // memory latency per batch, not one per channel.  Runs past the row end
-    // (C is a multiple of 32, so a run is in or out whole) keep factor 0.
-    {
-        constexpr int kRuns = NT * kTileGroups * kGroup / 4;
-        constexpr int kPerThread = (kRuns + kBlockThreads - 1) / kBlockThreads;
-        constexpr int kBatch = kPerThread < 4 ? kPerThread : 4;
-        static_assert(kPerThread % kBatch == 0, "whole batches");
-        const uint32_t nbytes = static_cast<uint32_t>(C) * 4;
-        const auto grs = row_rsrc(a.gamma, nbytes);
-        const auto brs = row_rsrc(a.beta, a.beta ? nbytes : 0);
-        const auto lrs = row_rsrc(a.lambda, a.lambda ? nbytes : 0);
-#pragma unroll 1
-        for (int b0 = 0; b0 < kPerThread; b0 += kBatch) {
-            u32x4_t gv[kBatch], bv[kBatch], lv[kBatch];
-#pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
-                const uint32_t off = (static_cast<uint32_t>(b0 + i) * kBlockThreads + threadIdx.x) * 16;
-                gv[i] = __builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0);
-                bv[i] = __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, 0);
-                lv[i] = __builtin_amdgcn_raw_buffer_load_b128(lrs, off, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
-                const int u = (b0 + i) * kBlockThreads + static_cast<int>(threadIdx.x);  // run: channels 4u .. 4u + 3
-                if (kRuns % kBlockThreads != 0 && u >= kRuns) continue;
-                f32x4_t mv = {0.0f, 0.0f, 0.0f, 0.0f}, bq = {0.0f, 0.0f, 0.0f, 0.0f};
-                if (4 * u < C) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const float lam = a.lambda ? as_f32(lv[i][t]) : 1.0f;
-                        mv[t] = as_f32(gv[i][t]) / lam;
-                        bq[t] = a.beta ? as_f32(bv[i][t]) / lam : 0.0f;
-                    }
-                }
-                const int p = u >> 3;  // group: 16 ss + j
-                const int k = 4 * (u & 7);  // first channel of the run in its group: 8 q + 4 h
-                const int lane_c = 16 * (k >> 3) + (p & 15);
-                const int unit = ((p >> 4) * 2 + ((k >> 2) & 1)) * kWave + lane_c;
-                fm[unit] = mv;
-                fb[unit] = bq;
-            }
-        }
-    }
-    __syncthreads();
-
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int w = static_cast<int>(blockIdx.x) * kBlockWaves + wave;
     const int j = lane & 15;
     const int q = lane >> 4;
     const uint32_t gpr = static_cast<uint32_t>(a.gpr);
-
-    // The block as the A operands of the two output halves (the layout of the
-    // plain rotate kernel): A_h[t] = R[8q + t][8 (j / 4) + 4 h + j % 4].
-    bf16x8_t A0, A1;
-    {
-        const int n0 = 8 * (j >> 2) + (j & 3);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            A0[t] = __builtin_bit_cast(__bf16, a.r_hat[(8 * q + t) * kGroup + n0]);
-            A1[t] = __builtin_bit_cast(__bf16, a.r_hat[(8 * q + t) * kGroup + n0 + 4]);
-        }
-    }
 
     const uint32_t row_bytes = gpr * kGroup * 2;
     const char* xb = static_cast<const char*>(a.x);
@@ -270,6 +208,106 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kWave * BW),
 #pragma unroll
         for (int st = 0; st < NT; ++st) load_tile(buf[st], r_any, st);
     };
+
+    // The block's 2 KB (raw bf16 bits; the operands are formed after the setup).
+    uint16_t r_raw[2][8];
+    {
+        const int n0 = 8 * (j >> 2) + (j & 3);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            r_raw[0][t] = a.r_hat[(8 * q + t) * kGroup + n0];
+            r_raw[1][t] = a.r_hat[(8 * q + t) * kGroup + n0 + 4];
+        }
+    }
+
+    // Factor setup: thread t takes the runs of 4 consecutive channels
+    // 4 t, 4 (t + threads), ... with 16-byte loads of gamma, beta and lambda
+    // (coalesced).  The 4 channels of a run fill one factor unit (one group,
+    // one lane, one half), so a run is one 16-byte LDS store.  A batch of
+    // runs issues all its loads before the first division waits on them: one
+    // memory latency per batch, not one per channel.  Runs past the row end
+    // (C is a multiple of 32, so a run is in or out whole) keep factor 0.
+    // The wave's first row is loaded right after the first batch's factors:
+    // vector loads complete in issue order for the wait counter, so the
+    // setup waits for its own loads only and overlaps the row's latency; the
+    // row load is unconditional (past the end through an empty buffer
+    // range), or the compiler's wait for the factors would have to assume
+    // the row loads may be the later ones and wait for them too.
+    constexpr int kRuns = NT * kTileGroups * kGroup / 4;
+    constexpr int kPerThread = (kRuns + kBlockThreads - 1) / kBlockThreads;
+    constexpr int kBatch = kPerThread < 4 ? kPerThread : 4;
+    static_assert(kPerThread % kBatch == 0, "whole batches");
+    const uint32_t nbytes = static_cast<uint32_t>(C) * 4;
+    const auto grs = row_rsrc(a.gamma, nbytes);
+    const auto brs = row_rsrc(a.beta, a.beta ? nbytes : 0);
+    const auto lrs = row_rsrc(a.lambda, a.lambda ? nbytes : 0);
+    typedef u32x4_t Batch[kBatch];
+    auto factor_loads = [&](int b0, Batch& gv, Batch& bv, Batch& lv) {
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const uint32_t off = (static_cast<uint32_t>(b0 + i) * kBlockThreads + threadIdx.x) * 16;
+            gv[i] = __builtin_amdgcn_raw_buffer_load_b128(grs, off, 0, 0);
+            bv[i] = __builtin_amdgcn_raw_buffer_load_b128(brs, off, 0, 0);
+            lv[i] = __builtin_amdgcn_raw_buffer_load_b128(lrs, off, 0, 0);
+        }
+    };
+    auto factor_math = [&](int b0, const Batch& gv, const Batch& bv, const Batch& lv) {
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int u = (b0 + i) * kBlockThreads + static_cast<int>(threadIdx.x);  // run: channels 4u .. 4u + 3
+            if (kRuns % kBlockThreads != 0 && u >= kRuns) continue;
+            f32x4_t mv = {0.0f, 0.0f, 0.0f, 0.0f}, bq = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (4 * u < C) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const float lam = a.lambda ? as_f32(lv[i][t]) : 1.0f;
+                    mv[t] = as_f32(gv[i][t]) / lam;
+                    bq[t] = a.beta ? as_f32(bv[i][t]) / lam : 0.0f;
+                }
+            }
+            const int p = u >> 3;  // group: 16 ss + j
+            const int k = 4 * (u & 7);  // first channel of the run in its group: 8 q + 4 h
+            const int lane_c = 16 * (k >> 3) + (p & 15);
+            const int unit = ((p >> 4) * 2 + ((k >> 2) & 1)) * kWave + lane_c;
+            fm[unit] = mv;
+            fb[unit] = bq;
+        }
+    };
+    u32x4_t bufA[NT][kSub], bufB[NT][kSub];
+    {
+        Batch gv, bv, lv;
+        factor_loads(0, gv, bv, lv);
+        // (keeps the compiler from hoisting the row loads above the factors')
+        asm volatile("" ::: "memory");
+        const bool in = w < a.tokens;
+        const auto rsrc0 = row_rsrc(xb + (in ? static_cast<int64_t>(w) : 0) * a.stride * 2, in ? row_bytes : 0u);
+#pragma unroll
+        for (int st = 0; st < NT; ++st)
+#pragma unroll
+            for (int s = 0; s < kSub; ++s) {
+                const uint32_t off = (static_cast<uint32_t>(kTileGroups * st + 16 * s + j) * kGroup + 8 * q) * 2;
+                bufA[st][s] = __builtin_amdgcn_raw_buffer_load_b128(rsrc0, off, 0, kAuxNT);
+            }
+        factor_math(0, gv, bv, lv);
+    }
+#pragma unroll 1
+    for (int b0 = kBatch; b0 < kPerThread; b0 += kBatch) {
+        Batch gv, bv, lv;
+        factor_loads(b0, gv, bv, lv);
+        factor_math(b0, gv, bv, lv);
+    }
+    // A bare barrier: __syncthreads() would also wait for the row's loads.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    // The block as the A operands of the two output halves (the layout of the
+    // plain rotate kernel): A_h[t] = R[8q + t][8 (j / 4) + 4 h + j % 4].
+    bf16x8_t A0, A1;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        A0[t] = __builtin_bit_cast(__bf16, r_raw[0][t]);
+        A1[t] = __builtin_bit_cast(__bf16, r_raw[1][t]);
+    }
+
     // Row statistics of a row held in registers (groups past the row end
     // loaded zeros).  LayerNorm: the first sweep gives a shift mu0 (an fp32
     // value near the mean); the second accumulates x - mu0 and its square, so
@@ -357,8 +395,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kWave * BW),
     // into its registers as soon as the current row's super-tile is encoded
     // (at 4096 channels this is 2-4 % faster than two buffers, bit-identical).
     constexpr bool kDouble = NT <= 1;
-    u32x4_t bufA[NT][kSub], bufB[NT][kSub];
-    if (w < a.tokens) load_row(bufA, w);
     // Rows the main loop cannot do exactly enough (rare) only set fix_seen
     // there and are redone after it: bf16 rows whose squares leave fp32's
     // range, and rows holding a group whose rotated maximum is below 2^-64.
