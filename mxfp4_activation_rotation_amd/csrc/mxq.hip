@@ -969,9 +969,9 @@ static mxq_status check_common(const void* x, int32_t x_dtype, int64_t tokens, i
     return MXQ_OK;
 }
 
-static mxq_status rotate_impl(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels,
-                              int64_t stride, const float* lambda, const uint16_t* r_hat, uint8_t* codes,
-                              uint8_t* scales, float* y, void* stream, bool tiled = false) {
+mxq_status rotate_impl(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels, int64_t stride,
+                       const float* lambda, const uint16_t* r_hat, uint8_t* codes, uint8_t* scales, float* y,
+                       void* stream, bool tiled) {
     mxq_status s = check_common(x, x_dtype, tokens, channels, stride, false);
     if (s != MXQ_OK) return s;
     if (tiled && channels % 128) return MXQ_ERR_SHAPE;
@@ -1022,7 +1022,7 @@ mxq_status mxq_rotate_quant(const void* x, int32_t x_dtype, int64_t tokens, int6
                             int64_t x_row_stride, const float* lambda, const uint16_t* r_hat,
                             uint8_t* codes, uint8_t* scales, void* stream) {
     return rotate_impl(x, x_dtype, tokens, channels, x_row_stride, lambda, r_hat, codes, scales, nullptr,
-                       stream);
+                       stream, false);
 }
 
 mxq_status mxq_rotate_quant_tiled(const void* x, int32_t x_dtype, int64_t tokens, int64_t channels,
@@ -1036,7 +1036,7 @@ mxq_status mxq_rotate_quant_ex(const void* x, int32_t x_dtype, int64_t tokens, i
                                int64_t x_row_stride, const float* lambda, const uint16_t* r_hat,
                                uint8_t* codes, uint8_t* scales, float* y_rot, void* stream) {
     return rotate_impl(x, x_dtype, tokens, channels, x_row_stride, lambda, r_hat, codes, scales, y_rot,
-                       stream);
+                       stream, false);
 }
 
 mxq_status mxq_absorb_quant(const void* w, int32_t w_dtype, int64_t rows, int64_t cols, int64_t w_row_stride,

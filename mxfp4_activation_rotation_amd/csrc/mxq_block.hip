@@ -1,8 +1,9 @@
 // Rotation by a B x B block for B = 16, 32, 64, 128, then MXFP4 of every
 // 32-element group: the block sizes of the DuQuant++ page's ablation
 // (sec. 4.3), which keeps MXFP4 groups 32 wide and varies the rotation
-// block.  B = 32 is the main path (mxq_rotate_quant, a separate tuned
-// kernel); this kernel serves the error study of the other sizes.
+// block.  B = 32 is the main path: the entry point sends it to the fused
+// kernel of mxq_rotate_quant (the same MFMA products, so the same bits);
+// this kernel serves the error study's other sizes.
 //
 // Layout.  A block of B = 32 KB channels is one column of the MFMA and its KB
 // input groups are KB k-steps: for the 16 blocks of a sub-tile, lane l
@@ -501,7 +502,6 @@ template <int XT, bool LAM>
 mxq_status dispatch_block(const BlockArgs& a, int block, hipStream_t st) {
     switch (block) {
         case 16: return launch<XT, LAM, 1, true>(a, st);
-        case 32: return launch<XT, LAM, 1, false>(a, st);
         case 64: return launch<XT, LAM, 2, false>(a, st);
         default: return launch<XT, LAM, 4, false>(a, st);
     }
@@ -521,6 +521,9 @@ extern "C" mxq_status mxq_rotate_quant_block(const void* x, int32_t x_dtype, int
     if (tokens < 0 || channels < 0 || channels % kGroup || channels % block || tokens >= (int64_t(1) << 31) ||
         channels > (int64_t(1) << 28))
         return MXQ_ERR_SHAPE;
+    if (block == 32)
+        return mxq::rotate_impl(x, x_dtype, tokens, channels, x_row_stride, lambda, r_block, codes, scales, y_rot,
+                                stream, false);
     if (tokens == 0 || channels == 0) return MXQ_OK;
     if (!x || !r_block || !codes || !scales) return MXQ_ERR_NULL;
     if (x_row_stride < channels) return MXQ_ERR_STRIDE;
