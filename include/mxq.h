@@ -144,8 +144,8 @@ mxq_status mxq_dequant(const uint8_t *codes, const uint8_t *scales, int64_t toke
  * every 32-element group of the result is MXFP4-encoded as in
  * mxq_rotate_quant.  block must be 16, 32, 64 or 128 and divide channels
  * (MXQ_ERR_SHAPE otherwise); y_rot may be NULL or fp32 [tokens][channels].
- * B = 32 gives the same bits as mxq_rotate_quant (same arithmetic, a kernel
- * not tuned for speed); otherwise the same arithmetic, layout and error
+ * B = 32 is mxq_rotate_quant itself (the call goes to its kernel); otherwise
+ * the same arithmetic, layout and error
  * rules: the product runs on the matrix cores with the bf16 terms of x' that
  * mxq_rotate_quant uses (exact without lambda, two rounded terms with it). */
 mxq_status mxq_rotate_quant_block(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
