@@ -144,10 +144,10 @@ mxq_status mxq_dequant(const uint8_t *codes, const uint8_t *scales, int64_t toke
  * every 32-element group of the result is MXFP4-encoded as in
  * mxq_rotate_quant.  block must be 16, 32, 64 or 128 and divide channels
  * (MXQ_ERR_SHAPE otherwise); y_rot may be NULL or fp32 [tokens][channels].
- * B = 32 is mxq_rotate_quant itself (the call goes to its kernel); otherwise
- * the same arithmetic, layout and error
- * rules: the product runs on the matrix cores with the bf16 terms of x' that
- * mxq_rotate_quant uses (exact without lambda, two rounded terms with it). */
+ * B = 32 is mxq_rotate_quant itself (the call goes to its kernel); other
+ * sizes follow the same arithmetic, layout and error rules: the product runs
+ * on the matrix cores with the bf16 terms of x' that mxq_rotate_quant uses
+ * (exact without lambda, two rounded terms with it). */
 mxq_status mxq_rotate_quant_block(const void *x, int32_t x_dtype, int64_t tokens, int64_t channels,
                                   int64_t x_row_stride, const float *lambda, const uint16_t *r_block,
                                   int32_t block, uint8_t *codes, uint8_t *scales, float *y_rot,
