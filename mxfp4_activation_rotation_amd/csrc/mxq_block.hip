@@ -420,7 +420,31 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kBlockThreads),
             __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(S), srsrc, grp, 0, 0);
         }
         // (groups past the row end, zeros whose stores are dropped, do not count)
-        return S < (kTinyScaleBits >> 23) && grp < gpr;
+        bool tiny = S < (kTinyScaleBits >> 23) && grp < gpr;
+        if constexpr (!FIX) {
+            // A block of zero inputs (padding rows of a serving batch) has
+            // x' = 0 exactly, so its codes and scales are exact already: only
+            // blocks holding a nonzero input bit pattern count (bit j of
+            // nzm[s]: block j of sub-tile s).  The ballots run only where some
+            // group fell below the bound.
+            if (any_lane(tiny)) {
+                uint32_t nzm[kSubs];
+#pragma unroll
+                for (int s = 0; s < kSubs; ++s) {
+                    uint32_t o = 0;
+#pragma unroll
+                    for (int k = 0; k < KB; ++k) o |= xin[s][k][0] | xin[s][k][1] | xin[s][k][2] | xin[s][k][3];
+                    const uint64_t b = __builtin_amdgcn_ballot_w64((o & 0x7fff7fffu) != 0u);
+                    const uint64_t f = b | (b >> 32);
+                    nzm[s] = static_cast<uint32_t>(f | (f >> 16)) & 0xffffu;
+                }
+                uint32_t nz = nzm[0];
+#pragma unroll
+                for (int s = 1; s < kSubs; ++s) nz = q / KB == s ? nzm[s] : nz;
+                tiny = tiny && ((nz >> j) & 1u);
+            }
+        }
+        return tiny;
     };
 
     bool tiny_seen = false;

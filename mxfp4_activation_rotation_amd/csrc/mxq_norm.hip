@@ -421,8 +421,21 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kWave * BW),
             float mu, mu_lo;
             row_stats(buf, s2, var, mean, mu, mu_lo);
             // bf16 rows whose sum of squares left fp32's safe range (squares
-            // over 2^128 or below 2^-149) are redone after the main loop
-            if constexpr (!kFp16) fix_seen |= !(s2 >= 0x1p-80 && s2 <= 0x1p+1000);
+            // over 2^128 or below 2^-149) are redone after the main loop; a
+            // row of zeros (padding in a serving batch) has exact statistics
+            // and is not (the test of its bits runs only in such rows)
+            if constexpr (!kFp16) {
+                if (!(s2 >= 0x1p-80 && s2 <= 0x1p+1000)) {
+                    uint32_t nz = 0;
+#pragma unroll
+                    for (int st = 0; st < NT; ++st)
+#pragma unroll
+                        for (int s = 0; s < kSub; ++s)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) nz |= buf[st][s][i] & 0x7fff7fffu;
+                    fix_seen |= !(s2 == 0.0 && !any_lane(nz != 0u));
+                }
+            }
             const float inv = static_cast<float>(1.0 / sqrt(var + static_cast<double>(a.eps)));
 
             // ---- normalize, smooth, rotate, encode
@@ -510,7 +523,28 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kWave * BW),
                 const uint32_t S = q == 0 ? sc[0] : q == 1 ? sc[1] : q == 2 ? sc[2] : sc[3];
                 const uint32_t g = static_cast<uint32_t>(kTileGroups * st + lane);
                 // (groups past the row end, zeros whose stores are dropped, do not count)
-                fix_seen |= S < (kTinyScaleBits >> 23) && g < gpr;
+                bool tiny = S < (kTinyScaleBits >> 23) && g < gpr;
+                if constexpr (NORM == kRms) {
+                    // With RMSNorm and no beta a group of zero inputs has
+                    // x' = 0 exactly, so its codes and scale are exact
+                    // already: only groups holding a nonzero input bit
+                    // pattern (bit j of nzm[s]: group 16 s + j) count.  The
+                    // ballots run only where some group fell below the bound.
+                    if (!a.beta && any_lane(tiny)) {
+                        uint32_t nzm[kSub];
+#pragma unroll
+                        for (int s = 0; s < kSub; ++s) {
+                            const u32x4_t& w = buf[st][s];
+                            const uint64_t b =
+                                __builtin_amdgcn_ballot_w64(((w[0] | w[1] | w[2] | w[3]) & 0x7fff7fffu) != 0u);
+                            const uint64_t f = b | (b >> 32);
+                            nzm[s] = static_cast<uint32_t>(f | (f >> 16)) & 0xffffu;
+                        }
+                        const uint32_t nz = q == 0 ? nzm[0] : q == 1 ? nzm[1] : q == 2 ? nzm[2] : nzm[3];
+                        tiny = tiny && ((nz >> j) & 1u);
+                    }
+                }
+                fix_seen |= tiny;
                 if constexpr (kStaged) {
                     stg[sb][wave][g] = u32x4_t{word[0], word[1], word[2], word[3]};
                     sstg[sb][g * BW + wave] = static_cast<uint8_t>(S);

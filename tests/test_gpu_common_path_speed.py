@@ -158,6 +158,49 @@ def test_rotate_quant_rows_of_zeros(dev, smoothed):
     assert not c2[1::2].any() and not s2[1::2].any()
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_norm_rows_of_zeros(dev, dtype):
+    """Padding rows (all zero) of an RMSNorm batch without beta have exact
+    statistics and x' = 0: they must not send the wave through the pass that
+    redoes rare rows, and they encode as zero codes and zero scale bytes."""
+    r = _orthogonal(32, 11, dev)
+    x, lam, gamma = _inputs(8192, 4096, 12, dev)
+    x = x.to(dtype)
+    xz = x.clone()
+    xz[1::2] = 0
+    codes, scales = _outputs(8192, 4096, dev)
+    t = _time_us(lambda: mxq.norm_rotate_quant(x, r, gamma, None, lam, codes=codes, scales=scales))
+    tz = _time_us(lambda: mxq.norm_rotate_quant(xz, r, gamma, None, lam, codes=codes, scales=scales))
+    print(f"  norm {dtype} 8192x4096: {t:.1f} us, every other row zero {tz:.1f} us")
+    assert tz < 1.3 * t
+    c1, s1 = mxq.norm_rotate_quant(x, r, gamma, None, lam)
+    c2, s2 = mxq.norm_rotate_quant(xz, r, gamma, None, lam)
+    torch.cuda.synchronize()
+    c1, s1, c2, s2 = (a.cpu().numpy() for a in (c1, s1, c2, s2))
+    assert np.array_equal(c1[0::2], c2[0::2]) and np.array_equal(s1[0::2], s2[0::2])
+    assert not c2[1::2].any() and not s2[1::2].any()
+
+
+@pytest.mark.parametrize("B", [64, 128])
+def test_block_rows_of_zeros(dev, B):
+    """The same for the block-size kernel: blocks of zero inputs are exact."""
+    rb = _orthogonal(B, 13, dev)
+    x, _, _ = _inputs(4096, 14336, 14, dev)
+    xz = x.clone()
+    xz[1::2] = 0
+    codes, scales = _outputs(4096, 14336, dev)
+    t = _time_us(lambda: mxq.rotate_quant_block(x, rb, codes=codes, scales=scales))
+    tz = _time_us(lambda: mxq.rotate_quant_block(xz, rb, codes=codes, scales=scales))
+    print(f"  block {B} 4096x14336: {t:.1f} us, every other row zero {tz:.1f} us")
+    assert tz < 1.3 * t
+    c1, s1 = mxq.rotate_quant_block(x, rb)
+    c2, s2 = mxq.rotate_quant_block(xz, rb)
+    torch.cuda.synchronize()
+    c1, s1, c2, s2 = (a.cpu().numpy() for a in (c1, s1, c2, s2))
+    assert np.array_equal(c1[0::2], c2[0::2]) and np.array_equal(s1[0::2], s2[0::2])
+    assert not c2[1::2].any() and not s2[1::2].any()
+
+
 @pytest.mark.parametrize("T,C,bound", [(8192, 4096, 1.4), (2048, 5120, 1.6)])
 def test_norm_tiled_output_keeps_pace(dev, T, C, bound):
     """The tiled output of long batches stages record rows in LDS and meets
