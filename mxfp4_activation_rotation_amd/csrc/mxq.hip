@@ -60,12 +60,14 @@
 #define MXQ_BATCH_SPLIT 1
 #endif
 // Smoothed instances (x * 1/lambda, x * lambda: two rounded bf16 terms)
-// keep two rows in flight per wave at 12 waves per CU.
+// keep one row in flight per wave at 8 waves per CU (side by side against
+// two rows at 12: fp16 32768 x 8192 118.6 -> 115.7 us, bf16 32768 x 4096
+// 61.4 -> 60.4 us, 16384 x 8192 62.0 -> 60.6 us, 8192 x 14336 level).
 #ifndef MXQ_WAVES_PER_CU_LAM
-#define MXQ_WAVES_PER_CU_LAM 12
+#define MXQ_WAVES_PER_CU_LAM 8
 #endif
 #ifndef MXQ_BATCH_LAM
-#define MXQ_BATCH_LAM 2
+#define MXQ_BATCH_LAM 1
 #endif
 // fp16 x times its factor in one v_fma_mix_f32; bf16 terms of a smoothed
 // x' (2: each rounded to nearest, |x' - hi - lo| <= 2^-18 |x'|; 3: exact).
@@ -908,12 +910,13 @@ static mxq_status launch(Args a, int64_t tokens, int64_t channels, hipStream_t s
     if (!make_plan((tokens + a.unit - 1) / a.unit, channels, cus, per_cu, &pl)) return MXQ_ERR_SHAPE;
     a.tcols = pl.tcols;
     if constexpr (kShareLamOf<LAM, TILED, true>) {
-        // A short batch (at most eight batches of rows per wave under the
-        // row-major plan) takes the block-shared-factor instance, planned
-        // at its own occupancy.  Whole blocks per column: the row step
-        // rounds up to a multiple of the block's waves (waves whose first
-        // row is past the end do nothing but share the block's factor load).
-        if ((tokens + pl.row_step - 1) / pl.row_step <= 8 * kBatchOf<XT, MODE, LAM>) {
+        // A short batch (at most 192 rows per CU and super-tile column:
+        // 16 rows per wave at 12 waves per CU) takes the block-shared-factor
+        // instance, planned at its own occupancy.  Whole blocks per column:
+        // the row step rounds up to a multiple of the block's waves (waves
+        // whose first row is past the end do nothing but share the block's
+        // factor load).
+        if ((tokens + pl.row_step - 1) / pl.row_step * per_cu <= 192) {
             const int occ_s = occupancy_waves_per_cu<XT, MODE, LAM, YOUT, TILED, true>();
             constexpr int want_s = kWavesPerCuFor<XT, MODE, LAM, TILED, true>;
             Plan ps;

@@ -506,7 +506,15 @@ int waves_per_cu() {
 template <int XT, bool LAM, int KB, bool HALF, bool YOUT>
 mxq_status launch_y(BlockArgs a, hipStream_t st) {
     a.tcols = (a.gpr + kTileGroups - 1) / kTileGroups;
-    const int64_t slots = static_cast<int64_t>(device_cu_count()) * waves_per_cu<XT, LAM, KB, HALF, YOUT>();
+    // The plan fills at most 8 waves per CU (two per SIMD), each walking more
+    // rows, whatever the occupancy allows: side by side (bf16 8192 x 14336)
+    // B = 16 52.8 -> 48.9 us, B = 64 52.7 -> 48.4 us, B = 128 57.2 -> 55.0 us,
+    // and fp16 32768 x 8192 with lambda B = 16 124.0 -> 116.3 us, B = 64
+    // level; 6 or 12 waves per CU were slower.  Smoothed B = 128 keeps its
+    // 12 (164.5 against 168.9 us with 8).
+    constexpr int kCapWavesPerCu = (KB == 4 && LAM) ? 1 << 20 : 8;
+    const int wpc = waves_per_cu<XT, LAM, KB, HALF, YOUT>();
+    const int64_t slots = static_cast<int64_t>(device_cu_count()) * (wpc < kCapWavesPerCu ? wpc : kCapWavesPerCu);
     int64_t rs = slots / a.tcols;
     if (rs < 1) rs = 1;
     if (rs > a.tokens) rs = a.tokens;
