@@ -59,6 +59,14 @@
 #ifndef MXQ_BATCH_SPLIT
 #define MXQ_BATCH_SPLIT 1
 #endif
+// ... and at most MXQ_SPLIT_LONG_WAVES per CU once the batch gives each wave
+// at least MXQ_SPLIT_LONG_ROWS rows (unsmoothed fp16; see launch()).
+#ifndef MXQ_SPLIT_LONG_WAVES
+#define MXQ_SPLIT_LONG_WAVES 12
+#endif
+#ifndef MXQ_SPLIT_LONG_ROWS
+#define MXQ_SPLIT_LONG_ROWS 4
+#endif
 // Smoothed instances (x * 1/lambda, x * lambda: two rounded bf16 terms)
 // keep one row in flight per wave at 8 waves per CU (side by side against
 // two rows at 12: fp16 32768 x 8192 118.6 -> 115.7 us, bf16 32768 x 4096
@@ -903,8 +911,19 @@ static mxq_status launch(Args a, int64_t tokens, int64_t channels, hipStream_t s
     const int occ = occupancy_waves_per_cu<XT, MODE, LAM, YOUT, TILED>();
     Plan pl;
     constexpr int want = kWavesPerCuOf<XT, MODE, LAM>;
-    const int per_cu = occ < want ? occ : want;
+    int per_cu = occ < want ? occ : want;
     const int cus = device_cu_count();
+    // fp16 without smoothing (two exact bf16 terms): 16 waves per CU suit
+    // batches of a round or two, but long batches stream better with fewer,
+    // longer-lived waves (fp16 32768 x 8192: 123.5 -> 112.9 us at 12 waves
+    // per CU; 8192 x 14336: 55.1 -> 52.6 us; 2048 x 4096 stays at 16: 6.2
+    // against 6.7 us).
+    if constexpr (kSplit<XT, MODE, LAM> && LAM == kLamNone && !TILED) {
+        const int64_t units = tokens * ((channels / kGroup + kTileGroups - 1) / kTileGroups);
+        if (per_cu > MXQ_SPLIT_LONG_WAVES &&
+            units >= static_cast<int64_t>(cus) * MXQ_SPLIT_LONG_WAVES * MXQ_SPLIT_LONG_ROWS)
+            per_cu = MXQ_SPLIT_LONG_WAVES;
+    }
     a.unit = 1;
     if (TILED) a.unit = tiled_unit(tokens, channels, static_cast<int64_t>(cus) * per_cu);
     if (!make_plan((tokens + a.unit - 1) / a.unit, channels, cus, per_cu, &pl)) return MXQ_ERR_SHAPE;
