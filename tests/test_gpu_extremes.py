@@ -328,6 +328,38 @@ def test_norm_small_factors(dev, orc, norm):
     assert int((scales < 61).sum()) > 0
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("T,C", [(64, 4096), (4200, 2048)])
+def test_norm_zero_rows_among_tiny_groups(dev, orc, dtype, T, C):
+    """RMSNorm without beta: rows and groups of zeros skip the pass that
+    redoes rare rows (their x' is exactly 0), while tiny nonzero groups
+    next to them, in the same row or wave, are still redone.  Row kinds:
+    all zero; extreme rows; half the groups zero and the rest tiny; all
+    groups zero but one holding a large value next to tiny ones."""
+    rng = np.random.default_rng(8900 + C + T)
+    tiny = 2.0 ** -80 if dtype == torch.bfloat16 else 2.0 ** -22
+    big = 2.0 ** 60 if dtype == torch.bfloat16 else 30000.0
+    x = extreme_rows(dtype, T, C, 8950 + C).float().numpy().astype(np.float64)
+    for t in range(T):
+        k = t % 4
+        if k == 0:
+            x[t] = 0.0
+        elif k == 2:
+            x[t, : C // 2] = 0.0
+            x[t, C // 2:] = tiny * rng.standard_normal(C - C // 2)
+        elif k == 3:
+            x[t] = 0.0
+            g = int(rng.integers(C // 32))
+            x[t, 32 * g: 32 * g + 32] = tiny * rng.standard_normal(32)
+            x[t, 32 * g + int(rng.integers(32))] = big
+    x = W.to_dtype(x, dtype)
+    gamma = rng.uniform(0.5, 1.5, C).astype(np.float32)
+    lam = np.exp(0.5 * rng.standard_normal(C)).astype(np.float32)
+    r = W.bf16_matrix(W.qr_orthogonal(rng))
+    codes, scales = norm_check(x, r, gamma, None, lam, "rms", 1e-5, dev, orc, f"zero rows {dtype} {T}x{C}")
+    assert not codes[0::4].any() and not scales[0::4].any()
+
+
 def test_norm_long_batch_staged_with_extreme_rows(dev, orc):
     """The staged tiled path (8- and 16-wave blocks) with rows to redo: the
     block's record stores complete before the rewrites."""
