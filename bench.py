@@ -196,7 +196,8 @@ def bench_gemm(args):
     operands (88 MB) are built once on the GPU before the timed region.
     With --decode, the activations are the first --rows tokens (1..64,
     default 16) of the same batch: the product is bound by reading the
-    weights, so its roofline is HBM.  Both
+    weights, so its roofline is HBM.  Without --decode, --rows (65..8192)
+    takes the first rows of the batch as a shorter prefill.  Both
     operands are in the fragment-tiled layout (the activations written so by
     the quantizer, the weights repacked once offline); --row-layout times the
     row-layout operands instead."""
@@ -216,7 +217,7 @@ def bench_gemm(args):
     M, K, N = ac.shape[0], wl.channels, workloads.DOWN_PROJ_OUT
     weight_bytes = N * (K // 2 + K // 32)
     tiled = not args.row_layout
-    if args.decode:
+    if args.rows is not None:
         M = args.rows
         ac, asc = ac[:M].contiguous(), asc[:M].contiguous()
     if tiled:
@@ -256,8 +257,10 @@ def bench_gemm(args):
         hbm = None
     elif args.decode:
         hbm = read_counters(0, DECODE_COUNTERS.get(M, ""), GEMM_SOURCES)
-    else:
+    elif M == 8192:
         hbm = read_counters(0, GEMM_COUNTERS, GEMM_SOURCES)
+    else:
+        hbm = None
     result = {
         "metric": "W4A4 MXFP4 GEMM throughput (consumer of the quantized activations): TFLOP/s",
         "value": round(flop * args.steps / wall / 1e12, 1),
@@ -267,9 +270,10 @@ def bench_gemm(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp4",
         "data": "synthetic",
-        "config": {"workload": "down_proj product: activations bf16 8192x14336 (the headline batch) rotated and "
-                               "MXFP4-quantized, times absorbed MXFP4 weights 4096x14336 (seeded N(0, 1/14336)); "
-                               "fp32 accumulation, bf16 output",
+        "config": {"workload": f"down_proj product: activations bf16 {M}x14336 ("
+                               + ("the headline batch" if M == 8192 else f"the first {M} tokens of the headline batch")
+                               + ") rotated and MXFP4-quantized, times absorbed MXFP4 weights 4096x14336 "
+                                 "(seeded N(0, 1/14336)); fp32 accumulation, bf16 output",
                    "M": M, "N": N, "K": K,
                    "operands": "E2M1 codes + E8M0 scales per 32 along K, " +
                                ("fragment-tiled records (16 rows x 128 positions)" if tiled else "row layout"),
@@ -430,8 +434,9 @@ def main():
                          "with absorbed, quantized weights (8192x14336 by 4096x14336)")
     ap.add_argument("--decode", action="store_true",
                     help="with --gemm: a few activation rows (decode), timed against HBM bandwidth")
-    ap.add_argument("--rows", type=int, default=16,
-                    help="with --gemm --decode: activation rows, 1..64 (default 16)")
+    ap.add_argument("--rows", type=int, default=None,
+                    help="with --gemm: activation rows, the first of the headline batch; with --decode "
+                         "1..64 (default 16), otherwise 65..8192 (default 8192)")
     ap.add_argument("--row-layout", action="store_true",
                     help="with --gemm: row-layout operands instead of fragment-tiled ones")
     ap.add_argument("--norm", action="store_true",
@@ -459,8 +464,12 @@ def main():
               f"does not launch on several GPUs (asked for --gpus {args.gpus}, WORLD_SIZE={world}).",
               file=sys.stderr)
         sys.exit(2)
-    if not 1 <= args.rows <= 64:
-        ap.error("--rows must be in 1..64 (the decode-shaped product kernel's range)")
+    if args.decode:
+        args.rows = 16 if args.rows is None else args.rows
+        if not 1 <= args.rows <= 64:
+            ap.error("--rows must be in 1..64 with --decode (the decode-shaped product kernel's range)")
+    elif args.rows is not None and not 65 <= args.rows <= 8192:
+        ap.error("--rows must be in 65..8192 without --decode (the headline batch has 8192 tokens)")
 
     import numpy as np
     import torch

@@ -34,6 +34,9 @@
 // bounded to the tile's rows (or records), so rows past M or N read as zero
 // (codes 0, scale 2^-127: products 0) and ragged edges need no branches.
 //
+// Mid-size products on tiled operands whose 256 x 256 grid has fewer tiles
+// than the chip has CUs: 256 x 128 tiles, two blocks per CU (gemm2_kernel).
+//
 // Decode-shaped products (M <= 64): split-K over the 16 waves of a block
 // that owns 16 output columns (see gemm_small_kernel).
 #include <hip/hip_runtime.h>
@@ -360,6 +363,155 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     }
 }
 
+// Mid-size products on fragment-tiled operands, whose grid of 256 x 256
+// tiles would leave CUs idle (fewer tiles than CUs, e.g. 2048 tokens by 4096
+// outputs): a 256 x 128 tile over 4 waves (one per SIMD, each 128 x 64 as
+// above, the same MFMA sequence, so the same bits) with two blocks resident
+// per CU.  The ring is 3 stages deep and each stage carries its own scale
+// records (A 16 KB + B 8 KB of codes, 1 KB + 512 B of scales: 76.5 KB per
+// block, so two fit in the 160 KB of LDS).  Stage kt + 2 is loaded while
+// stage kt computes, so before the barrier of step kt a wave's only loads in
+// flight are those of stage kt + 1 and it waits for all of them.  On grids
+// that already fill the chip the 256 x 256 kernel is faster: per flop, a CU
+// pulls 1.5x the operand bytes here.
+constexpr int k2WavesN = 2;
+constexpr int k2Waves = kWavesM * k2WavesN;  // 4
+constexpr int k2Threads = kWave * k2Waves;   // 256
+constexpr int k2BN = 16 * kFragN * k2WavesN; // 128
+constexpr int k2Nst = 3;
+constexpr int k2LoadsA = (kBM / 16) / k2Waves;   // 4
+constexpr int k2LoadsB = (k2BN / 16) / k2Waves;  // 2
+constexpr int k2LoadsPerStage = k2LoadsA + k2LoadsB + 2;
+
+struct Stage2 {
+    uint8_t a[kBM * kRowBytes];
+    uint8_t b[k2BN * kRowBytes];
+    uint8_t sa[kBM / 16 * 64];
+    uint8_t sb[k2BN / 16 * 64];
+};
+
+template <bool OUT_BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, k2Threads), amdgpu_waves_per_eu(2))) void gemm2_kernel(GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) Stage2 st[k2Nst];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int wm = wave / k2WavesN;
+    const int wn = wave % k2WavesN;
+    const int nblk = static_cast<int>(gridDim.x);
+    int bid = static_cast<int>(blockIdx.x);
+    if (nblk % kXcds == 0) bid = (bid % kXcds) * (nblk / kXcds) + bid / kXcds;
+    const int band = MXQ_GEMM_GROUP_M * g.tiles_n;
+    const int first_m = (bid / band) * MXQ_GEMM_GROUP_M;
+    const int band_rows = min(g.tiles_m - first_m, MXQ_GEMM_GROUP_M);
+    const int in_band = bid % band;
+    const int tm = __builtin_amdgcn_readfirstlane(first_m + in_band % band_rows);
+    const int tn = __builtin_amdgcn_readfirstlane(in_band / band_rows);
+    const int64_t m0 = static_cast<int64_t>(tm) * kBM;
+    const int64_t n0 = static_cast<int64_t>(tn) * k2BN;
+    const uint32_t nk32 = static_cast<uint32_t>(g.K) / kStageK;
+    const uint32_t recs_a = static_cast<uint32_t>(min<int64_t>(kBM / 16, (g.M + 15) / 16 - m0 / 16));
+    const uint32_t recs_b = static_cast<uint32_t>(min<int64_t>(k2BN / 16, (g.N + 15) / 16 - n0 / 16));
+    const auto ra = rsrc(g.a_codes + (m0 / 16) * nk32 * 1024, recs_a * nk32 * 1024);
+    const auto rb = rsrc(g.b_codes + (n0 / 16) * nk32 * 1024, recs_b * nk32 * 1024);
+    const auto rsa = rsrc(g.a_scales + (m0 / 16) * nk32 * 64, recs_a * nk32 * 64);
+    const auto rsb = rsrc(g.b_scales + (n0 / 16) * nk32 * 64, recs_b * nk32 * 64);
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    const uint32_t goff = 16 * static_cast<uint32_t>(lane) + static_cast<uint32_t>(wave) * nk32 * 1024;
+    // Each stage slot gets one 1 KB record per load (A records w, w + 4, ...;
+    // B records w, w + 4) and the stage's scale records: wave w fetches A
+    // records 4 w .. 4 w + 3 (16 lanes x 4 bytes each) and, with lanes 0-31,
+    // B records 2 w and 2 w + 1.  Every wave issues the same number of loads
+    // per stage (a partial-lane load still counts once in vmcnt).
+    const uint32_t sa_goff = (static_cast<uint32_t>(4 * wave + (lane >> 4)) * nk32) * 64 + 4 * static_cast<uint32_t>(lane & 15);
+    const uint32_t sb_goff = (static_cast<uint32_t>(2 * wave + ((lane >> 4) & 1)) * nk32) * 64 + 4 * static_cast<uint32_t>(lane & 15);
+    auto load = [&](int kt, int buf) {
+        Stage2& S = st[buf];
+#pragma unroll
+        for (int u = 0; u < k2LoadsA; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(S.a + (wave + k2Waves * u) * 1024), 16, goff,
+                                                     1024 * kt + u * k2Waves * static_cast<int>(nk32) * 1024, 0, 0);
+#pragma unroll
+        for (int u = 0; u < k2LoadsB; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(S.b + (wave + k2Waves * u) * 1024), 16, goff,
+                                                     1024 * kt + u * k2Waves * static_cast<int>(nk32) * 1024, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr)(S.sa + wave * 256), 4, sa_goff, 64 * kt, 0, 0);
+        if (lane < 32)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr)(S.sb + wave * 128), 4, sb_goff, 64 * kt, 0, 0);
+    };
+    f32x4g_t acc[kFragM][kFragN];
+#pragma unroll
+    for (int i = 0; i < kFragM; ++i)
+#pragma unroll
+        for (int j = 0; j < kFragN; ++j) acc[i][j] = f32x4g_t{0.f, 0.f, 0.f, 0.f};
+    const uint32_t op_off = 16 * static_cast<uint32_t>(lane);
+    u32x4g_t aop[kFragM], bop0[kFragN], bop1[kFragN];
+    int sa[kFragM], sb0[kFragN], sb1[kFragN];
+    auto read_a = [&](int kt, int f) {
+        const Stage2& S = st[kt % k2Nst];
+        aop[f] = *reinterpret_cast<const u32x4g_t*>(S.a + (wm * kFragM + f) * 1024 + op_off);
+        sa[f] = S.sa[(wm * kFragM + f) * 64 + lane];
+    };
+    auto read_b = [&](int kt, int j, u32x4g_t* bop, int* sb) {
+        const Stage2& S = st[kt % k2Nst];
+        bop[j] = *reinterpret_cast<const u32x4g_t*>(S.b + (wn * kFragN + j) * 1024 + op_off);
+        sb[j] = S.sb[(wn * kFragN + j) * 64 + lane];
+    };
+    const int nk = g.K / kStageK;
+#pragma unroll
+    for (int s0 = 0; s0 < k2Nst - 1; ++s0)
+        if (s0 < nk) load(s0, s0);
+    auto step = [&](int kt, const u32x4g_t* cb, const int* csb, u32x4g_t* nb, int* nsb) {
+        if (kt + 1 < nk) wait_vmcnt<0>();
+        asm volatile("s_barrier" ::: "memory");
+        if (kt + k2Nst - 1 < nk) load(kt + k2Nst - 1, (kt + k2Nst - 1) % k2Nst);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int f = 0; f < kFragM; ++f) {
+#pragma unroll
+            for (int j = 0; j < kFragN; ++j)
+                acc[f][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    operand(aop[f]), operand(cb[j]), acc[f][j], kFmtE2M1, kFmtE2M1, 0, sa[f], 0, csb[j]);
+            read_a(kt + 1, f);
+            if (f < kFragN) read_b(kt + 1, f, nb, nsb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    if (nk > 0) {
+        if (nk > 1)
+            wait_vmcnt<k2LoadsPerStage>();
+        else
+            wait_vmcnt<0>();
+        asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+        for (int f = 0; f < kFragM; ++f) read_a(0, f);
+#pragma unroll
+        for (int j = 0; j < kFragN; ++j) read_b(0, j, bop0, sb0);
+    }
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, bop0, sb0, bop1, sb1);
+        if (kt + 1 < nk) step(kt + 1, bop1, sb1, bop0, sb0);
+    }
+    const int h = lane >> 4;
+    const int c16 = lane & 15;
+#pragma unroll
+    for (int f = 0; f < kFragM; ++f) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t row = m0 + (wm * kFragM + f) * 16 + 4 * h + r;
+            if (row >= g.M) continue;
+#pragma unroll
+            for (int j = 0; j < kFragN; ++j) {
+                const int64_t col = n0 + (wn * kFragN + j) * 16 + c16;
+                if (col >= g.N) continue;
+                if constexpr (OUT_BF16)
+                    static_cast<__bf16*>(g.y)[row * g.ldy + col] = static_cast<__bf16>(acc[f][j][r]);
+                else
+                    static_cast<float*>(g.y)[row * g.ldy + col] = acc[f][j][r];
+            }
+        }
+    }
+}
+
 // Decode-shaped products (M <= 64 activation rows).  The weights dominate
 // the bytes, and a 256 x 256 tile would leave most of the chip idle, so a
 // block owns 16 weight rows (output columns) and its 16 waves split K: wave
@@ -500,6 +652,18 @@ mxq_status launch_gemm(const GemmArgs& g, bool out_bf16, hipStream_t st) {
         else
             launch_small<false, TILED>(g, st);
     } else {
+        if constexpr (TILED) {
+            if (static_cast<int64_t>(g.tiles_m) * g.tiles_n < device_cu_count()) {
+                GemmArgs g2 = g;
+                g2.tiles_n = (g.N + k2BN - 1) / k2BN;
+                const dim3 grid2(static_cast<unsigned>(static_cast<int64_t>(g2.tiles_m) * g2.tiles_n));
+                if (out_bf16)
+                    hipLaunchKernelGGL((gemm2_kernel<true>), grid2, dim3(k2Threads), 0, st, g2);
+                else
+                    hipLaunchKernelGGL((gemm2_kernel<false>), grid2, dim3(k2Threads), 0, st, g2);
+                return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_HIP;
+            }
+        }
         const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(g.tiles_m) * g.tiles_n));
         if (out_bf16)
             hipLaunchKernelGGL((gemm_kernel<true, TILED>), grid, dim3(kThreads), 0, st, g);

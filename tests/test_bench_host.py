@@ -30,6 +30,13 @@ def test_decode_rows_range(rows):
     assert "--rows must be in 1..64" in r.stderr
 
 
+@pytest.mark.parametrize("rows", ["64", "8193"])
+def test_prefill_rows_range(rows):
+    r = _run("--gemm", "--rows", rows)
+    assert r.returncode == 2
+    assert "--rows must be in 65..8192" in r.stderr
+
+
 def test_source_hash_is_stable():
     h = bench.kernel_source_hash()
     assert re.fullmatch(r"[0-9a-f]{16}", h)

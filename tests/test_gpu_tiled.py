@@ -147,6 +147,30 @@ def test_large_product_full_size_same_bits(dev):
     assert torch.equal(y_t, y_row)
 
 
+@pytest.mark.parametrize("M,N,K", [(257, 4000, 128), (2048, 4096, 1024), (3840, 4096, 256), (4096, 3840, 384),
+                                   (4096, 4000, 128), (4100, 3900, 384), (3900, 4100, 256), (2048, 4096, 14336)])
+def test_product_either_large_kernel_same_bits(dev, M, N, K):
+    """Both sides of the switch between the 256 x 256 kernel (grids with at
+    least one such tile per CU) and the two-blocks-per-CU 256 x 128 kernel
+    (fewer tiles), ragged edges included: the tiled product equals the
+    row-layout product (always the 256 x 256 kernel) bit for bit."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    tiles = -(-M // 256) * -(-N // 256)
+    g = torch.Generator(device=dev)
+    g.manual_seed(M * 7 + N * 3 + K)
+    a = (torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device=dev, generator=g),
+         torch.randint(115, 135, (M, K // 32), dtype=torch.uint8, device=dev, generator=g))
+    b = (torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=dev, generator=g),
+         torch.randint(115, 135, (N, K // 32), dtype=torch.uint8, device=dev, generator=g))
+    ta, tb = mxq.tile_mxfp4(*a), mxq.tile_mxfp4(*b)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        print(f"  product M={M} N={N} K={K} {out_dtype}: {tiles} tiles of 256x256 on {cus} CUs", flush=True)
+        y_row = mxq.gemm_mxfp4(*a, *b, out_dtype)
+        y_t = mxq.gemm_mxfp4_tiled(*ta, *tb, M, N, K, out_dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(y_t, y_row)
+
+
 @pytest.mark.parametrize("T,dtype,with_lam", [(5000, torch.bfloat16, False), (4700, torch.float16, True)])
 def test_rotate_quant_tiled_prefill_sizes(dev, T, dtype, with_lam):
     """Batches long enough that the quantizer writes records a 16-row unit at
