@@ -38,7 +38,11 @@
 // than the chip has CUs: 256 x 128 tiles, two blocks per CU (gemm2_kernel).
 //
 // Decode-shaped products (M <= 64): split-K over the 16 waves of a block
-// that owns 16 output columns (see gemm_small_kernel).
+// that owns 16 output columns (see gemm_small_kernel).  From 65 to
+// MXQ_GEMM_CHUNKED_MAX_M rows, while the 256 x 256 grid has fewer tiles
+// than CUs, the same kernel with one block row per 64 activation rows.  The
+// choice depends on the shape only, so both storage layouts give the same
+// bits.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -48,6 +52,9 @@
 
 #ifndef MXQ_GEMM_GROUP_M
 #define MXQ_GEMM_GROUP_M 4  // tile rows per band of the block order
+#endif
+#ifndef MXQ_GEMM_CHUNKED_MAX_M
+#define MXQ_GEMM_CHUNKED_MAX_M 128  // above 64 and up to this many rows: the decode kernel in 64-row block rows
 #endif
 #ifndef MXQ_GEMM_STAGES
 #define MXQ_GEMM_STAGES 4  // LDS ring of K stages; loads run MXQ_GEMM_STAGES - 1 stages ahead
@@ -528,12 +535,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, k2Threads), amdgpu_wave
 // non-temporal policy (each byte is used once); for the row layout the
 // default policy is faster, as the two halves of each 128-byte line are
 // fetched by different waves.
+//
+// Small batches above 64 rows (CHUNKED): block row y of a 2-D grid takes
+// activation rows 64 y .. 64 y + 63 with the 64-row code.  Dispatch ids go
+// round-robin over the dies, so when the column-group count is a multiple
+// of 8 (N a multiple of 128) the blocks of one column group land on one die
+// and share its L2 copy of the weight records (read with the default policy
+// here).  A 256-row tile would run one tile row of blocks on a mostly idle
+// chip.
 constexpr int kSmallWaves = 16;
 constexpr int kAuxNonTemporal = 2;  // cache policy bits of buffer ops
 constexpr int kSmallMaxM = 64;
 typedef __attribute__((ext_vector_type(4))) float f32x4s_t;
 
-template <bool OUT_BF16, int FM, bool TILED>
+template <bool OUT_BF16, int FM, bool TILED, bool CHUNKED>
 __global__ __launch_bounds__(kWave * kSmallWaves) void gemm_small_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) f32x4s_t red[kSmallWaves][FM][kWave];
     const int lane = threadIdx.x & (kWave - 1);
@@ -542,21 +557,25 @@ __global__ __launch_bounds__(kWave * kSmallWaves) void gemm_small_kernel(GemmArg
     const uint32_t cpr = static_cast<uint32_t>(g.K) / 2;
     const uint32_t spr = static_cast<uint32_t>(g.K) / 32;
     const uint32_t nk32 = static_cast<uint32_t>(g.K) / 128;
+    // CHUNKED: block row blockIdx.y owns activation rows 64 y .. 64 y + 63
+    const int64_t m_off = CHUNKED ? static_cast<int64_t>(blockIdx.y) * 64 : 0;
+    const int64_t rows_a = CHUNKED ? min<int64_t>(64, g.M - m_off) : g.M;
     __amdgpu_buffer_rsrc_t ra, rsa, rb, rsb;
     if constexpr (TILED) {
-        const uint32_t recs_a = static_cast<uint32_t>((g.M + 15) / 16);
-        ra = rsrc(g.a_codes, recs_a * nk32 * 1024);
-        rsa = rsrc(g.a_scales, recs_a * nk32 * 64);
+        const uint32_t recs_a = static_cast<uint32_t>((rows_a + 15) / 16);
+        ra = rsrc(g.a_codes + (m_off / 16) * nk32 * 1024, recs_a * nk32 * 1024);
+        rsa = rsrc(g.a_scales + (m_off / 16) * nk32 * 64, recs_a * nk32 * 64);
         rb = rsrc(g.b_codes + (n0 / 16) * nk32 * 1024, nk32 * 1024);
         rsb = rsrc(g.b_scales + (n0 / 16) * nk32 * 64, nk32 * 64);
     } else {
         const uint32_t rows_b = static_cast<uint32_t>(min<int64_t>(16, g.N - n0));
-        ra = rsrc(g.a_codes, static_cast<uint32_t>(g.M) * cpr);
-        rsa = rsrc(g.a_scales, static_cast<uint32_t>(g.M) * spr);
+        ra = rsrc(g.a_codes + m_off * cpr, static_cast<uint32_t>(rows_a) * cpr);
+        rsa = rsrc(g.a_scales + m_off * spr, static_cast<uint32_t>(rows_a) * spr);
         rb = rsrc(g.b_codes + n0 * cpr, rows_b * cpr);
         rsb = rsrc(g.b_scales + n0 * spr, rows_b * spr);
     }
-    constexpr int kAuxB = TILED ? kAuxNonTemporal : 0;
+    // (chunked launches reuse each weight record across block rows: default policy)
+    constexpr int kAuxB = (TILED && !CHUNKED) ? kAuxNonTemporal : 0;
     const uint32_t r16 = static_cast<uint32_t>(lane & 15);
     const uint32_t q = static_cast<uint32_t>(lane >> 4);
     f32x4s_t acc[FM];
@@ -623,11 +642,11 @@ __global__ __launch_bounds__(kWave * kSmallWaves) void gemm_small_kernel(GemmArg
         for (int w = 0; w < kSmallWaves; ++w) sum += red[w][f][l][r];
         const int64_t row = 16 * f + 4 * (l >> 4) + r;
         const int64_t col = n0 + (l & 15);
-        if (row < g.M && col < g.N) {
+        if (row < rows_a && col < g.N) {
             if constexpr (OUT_BF16)
-                static_cast<__bf16*>(g.y)[row * g.ldy + col] = static_cast<__bf16>(sum);
+                static_cast<__bf16*>(g.y)[(row + m_off) * g.ldy + col] = static_cast<__bf16>(sum);
             else
-                static_cast<float*>(g.y)[row * g.ldy + col] = sum;
+                static_cast<float*>(g.y)[(row + m_off) * g.ldy + col] = sum;
         }
     }
 }
@@ -637,23 +656,28 @@ void launch_small(const GemmArgs& g, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>((g.N + 15) / 16));
     const dim3 block(kWave * kSmallWaves);
     if (g.M <= 16)
-        hipLaunchKernelGGL((gemm_small_kernel<OUT_BF16, 1, TILED>), grid, block, 0, st, g);
+        hipLaunchKernelGGL((gemm_small_kernel<OUT_BF16, 1, TILED, false>), grid, block, 0, st, g);
     else if (g.M <= 32)
-        hipLaunchKernelGGL((gemm_small_kernel<OUT_BF16, 2, TILED>), grid, block, 0, st, g);
+        hipLaunchKernelGGL((gemm_small_kernel<OUT_BF16, 2, TILED, false>), grid, block, 0, st, g);
+    else if (g.M <= kSmallMaxM)
+        hipLaunchKernelGGL((gemm_small_kernel<OUT_BF16, 4, TILED, false>), grid, block, 0, st, g);
     else
-        hipLaunchKernelGGL((gemm_small_kernel<OUT_BF16, 4, TILED>), grid, block, 0, st, g);
+        hipLaunchKernelGGL((gemm_small_kernel<OUT_BF16, 4, TILED, true>),
+                           dim3(grid.x, static_cast<unsigned>((g.M + kSmallMaxM - 1) / kSmallMaxM)), block, 0, st, g);
 }
 
 template <bool TILED>
 mxq_status launch_gemm(const GemmArgs& g, bool out_bf16, hipStream_t st) {
-    if (g.M <= kSmallMaxM) {
+    const int64_t cus = device_cu_count();
+    const bool underfilled = static_cast<int64_t>(g.tiles_m) * g.tiles_n < cus;
+    if (g.M <= kSmallMaxM || (underfilled && g.M <= MXQ_GEMM_CHUNKED_MAX_M)) {
         if (out_bf16)
             launch_small<true, TILED>(g, st);
         else
             launch_small<false, TILED>(g, st);
     } else {
         if constexpr (TILED) {
-            if (static_cast<int64_t>(g.tiles_m) * g.tiles_n < device_cu_count()) {
+            if (underfilled) {
                 GemmArgs g2 = g;
                 g2.tiles_n = (g.N + k2BN - 1) / k2BN;
                 const dim3 grid2(static_cast<unsigned>(static_cast<int64_t>(g2.tiles_m) * g2.tiles_n));

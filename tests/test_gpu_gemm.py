@@ -52,7 +52,7 @@ def check_product(y, ref, s_abs, K, where=""):
 
 @pytest.mark.parametrize("M,N,K", [(16, 16, 256), (128, 128, 512), (1, 1, 256), (200, 130, 768),
                                    (300, 257, 1024), (129, 383, 2048), (64, 640, 4096), (33, 70, 128),
-                                   (100, 300, 384), (513, 260, 1152)])
+                                   (100, 300, 384), (513, 260, 1152), (700, 2300, 256), (1100, 1500, 384)])
 def test_gemm_random_operands(dev, orc, M, N, K):
     rng = np.random.default_rng(M * 7919 + N * 31 + K)
     ac, asc = W.random_mxfp4(rng, M, K)
@@ -68,10 +68,13 @@ def test_gemm_random_operands(dev, orc, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 14336), (7, 100, 128), (16, 4096, 4096), (17, 300, 1152),
-                                   (40, 64, 2048), (64, 1000, 14336), (16, 16, 256)])
+                                   (40, 64, 2048), (64, 1000, 14336), (16, 16, 256), (65, 300, 1152),
+                                   (128, 4096, 2048), (100, 1000, 1024), (97, 70, 14336)])
 def test_gemm_decode_shapes(dev, orc, M, N, K):
     """Decode-shaped products (the path for M <= 64 splits K over the waves
-    of a block and sums the partial tiles in a fixed order)."""
+    of a block and sums the partial tiles in a fixed order), and small
+    batches of 65 to 128 rows, which run the same kernel with one block row
+    per 64 rows (ragged last block row included)."""
     rng = np.random.default_rng(M * 131 + N * 17 + K + 5)
     ac, asc = W.random_mxfp4(rng, M, K)
     bc, bsc = W.random_mxfp4(rng, N, K)

@@ -147,13 +147,14 @@ def test_large_product_full_size_same_bits(dev):
     assert torch.equal(y_t, y_row)
 
 
-@pytest.mark.parametrize("M,N,K", [(257, 4000, 128), (2048, 4096, 1024), (3840, 4096, 256), (4096, 3840, 384),
+@pytest.mark.parametrize("M,N,K", [(257, 8000, 128), (2048, 4096, 1024), (3840, 4096, 256), (4096, 3840, 384),
                                    (4096, 4000, 128), (4100, 3900, 384), (3900, 4100, 256), (2048, 4096, 14336)])
 def test_product_either_large_kernel_same_bits(dev, M, N, K):
     """Both sides of the switch between the 256 x 256 kernel (grids with at
     least one such tile per CU) and the two-blocks-per-CU 256 x 128 kernel
-    (fewer tiles), ragged edges included: the tiled product equals the
-    row-layout product (always the 256 x 256 kernel) bit for bit."""
+    (fewer tiles, with too many rows for the chunked decode kernel), ragged
+    edges included: the tiled product equals the row-layout product (always
+    the 256 x 256 kernel at these sizes) bit for bit."""
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     tiles = -(-M // 256) * -(-N // 256)
     g = torch.Generator(device=dev)
